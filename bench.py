@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+Headline (the JSON `value`): decode KV-read bandwidth of the GQA split-KV
+decode workload -- batch 32, 64 query heads over 8 KV heads, T = 1,
+s_k = 8192, hd = 128, 64 partitions of 128 keys merged by LSE.  One step is
+fmha_decode_splitkv followed by fmha_lse_merge on the same stream, with all
+inputs resident in HBM.  The 1 GiB of K/V is four times the Infinity Cache,
+so every step streams it from HBM.
+
+Also reported on the same line:
+  roofline      the split kernel (the dominant one): algorithmic bytes per
+                launch / its mean duration from HIP events recorded around
+                each launch on the launch stream, against 8 TB/s.
+  cpu_baseline  the fp64 CPU oracle computing the same workload (split +
+                merge) on the host cores, as KV-read GB/s.
+  prefill       the largest causal MHA prefill point and the sliding-window
+                MQA prefill: fused-kernel TFLOP/s (algorithmic flops) against
+                the dense bf16 MFMA peak and against the bandwidth roofline,
+                timed from graph replays over input replicas rotated through
+                more than the Infinity Cache.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2516.6    # 256 CU x 2.4 GHz x 4096 flop/clk, dense bf16
+METRIC = "decode KV-read GB/s + prefill attn TFLOP/s (bf16), % of MI355X roofline"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_bytes(w):
+    kv = 4 * w.batch * w.n_kv_h * w.s_k * w.hd               # K + V, bf16
+    q = 2 * w.batch * w.T * w.n_h * w.hd
+    part_o = 4 * w.batch * w.n_h * w.T * w.n_split * w.hd
+    part_l = 4 * w.batch * w.n_h * w.T * w.n_split
+    o = 2 * w.batch * w.T * w.n_h * w.hd
+    lse = 4 * w.batch * w.n_h * w.T
+    split_kernel = kv + q + part_o + part_l                     # reads K, V, Q; writes partials
+    merge_kernel = part_o + part_l + o + lse                    # reads partials; writes O, lse
+    return kv, split_kernel, merge_kernel
+
+
+def prefill_work(w):
+    """Algorithmic (flops, bytes) of one fused call; masked keys are not work."""
+    pairs = 0
+    union_lo, union_hi = w.s_k, 0
+    for i in range(w.T):
+        pos = w.s_k - w.T + i
+        hi = min(w.s_k, pos + 1) if w.causal else w.s_k
+        lo = max(0, pos - w.window + 1) if w.window else 0
+        pairs += max(0, hi - lo)
+        union_lo, union_hi = min(union_lo, lo), max(union_hi, hi)
+    flops = 4.0 * w.hd * w.batch * w.n_h * pairs
+    u = max(0, union_hi - union_lo)
+    byts = (2 * 2 * w.batch * w.T * w.n_h * w.hd + 4 * w.batch * w.n_h * w.T
+            + 4 * w.batch * w.n_kv_h * u * w.hd)
+    return flops, byts
+
+
+def run_decode(args, torch, fa, I):
+    w = I.GQA_SPLITKV_DECODE
+    dev = torch.device("cuda:0")
+    log(f"decode workload {w.name}: drawing inputs on the device")
+    q, k, v = I.make_qkv(w, device="cuda")
+    o_part = torch.empty((w.batch, w.n_h, w.T, w.n_split, w.hd), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((w.batch, w.n_h, w.T, w.n_split), dtype=torch.float32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.n_h, w.T), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def split():
+        fa.fmha_decode_splitkv(q, k, v, o_part, lse_part, split_len=w.split_len, scale=w.scale, stream=stream)
+
+    def merge():
+        fa.fmha_lse_merge(o_part, lse_part, o, lse, stream=stream)
+
+    for _ in range(args.warmup):
+        split()
+        merge()
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    evs = [(E(), E(), E()) for _ in range(args.steps)]
+    t0, t1 = E(), E()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for a, b, c in evs:
+        a.record(stream)
+        split()
+        b.record(stream)
+        merge()
+        c.record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    split_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / args.steps
+    merge_ms = sum(b.elapsed_time(c) for _, b, c in evs) / args.steps
+    ms_per_step = total_ms / args.steps
+    kv_bytes, split_bytes, merge_bytes = decode_bytes(w)
+    log(f"decode: {ms_per_step * 1e3:.1f} us/step (split {split_ms * 1e3:.1f} us, merge {merge_ms * 1e3:.1f} us)")
+    res = {
+        "w": w, "ms_per_step": ms_per_step, "split_ms": split_ms, "merge_ms": merge_ms,
+        "value": kv_bytes / (ms_per_step * 1e-3) / 1e9,
+        "split_gbs": split_bytes / (split_ms * 1e-3) / 1e9,
+        "merge_gbs": merge_bytes / (merge_ms * 1e-3) / 1e9,
+        "split_bytes": split_bytes, "kv_bytes": kv_bytes,
+        "host_qkv": None,
+    }
+    if not args.no_cpu_baseline:
+        res["host_qkv"] = (q.cpu(), k.cpu(), v.cpu())
+    return res
+
+
+def graph_time_us(torch, calls, reps):
+    """Capture `calls` (one launch each) into one graph; return mean us per call."""
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for c in calls:  # warm, outside capture
+            c()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1e3 / (reps * len(calls))
+
+
+def run_prefill(torch, fa, I):
+    out = []
+    for w in (I.mha_causal_prefill(128, 512, 512), I.SWA_MQA_PREFILL):
+        flops, byts = prefill_work(w)
+        foot = 2 * (w.batch * w.T * w.n_h * w.hd * 2) + 2 * (w.batch * w.s_k * w.n_kv_h * w.hd * 2)
+        reps = max(1, min(64, math.ceil(512 * 2**20 / foot)))  # rotate >= 512 MiB
+        q, k, v = I.make_qkv(w, device="cuda")
+        bufs = []
+        for r in range(reps):
+            qr, kr, vr = (q, k, v) if r == 0 else (q.clone(), k.clone(), v.clone())
+            bufs.append((qr, kr, vr, torch.empty_like(qr),
+                         torch.empty((w.batch, w.n_h, w.T), dtype=torch.float32, device="cuda")))
+
+        def mk(bf):
+            return lambda: fa.fmha_forward(bf[0], bf[1], bf[2], bf[3], bf[4], scale=w.scale,
+                                           window=w.window, causal=w.causal,
+                                           stream=torch.cuda.current_stream())
+        us = graph_time_us(torch, [mk(bf) for bf in bufs], reps=max(3, 200 // reps))
+        t_roof_us = max(byts / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFS * 1e12)) * 1e6
+        tfs = flops / (us * 1e-6) / 1e12
+        out.append({"workload": w.name, "us_per_call": round(us, 2), "tflops": round(tfs, 1),
+                    "frac_of_mfma_peak": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+                    "frac_of_roofline": round(t_roof_us / us, 4), "roofline_bound": "hbm",
+                    "alg_gflop": round(flops / 1e9, 3), "alg_mib": round(byts / 2**20, 2),
+                    "rotated_replicas": reps})
+        log(f"prefill {w.name}: {us:.2f} us, {tfs:.1f} TFLOP/s, {t_roof_us / us:.1%} of roofline")
+        del bufs, q, k, v
+        torch.cuda.empty_cache()
+    return out
+
+
+def run_cpu_baseline(res, seconds):
+    import oracle
+    w = res["w"]
+    q, k, v = res["host_qkv"]
+    threads = oracle.default_threads()
+    log(f"cpu baseline: fp64 oracle on the full workload, {threads} threads")
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        op, lp = oracle.split(q, k, v, w.scale, w.split_len, threads=threads)
+        oracle.merge(op, lp)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or el / runs * (runs + 1) > 3 * seconds:
+            break
+    per = el / runs
+    return {"value": round(res["kv_bytes"] / per / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole workload (split into 64 partitions + LSE merge, fp64), run {runs}x, "
+                      f"{per:.2f} s each"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the attention path "
+              f"shards by batch, KV head or sequence with no cross-GPU step measured here)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import head_attention_fmha_amd as fa
+    from head_attention_fmha_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.load_library()
+    res = run_decode(args, torch, fa, I)
+    prefill = None if args.no_prefill else run_prefill(torch, fa, I)
+    cpu = None if args.no_cpu_baseline else run_cpu_baseline(res, args.cpu_seconds)
+    w = res["w"]
+    split_us = res["split_ms"] * 1e3
+    line = {
+        "metric": METRIC,
+        "value": round(res["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded device draws: Q, K ~ N(0,1), V ~ U(-1,1), bf16)",
+        "config": {"workload": w.name, "batch": w.batch, "n_h": w.n_h, "n_kv_h": w.n_kv_h, "T": w.T,
+                   "s_k": w.s_k, "hd": w.hd, "split_len": w.split_len, "n_split": w.n_split,
+                   "step": "fmha_decode_splitkv + fmha_lse_merge",
+                   "split_us": round(split_us, 2), "merge_us": round(res["merge_ms"] * 1e3, 2),
+                   "merge_gbs": round(res["merge_gbs"], 1)},
+        "roofline": {"kernel": "fwd_kernel<128,1,4,split>", "bound": "hbm",
+                     "achieved": round(res["split_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(res["split_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": res["split_bytes"], "launch_us": round(split_us, 2)},
+        "cpu_baseline": cpu,
+        "prefill": prefill,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,168 @@
-"""MI355X (gfx950) fused multi-head attention: a C-ABI HIP library plus a thin ctypes binding."""
+"""MI355X (gfx950) fused multi-head attention.
+
+The compute lives in libfmha.so (hand-written HIP kernels behind the C ABI
+of include/fmha.h).  This module is argument marshalling only: it turns
+torch tensors into device pointers, sizes and element strides, passes the
+current HIP stream, and raises FmhaError on a non-zero status.  There is no
+other implementation to fall back to: if the library is missing or a call
+fails, the error propagates.
+
+Entry points carry the C names:
+  fmha_forward(q, k, v, o, lse=None, *, scale=None, window=0, causal=False)
+  fmha_decode_splitkv(q, k, v, o_part, lse_part, *, split_len, scale=None, window=0, causal=False)
+  fmha_lse_merge(o_part, lse_part, o, lse=None)
+  fmha_status_string(status)
+Layouts: q, o [batch, T, n_h, hd]; k, v [batch, s_k, n_kv_h, hd] (a head
+stride of 0 expresses MQA); lse [batch, n_h, T];
+o_part [batch, n_h, T, n_split, hd]; lse_part [batch, n_h, T, n_split].
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["FmhaError", "fmha_forward", "fmha_decode_splitkv", "fmha_lse_merge", "fmha_status_string",
+           "n_split_for", "library_path", "load_library", "FmhaStrides"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libfmha.so")
+_lib = None
+
+
+class FmhaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class FmhaStrides(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("token", ctypes.c_int64), ("head", ctypes.c_int64)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libfmha.so (built by head_attention_fmha_amd.build); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise FmhaError(-1, f"{_LIB_PATH} is not built; run `python -m head_attention_fmha_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, FmhaStrides
+    lib.fmha_forward.argtypes = [P, P, P, P, P, I, I, I, I, I, I, S, S, S, S, F, I, I, P]
+    lib.fmha_forward.restype = I
+    lib.fmha_decode_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, S, S, S, F, I, I, I, P]
+    lib.fmha_decode_splitkv.restype = I
+    lib.fmha_lse_merge.argtypes = [P, P, P, P, I, I, I, I, I, S, P]
+    lib.fmha_lse_merge.restype = I
+    lib.fmha_status_string.argtypes = [I]
+    lib.fmha_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fmha_status_string(status: int) -> str:
+    return load_library().fmha_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise FmhaError(status, fmha_status_string(status))
+
+
+def _dev4(t: torch.Tensor, name: str, dtype=torch.bfloat16):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D, got shape {tuple(t.shape)}")
+    if t.stride(3) != 1 and t.shape[3] != 1:
+        raise ValueError(f"{name}: the head dimension must be contiguous")
+
+
+def _st(t: torch.Tensor) -> FmhaStrides:
+    return FmhaStrides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _scale(scale, hd):
+    return 1.0 / math.sqrt(hd) if scale is None else float(scale)
+
+
+def n_split_for(s_k: int, split_len: int) -> int:
+    return -(-s_k // split_len)
+
+
+def _dense(t: Optional[torch.Tensor], shape, name, dtype=torch.float32):
+    if t is None:
+        return
+    if t.dtype != dtype or t.device.type != "cuda" or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous {dtype} device tensor of shape {tuple(shape)}")
+
+
+def fmha_forward(q, k, v, o, lse=None, *, scale=None, window=0, causal=False, stream=None) -> None:
+    """o (and lse if given) <- attention(q, k, v); see include/fmha.h."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _dev4(t, n)
+    b, T, n_h, hd = q.shape
+    _, s_k, n_kv_h, _ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape) or k.shape[0] != b or k.shape[3] != hd:
+        raise ValueError("shape mismatch between q, k, v, o")
+    _dense(lse, (b, n_h, T), "lse")
+    _check(load_library().fmha_forward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, n_h, n_kv_h, T, s_k, hd,
+        _st(q), _st(k), _st(v), _st(o), _scale(scale, hd), int(window), int(bool(causal)), _stream(stream)))
+
+
+def fmha_decode_splitkv(q, k, v, o_part, lse_part, *, split_len, scale=None, window=0, causal=False,
+                        stream=None) -> None:
+    """Per-partition attention into fp32 o_part / lse_part; see include/fmha.h."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev4(t, n)
+    b, T, n_h, hd = q.shape
+    _, s_k, n_kv_h, _ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != b or k.shape[3] != hd:
+        raise ValueError("shape mismatch between q, k, v")
+    if split_len <= 0:
+        raise ValueError("split_len must be positive")
+    ns = n_split_for(s_k, split_len)
+    _dense(o_part, (b, n_h, T, ns, hd), "o_part")
+    _dense(lse_part, (b, n_h, T, ns), "lse_part")
+    _check(load_library().fmha_decode_splitkv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), b, n_h, n_kv_h, T, s_k, hd,
+        _st(q), _st(k), _st(v), _scale(scale, hd), int(window), int(bool(causal)), int(split_len),
+        _stream(stream)))
+
+
+def fmha_lse_merge(o_part, lse_part, o, lse=None, *, stream=None) -> None:
+    """o (bf16) and lse <- D5 merge of the partitions; see include/fmha.h."""
+    _dev4(o, "o")
+    if o_part.dim() != 5:
+        raise ValueError("o_part must be [batch, n_h, T, n_split, hd]")
+    b, n_h, T, ns, hd = o_part.shape
+    if tuple(o.shape) != (b, T, n_h, hd):
+        raise ValueError("o must be [batch, T, n_h, hd] matching o_part")
+    _dense(o_part, (b, n_h, T, ns, hd), "o_part")
+    _dense(lse_part, (b, n_h, T, ns), "lse_part")
+    _dense(lse, (b, n_h, T), "lse")
+    _check(load_library().fmha_lse_merge(
+        _ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), b, n_h, T, hd, ns, _st(o), _stream(stream)))

@@ -1,0 +1,46 @@
+// device_common.hpp -- small gfx950 building blocks shared by the fmha kernels.
+//
+// MFMA register layouts used throughout (v_mfma_f32_16x16x32_bf16, wave64):
+//   lane l = lr + 16*lg   (lr = l % 16, lg = l / 16)
+//   A (16 x 32):  lane l holds A[lr][8*lg + 0..7]        (8 bf16, one row)
+//   B (32 x 16):  lane l holds B[8*lg + 0..7][lr]        (8 bf16, one column)
+//   D (16 x 16):  lane l holds D[4*lg + 0..3][lr]        (4 fp32)
+// A and B index their reduction dimension through the same (lg, item)
+// pairs, so any permutation of that dimension applied to both operands
+// leaves the product unchanged; the kernels use this to feed softmax
+// probabilities straight from one MFMA's result registers into the next.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fmha {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Butterfly over lanes l ^ mask (wave64; every lane participates).
+__device__ __forceinline__ float xor_shuffle(float x, int mask) {
+    const int lane = __lane_id();
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
+}
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    __bf16 b = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+}  // namespace fmha

@@ -1,0 +1,197 @@
+// fmha_api.hip -- the C ABI of libfmha.so (declared in include/fmha.h):
+// argument validation, shape-class dispatch and kernel launches.
+//
+// Validation runs entirely on the host before any HIP call, so invalid
+// calls return a status without touching the device (and work on a machine
+// with no GPU).  Every launch goes to the caller's stream; nothing here
+// synchronises, allocates or keeps state.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fmha.h"
+#include "fwd_kernel.hpp"
+#include "merge_kernel.hpp"
+
+namespace {
+
+using fmha::FwdParams;
+using fmha::MergeParams;
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+bool stride_ok(int64_t s) { return s >= 0 && (s % 8) == 0; }
+
+bool strides_ok(const fmha_strides &st) {
+    return stride_ok(st.batch) && stride_ok(st.token) && stride_ok(st.head);
+}
+
+bool hd_supported(int hd) { return hd == 64 || hd == 128 || hd == 256 || hd == 512; }
+
+// Shared validation of fmha_forward / fmha_decode_splitkv.
+int validate_attention(const void *q, const void *k, const void *v, const void *out0, const void *out1,
+                       bool out1_required, int batch, int n_h, int n_kv_h, int T, int s_k, int hd,
+                       const fmha_strides &q_st, const fmha_strides &k_st, const fmha_strides &v_st,
+                       const fmha_strides *o_st, int window, int causal) {
+    if (!q || !k || !v || !out0 || (out1_required && !out1)) return FMHA_ERR_INVALID_ARG;
+    if (batch <= 0 || n_h <= 0 || n_kv_h <= 0 || T <= 0 || s_k <= 0 || hd <= 0) return FMHA_ERR_INVALID_ARG;
+    if (n_h % n_kv_h != 0) return FMHA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FMHA_ERR_INVALID_ARG;
+    if (window < 0) return FMHA_ERR_INVALID_ARG;
+    if ((causal || window > 0) && T > s_k) return FMHA_ERR_INVALID_ARG;
+    if (!hd_supported(hd) || T > 128) return FMHA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out0) || (out1 && !aligned16(out1)))
+        return FMHA_ERR_ALIGNMENT;
+    if (!strides_ok(q_st) || !strides_ok(k_st) || !strides_ok(v_st) || (o_st && !strides_ok(*o_st)))
+        return FMHA_ERR_ALIGNMENT;
+    return FMHA_OK;
+}
+
+FwdParams make_params(const void *q, const void *k, const void *v, int batch, int n_h, int n_kv_h, int T,
+                      int s_k, const fmha_strides &q_st, const fmha_strides &k_st, const fmha_strides &v_st,
+                      float scale, int window, int causal) {
+    // K and V both with head stride 0 hold one KV head for every query
+    // head: run it as MQA (n_kv_h = 1), streaming K/V once per batch.
+    if (k_st.head == 0 && v_st.head == 0) n_kv_h = 1;
+    FwdParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.q_sb = q_st.batch; p.q_st = q_st.token; p.q_sh = q_st.head;
+    p.k_sb = k_st.batch; p.k_st = k_st.token; p.k_sh = k_st.head;
+    p.v_sb = v_st.batch; p.v_st = v_st.token; p.v_sh = v_st.head;
+    p.batch = batch; p.n_h = n_h; p.n_kv_h = n_kv_h; p.T = T; p.s_k = s_k;
+    p.group = n_h / n_kv_h;
+    p.rows = p.group * T;
+    p.window = window;
+    p.causal = causal;
+    p.scale_log2 = scale * fmha::kLog2e;
+    return p;
+}
+
+// Waves per workgroup along rows (NWR) and along keys (NWK).  Few rows per
+// (batch, kv_head) -> split the keys across the waves and merge in LDS;
+// many rows -> give each wave its own 16-row tile sharing the staged keys.
+// NWK is capped per head dim so a chunk of K+V (32*NWK keys) fits in LDS.
+template <int HD, bool SPLIT>
+hipError_t launch_hd(FwdParams p, hipStream_t stream) {
+    constexpr int NWK_MAX = HD <= 128 ? 4 : (HD == 256 ? 2 : 1);
+    int nwr, nwk;
+    if (p.rows <= 16) {
+        nwr = 1; nwk = NWK_MAX;
+    } else if (p.rows <= 32) {
+        nwr = 2; nwk = NWK_MAX >= 2 ? 2 : 1;
+    } else {
+        nwr = 4; nwk = 1;
+    }
+    p.n_row_blocks = (p.rows + 16 * nwr - 1) / (16 * nwr);
+    const int64_t units = (int64_t)p.n_row_blocks * p.n_split * p.n_kv_h * p.batch;
+    if (units > 0x7fffffff) return hipErrorInvalidConfiguration;
+    p.n_units = (int)units;
+    p.xcd_remap = (p.n_units % 8 == 0) ? 1 : 0;
+    const dim3 grid(p.n_units);
+    const dim3 block(64 * nwr * nwk);
+    if (nwr == 1 && nwk == NWK_MAX)
+        hipLaunchKernelGGL((fmha::fwd_kernel<HD, 1, NWK_MAX, SPLIT>), grid, block, 0, stream, p);
+    else if (nwr == 2 && nwk == 2 && NWK_MAX >= 2)
+        hipLaunchKernelGGL((fmha::fwd_kernel<HD, 2, (NWK_MAX >= 2 ? 2 : 1), SPLIT>), grid, block, 0, stream, p);
+    else if (nwr == 2)
+        hipLaunchKernelGGL((fmha::fwd_kernel<HD, 2, 1, SPLIT>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((fmha::fwd_kernel<HD, 4, 1, SPLIT>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+template <bool SPLIT>
+int launch_attention(const FwdParams &p, int hd, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    switch (hd) {
+        case 64: err = launch_hd<64, SPLIT>(p, s); break;
+        case 128: err = launch_hd<128, SPLIT>(p, s); break;
+        case 256: err = launch_hd<256, SPLIT>(p, s); break;
+        default: err = launch_hd<512, SPLIT>(p, s); break;
+    }
+    return err == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fmha_forward(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int n_h,
+                 int n_kv_h, int T, int s_k, int hd, fmha_strides q_st, fmha_strides k_st, fmha_strides v_st,
+                 fmha_strides o_st, float scale, int window, int causal, void *stream) {
+    int rc = validate_attention(q, k, v, o, lse, false, batch, n_h, n_kv_h, T, s_k, hd, q_st, k_st, v_st, &o_st,
+                                window, causal);
+    if (rc != FMHA_OK) return rc;
+    FwdParams p = make_params(q, k, v, batch, n_h, n_kv_h, T, s_k, q_st, k_st, v_st, scale, window, causal);
+    p.o = static_cast<uint16_t *>(o);
+    p.lse = lse;
+    p.o_sb = o_st.batch; p.o_st = o_st.token; p.o_sh = o_st.head;
+    p.split_len = s_k;
+    p.n_split = 1;
+    return launch_attention<false>(p, hd, stream);
+}
+
+int fmha_decode_splitkv(const void *q, const void *k, const void *v, float *o_part, float *lse_part, int batch,
+                        int n_h, int n_kv_h, int T, int s_k, int hd, fmha_strides q_st, fmha_strides k_st,
+                        fmha_strides v_st, float scale, int window, int causal, int split_len, void *stream) {
+    if (split_len <= 0) return FMHA_ERR_INVALID_ARG;
+    int rc = validate_attention(q, k, v, o_part, lse_part, true, batch, n_h, n_kv_h, T, s_k, hd, q_st, k_st, v_st,
+                                nullptr, window, causal);
+    if (rc != FMHA_OK) return rc;
+    FwdParams p = make_params(q, k, v, batch, n_h, n_kv_h, T, s_k, q_st, k_st, v_st, scale, window, causal);
+    p.o_part = o_part;
+    p.lse_part = lse_part;
+    p.split_len = split_len;
+    p.n_split = (int)(((int64_t)s_k + split_len - 1) / split_len);
+    return launch_attention<true>(p, hd, stream);
+}
+
+int fmha_lse_merge(const float *o_part, const float *lse_part, void *o, float *lse, int batch, int n_h, int T,
+                   int hd, int n_split, fmha_strides o_st, void *stream) {
+    if (!o_part || !lse_part || !o) return FMHA_ERR_INVALID_ARG;
+    if (batch <= 0 || n_h <= 0 || T <= 0 || hd <= 0 || n_split <= 0) return FMHA_ERR_INVALID_ARG;
+    if (!hd_supported(hd)) return FMHA_ERR_UNSUPPORTED;
+    if (!aligned16(o_part) || !aligned16(lse_part) || !aligned16(o) || (lse && !aligned16(lse)))
+        return FMHA_ERR_ALIGNMENT;
+    if (!strides_ok(o_st)) return FMHA_ERR_ALIGNMENT;
+    const int64_t rows = (int64_t)batch * n_h * T;
+    MergeParams p{};
+    p.o_part = o_part;
+    p.lse_part = lse_part;
+    p.o = static_cast<uint16_t *>(o);
+    p.lse = lse;
+    p.o_sb = o_st.batch; p.o_st = o_st.token; p.o_sh = o_st.head;
+    p.n_h = n_h;
+    p.T = T;
+    p.n_split = n_split;
+    const int rpw = 256 / (hd / 4);
+    const int64_t blocks = (rows + rpw - 1) / rpw;
+    if (rows > 0x7fffffff || blocks > 0x7fffffff) return FMHA_ERR_UNSUPPORTED;
+    p.rows = (int)rows;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)blocks), block(256);
+    switch (hd) {
+        case 64: hipLaunchKernelGGL(fmha::merge_kernel<64>, grid, block, 0, s, p); break;
+        case 128: hipLaunchKernelGGL(fmha::merge_kernel<128>, grid, block, 0, s, p); break;
+        case 256: hipLaunchKernelGGL(fmha::merge_kernel<256>, grid, block, 0, s, p); break;
+        default: hipLaunchKernelGGL(fmha::merge_kernel<512>, grid, block, 0, s, p); break;
+    }
+    return hipGetLastError() == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+}
+
+const char *fmha_status_string(int status) {
+    switch (status) {
+        case FMHA_OK: return "FMHA_OK: success";
+        case FMHA_ERR_INVALID_ARG: return "FMHA_ERR_INVALID_ARG: null pointer, non-positive size, n_h not a "
+                                          "multiple of n_kv_h, bad mask arguments or split_len";
+        case FMHA_ERR_UNSUPPORTED: return "FMHA_ERR_UNSUPPORTED: head dim must be 64, 128, 256 or 512 and T at most 128";
+        case FMHA_ERR_ALIGNMENT: return "FMHA_ERR_ALIGNMENT: pointers must be 16-byte aligned and strides multiples of 8 elements";
+        case FMHA_ERR_LAUNCH: return "FMHA_ERR_LAUNCH: the HIP kernel launch failed";
+        default: return "unknown fmha status";
+    }
+}
+
+}  // extern "C"

@@ -49,18 +49,24 @@ class Workload:
 
 
 def _draw(g: torch.Generator, shape, dist: str, sigma: float) -> torch.Tensor:
+    dev = g.device
     if dist == "normal":
-        x = torch.randn(shape, generator=g, dtype=torch.float32) * sigma
+        x = torch.randn(shape, generator=g, dtype=torch.float32, device=dev) * sigma
     elif dist == "uniform":
-        x = torch.rand(shape, generator=g, dtype=torch.float32) * 2.0 - 1.0
+        x = torch.rand(shape, generator=g, dtype=torch.float32, device=dev) * 2.0 - 1.0
     else:
         raise ValueError(dist)
     return x.to(torch.bfloat16)
 
 
-def make_qkv(w: Workload, seed: Optional[int] = None):
-    """Returns (q, k, v) as bf16 CPU tensors for workload w."""
-    g = torch.Generator(device="cpu")
+def make_qkv(w: Workload, seed: Optional[int] = None, device: str = "cpu"):
+    """Returns (q, k, v) as bf16 tensors for workload w.
+
+    device="cpu" draws with the CPU generator (the recipe above).  For the
+    gigabyte-sized workloads device="cuda" draws with the seeded device
+    generator instead (same recipe, a different random stream); whoever
+    checks the result copies those exact bf16 tensors to the host."""
+    g = torch.Generator(device=device)
     g.manual_seed(w.seed if seed is None else seed)
     q = _draw(g, (w.batch, w.T, w.n_h, w.hd), w.q_dist, w.sigma)
     k = _draw(g, (w.batch, w.s_k, w.n_kv_h, w.hd), w.k_dist, w.sigma)

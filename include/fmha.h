@@ -1,0 +1,156 @@
+/*
+ * fmha.h -- C ABI of libfmha.so, fused multi-head attention for AMD MI355X
+ * (gfx950, CDNA4).
+ *
+ * What every entry point computes.  For batch b, query head h and query row
+ * i (0 <= i < T), with kv = h / (n_h / n_kv_h) and pos_i = s_k - T + i (the
+ * T queries are the last T positions of the sequence):
+ *
+ *   key j is visible iff j < s_k and (causal == 0 or j <= pos_i)
+ *                        and (window == 0 or j > pos_i - window)
+ *   s_j   = scale * <Q[b,i,h,:], K[b,j,kv,:]>
+ *   O     = sum_j softmax(s)_j * V[b,j,kv,:]   over visible j
+ *   lse   = ln sum_j exp(s_j)                  over visible j (natural log)
+ *
+ * Sources (nvfp4-megamoe-kernel pages, directory dsv4/):
+ *   - "CURRENT_ISSUE.md: UMMA FMHA -- Full Pipeline + Production",
+ *     section "What's working": the fused QK -> softmax -> PV pipeline;
+ *     section "Key lessons": the product Q.K is taken unscaled and the
+ *     1/sqrt(HD) factor is applied in the softmax (here `scale`, which the
+ *     caller sets, normally to 1/sqrt(hd));
+ *     section "Next steps", item 4: KV lengths over many tiles combined by
+ *     the D5 merge O = sum_i exp(lse_i) O_i / sum_i exp(lse_i).
+ *   - commit log at e4ee9fdc: one workgroup grid over (head, batch), MQA
+ *     expressed as a K/V head stride of 0, a pure C API loaded through
+ *     ctypes, one launch with no device synchronisation, the multi-tile
+ *     kernel's running max / running sum (online softmax) over KV tiles.
+ *   - commit log at 593bc25a: the sliding-window mask (D3) and the causal
+ *     mask (D4) of the reference kernel.
+ * A row with no visible key yields O = 0 and lse = -inf.
+ *
+ * Conventions shared by all entry points
+ *   - Element types: q, k, v and o are bfloat16 bit patterns (uint16_t in
+ *     memory); lse, o_part and lse_part are float32.  Accumulation and the
+ *     softmax are float32; o is rounded to bf16 to nearest-even.
+ *   - Layout: every tensor is addressed through an fmha_strides triple in
+ *     ELEMENTS: element (b, token, head, d) lives at
+ *     base + b*batch + token*token_stride + head*head + d.  The head dimension
+ *     is contiguous (stride 1).  The natural layouts are
+ *     q, o [batch][T][n_h][hd] and k, v [batch][s_k][n_kv_h][hd].
+ *     A K/V head stride of 0 with n_kv_h == n_h is MQA and gives the same
+ *     result as n_kv_h == 1.
+ *   - Ownership: all pointers are DEVICE memory owned by the caller.  The
+ *     library never allocates, frees or retains memory and keeps no mutable
+ *     global state; calls are thread-safe.
+ *   - Asynchrony: every call enqueues its kernels on `stream` (a
+ *     hipStream_t; NULL is the default stream) and returns without
+ *     synchronising.  Outputs are valid once the stream reaches that point.
+ *   - Errors: the return value is an fmha_status.  Arguments are validated
+ *     on the host before any HIP call; on a validation error nothing is
+ *     launched and no output is touched.  FMHA_ERR_LAUNCH reports a HIP
+ *     launch failure (hipGetLastError after the launch).  Nothing is
+ *     printed and no exception crosses the ABI.
+ *   - Alignment: every pointer must be 16-byte aligned and every batch,
+ *     token and head stride a multiple of 8 elements (0 is allowed for a
+ *     K/V head stride): the kernels move 16-byte vectors.
+ *   - Supported sizes: hd in {64, 128, 256, 512}; 1 <= T <= 128;
+ *     s_k >= 1; n_h a multiple of n_kv_h.  With causal or window set, T
+ *     must not exceed s_k.
+ */
+#ifndef FMHA_H
+#define FMHA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Strides of a 4-D [batch][token][head][hd] tensor, in elements. */
+typedef struct {
+    int64_t batch;
+    int64_t token;
+    int64_t head;
+} fmha_strides;
+
+typedef enum {
+    FMHA_OK = 0,
+    FMHA_ERR_INVALID_ARG = 1, /* null pointer, size <= 0, n_h % n_kv_h != 0, bad mask
+                                 arguments, T > s_k with a mask, split_len <= 0 */
+    FMHA_ERR_UNSUPPORTED = 2, /* hd not in {64,128,256,512}, or T > 128 */
+    FMHA_ERR_ALIGNMENT = 3,   /* pointer not 16-byte aligned or stride not a multiple of 8 */
+    FMHA_ERR_LAUNCH = 4       /* the HIP launch failed */
+} fmha_status;
+
+/*
+ * fmha_forward -- fused attention in one launch.
+ *
+ * Computes O and (optionally) lse as defined above, over all s_k keys, with
+ * the online softmax (running max and running sum, rescaling the partial
+ * output as each 32-key slice arrives) of the multi-tile kernel in the
+ * e4ee9fdc commit log.
+ *
+ *   q      [batch][T][n_h][hd]      bf16, strides q_st
+ *   k, v   [batch][s_k][n_kv_h][hd] bf16, strides k_st, v_st (head 0 = MQA)
+ *   o      [batch][T][n_h][hd]      bf16, strides o_st (written)
+ *   lse    [batch][n_h][T]          fp32, dense (written); may be NULL
+ *   scale  multiplies the unscaled dot product (normally 1/sqrt(hd))
+ *   window 0 = none; else only keys j > pos_i - window stay visible
+ *   causal 0 or 1
+ *   stream hipStream_t or NULL
+ */
+int fmha_forward(const void *q, const void *k, const void *v, void *o, float *lse,
+                 int batch, int n_h, int n_kv_h, int T, int s_k, int hd,
+                 fmha_strides q_st, fmha_strides k_st, fmha_strides v_st, fmha_strides o_st,
+                 float scale, int window, int causal, void *stream);
+
+/*
+ * fmha_decode_splitkv -- attention per KV partition (split-KV, "D2
+ * multi-CTA" in the 593bc25a log; partitions merged by the D5 formula of
+ * "Next steps", item 4).
+ *
+ * Partition p covers keys [p*split_len, min((p+1)*split_len, s_k)),
+ * p = 0 .. n_split-1 with n_split = ceil(s_k / split_len).  For each
+ * (b, h, i, p) it writes the attention restricted to that range, NORMALISED
+ * within the partition, and its lse; a partition with no visible key gets
+ * O_p = 0 and lse_p = -inf.  Any T in 1..128 is accepted (decode is T = 1).
+ *
+ *   o_part   [batch][n_h][T][n_split][hd] fp32, dense (written)
+ *   lse_part [batch][n_h][T][n_split]     fp32, dense (written)
+ * The other arguments are as for fmha_forward.  Feed both outputs to
+ * fmha_lse_merge on the same stream.
+ */
+int fmha_decode_splitkv(const void *q, const void *k, const void *v,
+                        float *o_part, float *lse_part,
+                        int batch, int n_h, int n_kv_h, int T, int s_k, int hd,
+                        fmha_strides q_st, fmha_strides k_st, fmha_strides v_st,
+                        float scale, int window, int causal, int split_len, void *stream);
+
+/*
+ * fmha_lse_merge -- the D5 merge ("Next steps", item 4 of CURRENT_ISSUE.md):
+ *   O   = sum_p exp(lse_p) O_p / sum_p exp(lse_p)
+ *   lse = ln sum_p exp(lse_p)
+ * evaluated with max_p lse_p factored out.  Partitions with lse_p = -inf
+ * carry no weight; a row whose partitions are all -inf gets O = 0 and
+ * lse = -inf.
+ *
+ *   o_part   [batch][n_h][T][n_split][hd] fp32, dense (read)
+ *   lse_part [batch][n_h][T][n_split]     fp32, dense (read)
+ *   o        [batch][T][n_h][hd]          bf16, strides o_st (written)
+ *   lse      [batch][n_h][T]              fp32, dense (written); may be NULL
+ * Errors: FMHA_ERR_INVALID_ARG for null inputs/o or sizes <= 0,
+ * FMHA_ERR_UNSUPPORTED for hd outside {64,128,256,512}, FMHA_ERR_ALIGNMENT
+ * as above.
+ */
+int fmha_lse_merge(const float *o_part, const float *lse_part, void *o, float *lse,
+                   int batch, int n_h, int T, int hd, int n_split,
+                   fmha_strides o_st, void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *fmha_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FMHA_H */

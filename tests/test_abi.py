@@ -1,0 +1,109 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects each class of invalid argument with its status
+code before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import head_attention_fmha_amd as fa
+from head_attention_fmha_amd import FmhaStrides
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, ALIGN, LAUNCH = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.library_path()):
+        from head_attention_fmha_amd.build import build_library
+        build_library()
+    return fa.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "fmha.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(fmha_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    assert declared_functions() == ["fmha_decode_splitkv", "fmha_forward", "fmha_lse_merge", "fmha_status_string"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in (OK, INVALID, UNSUPPORTED, ALIGN, LAUNCH):
+        s = fa.fmha_status_string(code)
+        assert s and "unknown" not in s
+    assert "unknown" in fa.fmha_status_string(99)
+
+
+# fake, 256-byte aligned device addresses: validation must fail before any use
+QP, KP, VP, OP, LP = (ctypes.c_void_p(0x10000 * (i + 1)) for i in range(5))
+
+
+def dense(T, n_h, hd):
+    return FmhaStrides(T * n_h * hd, n_h * hd, hd)
+
+
+def fwd(lib, q=QP, k=KP, v=VP, o=OP, lse=LP, b=2, n_h=8, n_kv_h=2, T=4, s_k=64, hd=128,
+        q_st=None, k_st=None, v_st=None, o_st=None, scale=0.1, window=0, causal=1):
+    q_st = q_st or dense(T, n_h, hd)
+    k_st = k_st or dense(s_k, n_kv_h, hd)
+    v_st = v_st or dense(s_k, n_kv_h, hd)
+    o_st = o_st or dense(T, n_h, hd)
+    return lib.fmha_forward(q, k, v, o, lse, b, n_h, n_kv_h, T, s_k, hd, q_st, k_st, v_st, o_st,
+                            scale, window, causal, None)
+
+
+def split(lib, split_len=16, q=QP, o_part=OP, lse_part=LP, T=1, s_k=64, hd=128, window=0, causal=0):
+    st_q = dense(T, 8, hd)
+    st_k = dense(s_k, 2, hd)
+    return lib.fmha_decode_splitkv(q, KP, VP, o_part, lse_part, 2, 8, 2, T, s_k, hd, st_q, st_k, st_k,
+                                   0.1, window, causal, split_len, None)
+
+
+def merge(lib, o_part=QP, lse_part=KP, o=OP, b=2, n_h=8, T=1, hd=128, n_split=4, o_st=None):
+    o_st = o_st or dense(T, n_h, hd)
+    return lib.fmha_lse_merge(o_part, lse_part, o, None, b, n_h, T, hd, n_split, o_st, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(o=None), INVALID),
+    (dict(b=0), INVALID), (dict(n_h=0), INVALID), (dict(n_kv_h=0), INVALID), (dict(T=0), INVALID),
+    (dict(s_k=0), INVALID), (dict(hd=0), INVALID), (dict(n_h=8, n_kv_h=3), INVALID),
+    (dict(causal=2), INVALID), (dict(window=-1), INVALID), (dict(T=65, s_k=64), INVALID),
+    (dict(T=65, s_k=64, causal=0, window=4), INVALID),
+    (dict(hd=96), UNSUPPORTED), (dict(hd=1024), UNSUPPORTED), (dict(T=129, s_k=256), UNSUPPORTED),
+    (dict(q=ctypes.c_void_p(0x10008)), ALIGN), (dict(o=ctypes.c_void_p(0x50004)), ALIGN),
+    (dict(lse=ctypes.c_void_p(0x50002)), ALIGN),
+    (dict(q_st=FmhaStrides(4 * 8 * 128, 8 * 128 + 4, 128)), ALIGN),
+    (dict(k_st=FmhaStrides(64 * 256, 256, 130)), ALIGN),
+    (dict(o_st=FmhaStrides(-8, 1024, 128)), ALIGN),
+])
+def test_forward_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(split_len=0), INVALID), (dict(split_len=-5), INVALID), (dict(o_part=None), INVALID),
+    (dict(lse_part=None), INVALID), (dict(hd=80), UNSUPPORTED), (dict(T=2, s_k=1, causal=1), INVALID),
+    (dict(lse_part=ctypes.c_void_p(0x50004)), ALIGN),
+])
+def test_splitkv_rejects(lib, kw, code):
+    assert split(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o_part=None), INVALID), (dict(lse_part=None), INVALID), (dict(o=None), INVALID),
+    (dict(n_split=0), INVALID), (dict(b=0), INVALID), (dict(hd=32), UNSUPPORTED),
+    (dict(lse_part=ctypes.c_void_p(0x20004)), ALIGN), (dict(o_st=FmhaStrides(1024, 1024, 12)), ALIGN),
+])
+def test_merge_rejects(lib, kw, code):
+    assert merge(lib, **kw) == code

@@ -1,0 +1,304 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on
+the same seeded bf16 inputs.  Needs an MI355X; every case prints its name
+before touching the GPU."""
+import itertools
+import math
+import sys
+
+import pytest
+import torch
+
+import oracle
+import head_attention_fmha_amd as fa
+from head_attention_fmha_amd import inputs as I
+from attn_compare import check_attention
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def announce(request):
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    fa.load_library()
+    sys.stderr.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.stderr.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+def nan_bf16(*shape):
+    return torch.full(shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+
+
+def nan_f32(*shape):
+    return torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
+
+
+def gpu_forward(q, k, v, scale, causal=False, window=0, o=None, want_lse=True):
+    qd, kd, vd = (x if x.is_cuda else x.to(DEV) for x in (q, k, v))
+    b, T, n_h, hd = qd.shape
+    if o is None:
+        o = nan_bf16(b, T, n_h, hd)
+    lse = nan_f32(b, n_h, T) if want_lse else None
+    fa.fmha_forward(qd, kd, vd, o, lse, scale=scale, window=window, causal=causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def gpu_split(q, k, v, scale, split_len, causal=False, window=0):
+    qd, kd, vd = (x if x.is_cuda else x.to(DEV) for x in (q, k, v))
+    b, T, n_h, hd = qd.shape
+    ns = fa.n_split_for(kd.shape[1], split_len)
+    o_part = nan_f32(b, n_h, T, ns, hd)
+    lse_part = nan_f32(b, n_h, T, ns)
+    fa.fmha_decode_splitkv(qd, kd, vd, o_part, lse_part, split_len=split_len, scale=scale,
+                           window=window, causal=causal)
+    o = nan_bf16(b, T, n_h, hd)
+    lse = nan_f32(b, n_h, T)
+    fa.fmha_lse_merge(o_part, lse_part, o, lse)
+    torch.cuda.synchronize()
+    return o, lse, o_part, lse_part
+
+
+def check_workload(w: I.Workload):
+    q, k, v = I.make_qkv(w)
+    o_ref, lse_ref = oracle.attention(q, k, v, w.scale, causal=w.causal, window=w.window)
+    o, lse = gpu_forward(q, k, v, w.scale, w.causal, w.window)
+    return check_attention(o, lse, o_ref, lse_ref, what=w.name)
+
+
+# ---------------------------------------------------------------------------
+# The five target workloads
+# ---------------------------------------------------------------------------
+
+def test_single_head_decode():
+    check_workload(I.SINGLE_HEAD_DECODE)
+
+
+@pytest.mark.parametrize("w", I.MQA_DECODE_GRID, ids=lambda w: w.name)
+def test_mqa_decode_grid(w):
+    check_workload(w)
+
+
+@pytest.mark.parametrize("hd,s_k", [(64, 128), (512, 384)])
+def test_mqa_head_stride_zero_is_bitwise_one_kv_head(hd, s_k):
+    w = I.mqa_decode(hd, s_k)
+    q, k, v = I.make_qkv(w)
+    o1, l1 = gpu_forward(q, k, v, w.scale)
+    kd, vd = k.to(DEV), v.to(DEV)
+    k0 = kd.expand(w.batch, s_k, w.n_h, hd)
+    v0 = vd.expand(w.batch, s_k, w.n_h, hd)
+    assert k0.stride(2) == 0
+    o2, l2 = gpu_forward(q, k0, v0, w.scale)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_gqa_splitkv_decode_full_size():
+    """The full 1 GiB workload on the GPU; the oracle checks sampled batches."""
+    w = I.GQA_SPLITKV_DECODE
+    q, k, v = I.make_qkv(w, device=DEV)
+    o, lse, o_part, lse_part = gpu_split(q, k, v, w.scale, w.split_len)
+    for bi in (0, 13, w.batch - 1):
+        qs, ks, vs = (x[bi:bi + 1].cpu() for x in (q, k, v))
+        o_ref, lse_ref = oracle.attention(qs, ks, vs, w.scale)
+        check_attention(o[bi:bi + 1], lse[bi:bi + 1], o_ref, lse_ref, what=f"{w.name} batch {bi}")
+        op_ref, lp_ref = oracle.split(qs, ks, vs, w.scale, w.split_len)
+        perr = (o_part[bi:bi + 1].cpu().double() - op_ref).abs().max().item()
+        lerr = (lse_part[bi:bi + 1].cpu().double() - lp_ref).abs().max().item()
+        assert perr <= 1e-2 and lerr <= 1e-3, (perr, lerr)
+
+
+def test_gqa_splitkv_decode_small_full_compare():
+    """Same shape class at a size the oracle checks completely."""
+    w = I.Workload("gqa_splitkv_small", 3, 64, 8, 1, 1000, 128, v_dist="uniform", split_len=128)
+    q, k, v = I.make_qkv(w)
+    o, lse, o_part, lse_part = gpu_split(q, k, v, w.scale, w.split_len)
+    o_ref, lse_ref = oracle.attention(q, k, v, w.scale)
+    check_attention(o, lse, o_ref, lse_ref, what=w.name)
+    op_ref, lp_ref = oracle.split(q, k, v, w.scale, w.split_len)
+    assert (o_part.cpu().double() - op_ref).abs().max().item() <= 1e-2
+    assert (lse_part.cpu().double() - lp_ref).abs().max().item() <= 1e-3
+
+
+@pytest.mark.parametrize("w", I.MHA_PREFILL_GRID, ids=lambda w: w.name)
+def test_mha_causal_prefill_grid(w):
+    check_workload(w)
+
+
+def test_swa_mqa_prefill_and_unread_keys():
+    w = I.SWA_MQA_PREFILL
+    q, k, v = I.make_qkv(w)
+    o_ref, lse_ref = oracle.attention(q, k, v, w.scale, causal=True, window=w.window)
+    o, lse = gpu_forward(q, k, v, w.scale, True, w.window)
+    check_attention(o, lse, o_ref, lse_ref, what=w.name)
+    # keys 0..3840 are outside every query's window: poison them; the result
+    # must not change by a single bit (the kernel never reads them)
+    first_visible = w.s_k - w.T - w.window + 1
+    assert first_visible == 3841
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :first_visible] = float("nan")
+    v2[:, :first_visible] = float("nan")
+    o2, lse2 = gpu_forward(k=k2, v=v2, q=q, scale=w.scale, causal=True, window=w.window)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+# ---------------------------------------------------------------------------
+# Edge cases: ragged tails, masks, layouts, head groups
+# ---------------------------------------------------------------------------
+
+EDGE = list(itertools.product([64, 128, 256, 512], [(1, 1), (4, 1), (16, 2)], [1, 3, 17, 33, 128]))
+
+
+@pytest.mark.parametrize("hd,heads,T", EDGE, ids=lambda x: str(x))
+def test_ragged_shapes_all_masks(hd, heads, T):
+    n_h, n_kv_h = heads
+    seed = hd * 1000 + n_h * 10 + T
+    for s_k, causal, window in ((max(T, 1), True, 0), (T + 6, False, 0), (T + 100, True, 0), (127 + T, True, 37),
+                                (129, False, 0), (200 + T, True, 128), (max(T, 7), True, 1)):
+        if causal and T > s_k:
+            continue
+        q = I.randn_bf16((2, T, n_h, hd), seed)
+        k = I.randn_bf16((2, s_k, n_kv_h, hd), seed + 1)
+        v = I.randn_bf16((2, s_k, n_kv_h, hd), seed + 2)
+        scale = 1.0 / math.sqrt(hd)
+        o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=causal, window=window)
+        o, lse = gpu_forward(q, k, v, scale, causal, window)
+        check_attention(o, lse, o_ref, lse_ref, what=f"hd{hd} h{n_h}/{n_kv_h} T{T} sk{s_k} c{causal} w{window}")
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+def test_single_key_is_exact(hd):
+    """s_k = 1: the weight is exactly 1, so O is V_0 bit for bit."""
+    q = I.randn_bf16((2, 1, 8, hd), 1)
+    k = I.randn_bf16((2, 1, 2, hd), 2)
+    v = I.randn_bf16((2, 1, 2, hd), 3)
+    o, lse = gpu_forward(q, k, v, 0.1)
+    ref = v.repeat_interleave(4, dim=2).to(DEV)
+    assert torch.equal(o, ref)
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 50)])
+def test_constant_v_rows_are_returned_exactly(hd, causal, window):
+    """Regression for normalising twice: constant V rows must come back unchanged."""
+    b, T, n_h, s_k = 2, 5, 4, 300
+    q = I.randn_bf16((b, T, n_h, hd), 5, sigma=2.0)
+    k = I.randn_bf16((b, s_k, 1, hd), 6, sigma=2.0)
+    c = I.randn_bf16((b, 1, 1, hd), 7)
+    v = c.expand(b, s_k, 1, hd).contiguous()
+    o, _ = gpu_forward(q, k, v, 1.0 / math.sqrt(hd), causal, window)
+    assert torch.equal(o.cpu(), c.expand(b, T, n_h, hd))
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 9), (True, 300)])
+def test_flat_scores_give_log_count(causal, window):
+    """scale = 0: lse = ln(visible keys) in closed form, O = mean of visible V."""
+    b, T, n_h, s_k, hd = 1, 40, 2, 333, 128
+    q, k, v = (I.randn_bf16(s, i) for i, s in enumerate([(b, T, n_h, hd), (b, s_k, 1, hd), (b, s_k, 1, hd)]))
+    o, lse = gpu_forward(q, k, v, 0.0, causal, window)
+    for i in range(T):
+        pos = s_k - T + i
+        hi = pos + 1 if causal else s_k
+        lo = max(0, pos - window + 1) if window else 0
+        assert abs(lse[0, 0, i].item() - math.log(hi - lo)) < 1e-5
+        mean = v[0, lo:hi, 0].double().mean(0)
+        assert (o[0, i, 0].cpu().double() - mean).abs().max().item() < 1e-2
+
+
+def test_strided_layouts():
+    """BHSD-ordered Q/O memory, padded token strides for K/V, strided output."""
+    b, T, n_h, n_kv_h, s_k, hd = 2, 17, 8, 2, 150, 128
+    scale = 1.0 / math.sqrt(hd)
+    q = I.randn_bf16((b, T, n_h, hd), 11)
+    k = I.randn_bf16((b, s_k, n_kv_h, hd), 12)
+    v = I.randn_bf16((b, s_k, n_kv_h, hd), 13)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=True)
+    q_bhsd = q.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3)      # memory [b][h][T][hd]
+    kpad = torch.zeros((b, s_k, n_kv_h + 1, hd + 64), dtype=torch.bfloat16, device=DEV)
+    kpad[:, :, :n_kv_h, :hd] = k.to(DEV)
+    vpad = torch.zeros((b, s_k + 3, n_kv_h, hd), dtype=torch.bfloat16, device=DEV)
+    vpad[:, :s_k] = v.to(DEV)
+    k_view = kpad[:, :, :n_kv_h, :hd]
+    v_view = vpad[:, :s_k]
+    obuf = nan_bf16(b, n_h, T, hd + 16)
+    o_view = obuf[..., :hd].permute(0, 2, 1, 3)
+    assert not q_bhsd.is_contiguous() and not k_view.is_contiguous() and not o_view.is_contiguous()
+    o, lse = gpu_forward(q_bhsd, k_view, v_view, scale, True, 0, o=o_view)
+    check_attention(o, lse, o_ref, lse_ref, what="strided")
+    assert torch.isnan(obuf[..., hd:].float()).all(), "writes outside the output view"
+
+
+def test_lse_is_optional():
+    q, k, v = (I.randn_bf16(s, i) for i, s in enumerate([(1, 4, 4, 64), (1, 64, 4, 64), (1, 64, 4, 64)]))
+    o1, _ = gpu_forward(q, k, v, 0.125, True, 0, want_lse=False)
+    o2, _ = gpu_forward(q, k, v, 0.125, True, 0)
+    assert torch.equal(o1, o2)
+
+
+def test_prefill_rows_match_decode_at_their_positions():
+    b, T, n_h, s_k, hd = 1, 16, 4, 260, 128
+    q, k, v = (I.randn_bf16(s, 30 + i) for i, s in enumerate([(b, T, n_h, hd), (b, s_k, 4, hd), (b, s_k, 4, hd)]))
+    o, lse = gpu_forward(q, k, v, 0.1, True, 0)
+    for i in (0, 7, 15):
+        pos = s_k - T + i
+        od, ld = gpu_forward(q[:, i:i + 1].contiguous(), k[:, :pos + 1].contiguous(), v[:, :pos + 1].contiguous(),
+                             0.1, True, 0)
+        assert (o[:, i].float() - od[:, 0].float()).abs().max().item() <= 1e-2
+        assert (lse[:, :, i] - ld[:, :, 0]).abs().max().item() <= 1e-4
+
+
+def test_results_are_deterministic():
+    w = I.mha_causal_prefill(128, 512, 128)
+    q, k, v = (x.to(DEV) for x in I.make_qkv(w))
+    o1, l1 = gpu_forward(q, k, v, w.scale, True)
+    o2, l2 = gpu_forward(q, k, v, w.scale, True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    a = gpu_split(q, k, v, w.scale, 100, causal=True)
+    c = gpu_split(q, k, v, w.scale, 100, causal=True)
+    for x, y in zip(a, c):
+        assert torch.equal(x, y)
+
+
+# ---------------------------------------------------------------------------
+# Split-KV and the merge kernel
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+@pytest.mark.parametrize("split_len,causal,window,T", [(128, False, 0, 1), (37, False, 0, 1), (64, True, 0, 8),
+                                                      (100, True, 70, 20), (1000, False, 0, 2)])
+def test_split_then_merge_matches_oracle(hd, split_len, causal, window, T):
+    b, n_h, n_kv_h, s_k = 2, 16, 2, 555
+    q = I.randn_bf16((b, T, n_h, hd), hd + T)
+    k = I.randn_bf16((b, s_k, n_kv_h, hd), hd + T + 1)
+    v = I.randn_bf16((b, s_k, n_kv_h, hd), hd + T + 2)
+    scale = 1.0 / math.sqrt(hd)
+    o, lse, o_part, lse_part = gpu_split(q, k, v, scale, split_len, causal, window)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=causal, window=window)
+    check_attention(o, lse, o_ref, lse_ref, what="split+merge")
+    op_ref, lp_ref = oracle.split(q, k, v, scale, split_len, causal=causal, window=window)
+    fin = torch.isfinite(lp_ref)
+    lp = lse_part.cpu().double()
+    assert torch.all(lp[~fin] == -math.inf)
+    assert (lp[fin] - lp_ref[fin]).abs().max().item() <= 1e-3
+    assert torch.all(o_part.cpu()[~fin] == 0)
+    assert (o_part.cpu().double() - op_ref).abs().max().item() <= 1e-2
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+@pytest.mark.parametrize("n_split", [1, 3, 64, 77])
+def test_merge_kernel_against_oracle_merge(hd, n_split):
+    b, n_h, T = 3, 5, 2
+    o_part = I.rand_f32((b, n_h, T, n_split, hd), seed=hd + n_split, lo=-2.0, hi=2.0)
+    lse_part = I.rand_f32((b, n_h, T, n_split), seed=hd + n_split + 1, lo=-30.0, hi=30.0)
+    if n_split > 1:
+        lse_part[:, :, :, 1] = -math.inf          # an empty partition: no weight,
+        o_part[:, :, :, 1] = float("nan")         # whatever its O holds
+    lse_part[0, 0, 0, :] = -math.inf              # a row with no visible key at all
+    o_ref, lse_ref = oracle.merge(o_part.double(), lse_part.double())
+    o_ref[0, 0, 0] = 0.0
+    o = nan_bf16(b, T, n_h, hd)
+    lse = nan_f32(b, n_h, T)
+    fa.fmha_lse_merge(o_part.to(DEV), lse_part.to(DEV), o, lse)
+    torch.cuda.synchronize()
+    check_attention(o, lse, o_ref.permute(0, 2, 1, 3), lse_ref, lse_tol=1e-5, what="merge")
