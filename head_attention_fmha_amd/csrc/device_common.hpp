@@ -35,6 +35,19 @@ __device__ __forceinline__ float xor_shuffle(float x, int mask) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; a field at its maximum does not wait).
+constexpr int waitcnt_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
+// 16 bytes per lane straight from global memory into LDS
+// (global_load_lds_dwordx4): lane L's data lands at lds_base + 16*L.  The
+// LDS write completes asynchronously and is tracked by vmcnt, not by the
+// compiler: wait with s_waitcnt vmcnt before reading the destination.
+__device__ __forceinline__ void load_lds_16(const void *gptr, void *lds_base) {
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 

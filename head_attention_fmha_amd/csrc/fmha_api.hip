@@ -10,6 +10,7 @@
 #include <cstdint>
 
 #include "fmha.h"
+#include "decode_kernel.hpp"
 #include "fwd_kernel.hpp"
 #include "merge_kernel.hpp"
 
@@ -76,6 +77,18 @@ FwdParams make_params(const void *q, const void *k, const void *v, int batch, in
 template <int HD, bool SPLIT>
 hipError_t launch_hd(FwdParams p, hipStream_t stream) {
     constexpr int NWK_MAX = HD <= 128 ? 4 : (HD == 256 ? 2 : 1);
+    if constexpr (HD <= 128) {
+        if (p.rows <= 16) {
+            // one 16-row tile per (batch, kv head, partition): the bandwidth kernel
+            p.n_row_blocks = 1;
+            const int64_t units = (int64_t)p.n_split * p.n_kv_h * p.batch;
+            if (units > 0x7fffffff) return hipErrorInvalidConfiguration;
+            p.n_units = (int)units;
+            p.xcd_remap = (p.n_units % 8 == 0) ? 1 : 0;
+            hipLaunchKernelGGL((fmha::decode_kernel<HD, SPLIT>), dim3(p.n_units), dim3(256), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
     int nwr, nwk;
     if (p.rows <= 16) {
         nwr = 1; nwk = NWK_MAX;
@@ -167,7 +180,13 @@ int fmha_lse_merge(const float *o_part, const float *lse_part, void *o, float *l
     p.n_h = n_h;
     p.T = T;
     p.n_split = n_split;
-    const int rpw = 256 / (hd / 4);
+    int rpw;
+    switch (hd) {
+        case 64: rpw = fmha::MergeShape<64>::RPW; break;
+        case 128: rpw = fmha::MergeShape<128>::RPW; break;
+        case 256: rpw = fmha::MergeShape<256>::RPW; break;
+        default: rpw = fmha::MergeShape<512>::RPW; break;
+    }
     const int64_t blocks = (rows + rpw - 1) / rpw;
     if (rows > 0x7fffffff || blocks > 0x7fffffff) return FMHA_ERR_UNSUPPORTED;
     p.rows = (int)rows;
