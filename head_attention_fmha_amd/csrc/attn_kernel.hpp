@@ -1,0 +1,328 @@
+// attn_kernel.hpp -- the fused attention kernel for gfx950.
+//
+// One workgroup (4 waves) computes one 16-row tile of one (batch, kv head)
+// over one key range.  A row is one (query position t, query head h) that
+// reads this KV head, numbered r = t * group + (h - kv*group): the GQA/MQA
+// query heads sharing K/V are stacked into the same MFMA tile, and the rows
+// of a tile have the same or adjacent positions (tight mask ranges).
+//
+// The four waves form NK key groups x NH head-dimension parts (HDP = HD/NH
+// columns each, 64 or 128):
+//   * key group g takes keys [c + 32g, c + 32g + 32) of every chunk of
+//     32*NK keys and keeps its own online-softmax state; the NK groups are
+//     merged once at the end, in a fixed order;
+//   * head part j loads only columns [j*HDP, (j+1)*HDP) of K and V, so every
+//     byte of K/V is fetched once per workgroup and the output accumulator
+//     is 16 rows x HDP columns per wave for every hd (<= 32 registers).
+//     The NH partial QK scores of a slice are summed through LDS in a fixed
+//     order, so the NH waves of a key group hold bit-identical scores and
+//     probabilities.
+//
+// Both products are taken transposed, keys in the MFMA M dimension
+// (v_mfma_f32_16x16x32_bf16; lane l = lr + 16*lg):
+//   S^T (keys x rows) = K . Q^T      lane holds S^T[4*lg + j][lr]
+//   O^T (hd x rows)  += V^T . P^T    lane holds O^T[4*lg + j][lr]
+// so all softmax state of row lr lives in lanes lr, lr+16, lr+32, lr+48:
+// the running max needs two butterfly steps, the rescale factor is a
+// per-lane scalar, and the probabilities leave the QK result registers in
+// exactly the B-operand layout of the PV product (the 32-key reduction
+// index is permuted identically in both PV operands).
+//
+// Data movement per 32-key slice and wave:
+//   * K: HBM -> QK A-operand registers (lane lr + 16*lg loads 16 bytes of
+//     key lr at column offset 32*s + 8*lg) -- no LDS round trip;
+//   * V: HBM -> a wave-private LDS slice with global_load_lds_dwordx4 (no
+//     registers held in flight); a run of lanes covers one whole key-row
+//     part, so loads stay coalesced.  The 16-byte chunks of LDS key row k
+//     are rotated by 2*((k/4) % 4) positions: the PV operand gathers V[k][d]
+//     for keys 4*lg + j across the four lane groups, and the rotation puts
+//     the four groups on disjoint LDS banks.
+//
+// Softmax: online (running max m, running sum l, rescale of the partial
+// output by exp(m_old - m_new) when a slice raises the max), as in the
+// multi-tile kernel of the e4ee9fdc commit log of the pages, with one
+// division by the sum in the epilogue.  Scores are kept in base 2
+// (x = q.k * scale * log2 e), so exp is one v_exp_f32.  The output is
+// normalised by the sum of the same bf16-rounded weights the PV product
+// consumes (an exact convex combination of V rows); lse uses the fp32 sum.
+#pragma once
+
+#include "device_common.hpp"
+#include "params.hpp"
+
+namespace fmha {
+
+template <int HD, int NK, int NH>
+struct AttnShape {
+    static_assert(NK * NH == 4, "four waves per workgroup");
+    static constexpr int HDP = HD / NH;               // head-dim columns per wave
+    static constexpr int KSTEPS = HDP / 32;           // QK MFMA steps
+    static constexpr int NB = HDP / 16;               // 16-column blocks of O^T
+    static constexpr int CHUNKS = HDP / 8;            // 16-byte chunks per key-row part
+    static constexpr int ROW_BYTES = HDP * 2;         // LDS key-row part
+    static constexpr int KEYS_PER_LOAD = 64 / CHUNKS;  // keys per wave-wide 16-byte load
+    static constexpr int VLOADS = 32 / KEYS_PER_LOAD;
+    static constexpr int SLOTS = NB * 4 + 3;          // merge record per lane: m, l, lq, O^T
+    static constexpr int V_BYTES = 4 * 32 * ROW_BYTES;
+    static constexpr int M_BYTES = (NK - 1) * NH * SLOTS * 64 * 4;
+    static constexpr int S_BYTES = NH > 1 ? 2 * 4 * 8 * 64 * 4 : 0;  // two parity buffers
+    static constexpr int VM_BYTES = V_BYTES > M_BYTES ? V_BYTES : M_BYTES;
+    static constexpr int LDS_BYTES = VM_BYTES + S_BYTES;
+    static constexpr int MIN_BLOCKS = NH > 1 ? 3 : 4;  // per CU: register budget
+    static_assert(HDP == 64 || HDP == 128, "head-dim part of 64 or 128 columns");
+};
+
+template <int HD, int NK, int NH, bool SPLIT>
+__global__ __launch_bounds__(256, (AttnShape<HD, NK, NH>::MIN_BLOCKS)) void attn_kernel(const FwdParams p) {
+    using S = AttnShape<HD, NK, NH>;
+    constexpr int HDP = S::HDP, KSTEPS = S::KSTEPS, NB = S::NB, CHUNKS = S::CHUNKS;
+    constexpr int ROW_BYTES = S::ROW_BYTES, KEYS_PER_LOAD = S::KEYS_PER_LOAD, VLOADS = S::VLOADS;
+    constexpr int SLOTS = S::SLOTS;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kg = wave / NH;  // key group
+    const int hp = wave % NH;  // head-dim part
+    const int lr = lane & 15;
+    const int lg = lane >> 4;
+
+    // ---- work unit: row tiles fastest (they share K/V through L2), then KV
+    // heads (units reading the same cache rows run together) ------------------
+    int bid = blockIdx.x;
+    if (p.xcd_remap) {
+        const int per = p.n_units >> 3;
+        bid = (bid & 7) * per + (bid >> 3);
+    }
+    const int rb = bid % p.n_row_blocks;
+    bid /= p.n_row_blocks;
+    const int kvh = bid % p.n_kv_h;
+    bid /= p.n_kv_h;
+    const int part = bid % p.n_split;
+    const int b = bid / p.n_split;
+
+    const int row0 = rb * 16;
+    const int row_last = min(row0 + 16, p.rows) - 1;
+    const int pos_lo = p.s_k - p.T + row0 / p.group;
+    const int pos_hi = p.s_k - p.T + row_last / p.group;
+    // key range: the partition, cut to the union of the tile rows' masks
+    int klo = part * p.split_len;
+    int khi = min(klo + p.split_len, p.s_k);
+    if (p.causal) khi = min(khi, pos_hi + 1);
+    if (p.window > 0) klo = max(klo, pos_lo - p.window + 1);
+
+    const int row = row0 + lr;
+    const bool row_ok = row < p.rows;
+    const int t = row_ok ? row / p.group : 0;
+    const int h = kvh * p.group + (row_ok ? row % p.group : 0);
+    const int pos = p.s_k - p.T + t;
+    int r_hi = p.causal ? min(khi, pos + 1) : khi;
+    const int r_lo = p.window > 0 ? max(klo, pos - p.window + 1) : klo;
+    if (!row_ok) r_hi = r_lo;  // no visible key: the row stays at -inf
+
+    const int col0 = hp * HDP;  // first head-dim column of this wave
+    bf16x8 qf[KSTEPS];          // Q^T B operand: Q[row lr][col0 + 32*s + 8*lg + 0..7]
+    {
+        const uint16_t *qp = p.q + (int64_t)b * p.q_sb + (int64_t)t * p.q_st + (int64_t)h * p.q_sh + col0 + 8 * lg;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+            qf[s] = row_ok ? *reinterpret_cast<const bf16x8 *>(qp + 32 * s) : bf16x8{};
+    }
+
+    f32x4 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY;  // running max (base 2), equal in the 4 lanes of a row
+    float l = 0.f;        // this lane's share of the fp32 sum of weights (-> lse)
+    float lq = 0.f;       // the same over the bf16-rounded weights (-> O)
+
+    const uint16_t *kbase = p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh + col0;
+    const uint16_t *vbase = p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh + col0;
+    unsigned char *sV = smem + wave * 32 * ROW_BYTES;
+    float *sS = reinterpret_cast<float *>(smem + S::VM_BYTES);
+    const int v_row_in_load = lane / CHUNKS;
+    const int v_slot = lane % CHUNKS;
+
+    int iter = 0;
+    for (int c = klo; c < khi; c += 32 * NK, ++iter) {
+        const int k0 = c + 32 * kg;
+        const bool active = k0 < khi;  // uniform over the wave
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        if (active) {
+            // the previous slice's V reads are complete before new V lands
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            // V part: HBM -> LDS; keys past khi read key khi-1 (weight 0)
+#pragma unroll
+            for (int it = 0; it < VLOADS; ++it) {
+                const int r = it * KEYS_PER_LOAD + v_row_in_load;
+                const int rot = (2 * ((r >> 2) & 3)) % CHUNKS;
+                const int chunk = (v_slot - rot + CHUNKS) % CHUNKS;
+                const int key = min(k0 + r, khi - 1);
+                load_lds_16(vbase + (int64_t)key * p.v_st + chunk * 8, sV + it * 64 * 16);
+            }
+            // K part: HBM -> QK A-operand registers; keys past khi are masked
+            bf16x8 kf[2][KSTEPS];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const int key = min(k0 + 16 * blk + lr, khi - 1);
+                const uint16_t *kp = kbase + (int64_t)key * p.k_st + 8 * lg;
+#pragma unroll
+                for (int s = 0; s < KSTEPS; ++s) kf[blk][s] = *reinterpret_cast<const bf16x8 *>(kp + 32 * s);
+            }
+            // every load of the slice is issued before the first wait
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+                s0 = mfma_16x16x32(kf[0][s], qf[s], s0);
+                s1 = mfma_16x16x32(kf[1][s], qf[s], s1);
+            }
+        }
+        if constexpr (NH > 1) {
+            // sum the NH head-part scores of this key group (fixed order)
+            float *buf = sS + (iter & 1) * (4 * 8 * 64);
+            if (active) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    buf[(wave * 8 + j) * 64 + lane] = s0[j];
+                    buf[(wave * 8 + 4 + j) * 64 + lane] = s1[j];
+                }
+            }
+            __syncthreads();
+            if (active) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float a = 0.f, c2 = 0.f;
+#pragma unroll
+                    for (int q = 0; q < NH; ++q) {
+                        a += buf[((kg * NH + q) * 8 + j) * 64 + lane];
+                        c2 += buf[((kg * NH + q) * 8 + 4 + j) * 64 + lane];
+                    }
+                    s0[j] = a;
+                    s1[j] = c2;
+                }
+            }
+        }
+        if (active) {
+            // ---- mask, online softmax ---------------------------------------------
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int ka = k0 + 4 * lg + j;
+                const int kb = ka + 16;
+                x[j] = (ka >= r_lo && ka < r_hi) ? s0[j] * p.scale_log2 : -INFINITY;
+                x[4 + j] = (kb >= r_lo && kb < r_hi) ? s1[j] * p.scale_log2 : -INFINITY;
+            }
+            float mx = x[0];
+#pragma unroll
+            for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+            mx = fmaxf(mx, xor_shuffle(mx, 16));
+            mx = fmaxf(mx, xor_shuffle(mx, 32));
+            const float m_new = fmaxf(m, mx);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = fast_exp2(m - m_use);
+            bf16x8 pt;
+            float psum = 0.f, qsum = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float pj = fast_exp2(x[j] - m_use);
+                const __bf16 pb = to_bf16(pj);
+                pt[j] = pb;
+                psum += pj;
+                qsum += (float)pb;
+            }
+            l = l * alpha + psum;
+            lq = lq * alpha + qsum;
+            m = m_new;
+            // ---- V has landed -------------------------------------------------------
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // ---- O^T = alpha O^T + V^T . P^T; item j of lane (lr, lg) is key
+            // 4*lg + j (j < 4) or 16 + 4*lg + (j - 4); both rows rotate by 2*lg -------
+            const int rot = (2 * lg) % CHUNKS;
+            const unsigned char *r0 = sV + (4 * lg) * ROW_BYTES;
+            const unsigned char *r1 = r0 + 16 * ROW_BYTES;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int d = 16 * nb + lr;
+                const int off = (((d >> 3) + rot) % CHUNKS) * 16 + (d & 7) * 2;
+                bf16x8 vt;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    vt[j] = *reinterpret_cast<const __bf16 *>(r0 + j * ROW_BYTES + off);
+                    vt[4 + j] = *reinterpret_cast<const __bf16 *>(r1 + j * ROW_BYTES + off);
+                }
+                acc[nb] = acc[nb] * alpha;
+                acc[nb] = mfma_16x16x32(vt, pt, acc[nb]);
+            }
+        }
+    }
+
+    // full row sums over the four lanes of a row
+    l += xor_shuffle(l, 16);
+    l += xor_shuffle(l, 32);
+    lq += xor_shuffle(lq, 16);
+    lq += xor_shuffle(lq, 32);
+
+    // ---- merge the NK key groups of each head part (fixed order) -----------------
+    if constexpr (NK > 1) {
+        __syncthreads();  // all V slices and score buffers are consumed
+        float *red = reinterpret_cast<float *>(smem);
+        if (kg != 0) {
+            float *mine = red + ((kg - 1) * NH + hp) * SLOTS * 64 + lane;
+            mine[0] = m;
+            mine[64] = l;
+            mine[128] = lq;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) mine[(3 + nb * 4 + j) * 64] = acc[nb][j];
+        }
+        __syncthreads();
+        if (kg != 0) return;
+        float M = m;
+#pragma unroll
+        for (int g = 1; g < NK; ++g) M = fmaxf(M, red[((g - 1) * NH + hp) * SLOTS * 64 + lane]);
+        const float M_use = (M == -INFINITY) ? 0.f : M;
+        const float w0 = fast_exp2(m - M_use);
+        l *= w0;
+        lq *= w0;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = acc[nb] * w0;
+#pragma unroll
+        for (int g = 1; g < NK; ++g) {
+            const float *src = red + ((g - 1) * NH + hp) * SLOTS * 64 + lane;
+            const float wgt = fast_exp2(src[0] - M_use);
+            l += wgt * src[64];
+            lq += wgt * src[128];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[nb][j] += wgt * src[(3 + nb * 4 + j) * 64];
+        }
+        m = M;
+    }
+    if (!row_ok) return;
+
+    // ---- epilogue: one division; lse = (m + log2 l) ln 2 -------------------------
+    const float inv = lq > 0.f ? 1.f / lq : 0.f;
+    const float lse_val = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+    if constexpr (SPLIT) {
+        const int64_t r = (((int64_t)b * p.n_h + h) * p.T + t) * p.n_split + part;
+        float *op = p.o_part + r * HD + col0 + 4 * lg;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f32x4 *>(op + 16 * nb) = acc[nb] * inv;
+        if (hp == 0 && lg == 0) p.lse_part[r] = lse_val;
+    } else {
+        uint16_t *op = p.o + (int64_t)b * p.o_sb + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + col0 + 4 * lg;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            uint2 packed;
+            packed.x = (uint32_t)bf16_bits(acc[nb][0] * inv) | ((uint32_t)bf16_bits(acc[nb][1] * inv) << 16);
+            packed.y = (uint32_t)bf16_bits(acc[nb][2] * inv) | ((uint32_t)bf16_bits(acc[nb][3] * inv) << 16);
+            *reinterpret_cast<uint2 *>(op + 16 * nb) = packed;
+        }
+        if (hp == 0 && lg == 0 && p.lse != nullptr) p.lse[((int64_t)b * p.n_h + h) * p.T + t] = lse_val;
+    }
+}
+
+}  // namespace fmha

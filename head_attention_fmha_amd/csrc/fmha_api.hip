@@ -10,8 +10,7 @@
 #include <cstdint>
 
 #include "fmha.h"
-#include "decode_kernel.hpp"
-#include "fwd_kernel.hpp"
+#include "attn_kernel.hpp"
 #include "merge_kernel.hpp"
 
 namespace {
@@ -70,48 +69,25 @@ FwdParams make_params(const void *q, const void *k, const void *v, int batch, in
     return p;
 }
 
-// Waves per workgroup along rows (NWR) and along keys (NWK).  Few rows per
-// (batch, kv_head) -> split the keys across the waves and merge in LDS;
-// many rows -> give each wave its own 16-row tile sharing the staged keys.
-// NWK is capped per head dim so a chunk of K+V (32*NWK keys) fits in LDS.
+// One workgroup per (16-row tile, KV head, partition, batch).  The four
+// waves split keys (NK groups) and head-dim columns (NH parts of 64 or 128):
+// hd 64/128 -> 4 key groups, hd 256 -> 2 x 2, hd 512 -> 4 head parts.
+template <int HD>
+struct Waves;
+template <> struct Waves<64> { static constexpr int NK = 4, NH = 1; };
+template <> struct Waves<128> { static constexpr int NK = 4, NH = 1; };
+template <> struct Waves<256> { static constexpr int NK = 2, NH = 2; };
+template <> struct Waves<512> { static constexpr int NK = 1, NH = 4; };
+
 template <int HD, bool SPLIT>
 hipError_t launch_hd(FwdParams p, hipStream_t stream) {
-    constexpr int NWK_MAX = HD <= 128 ? 4 : (HD == 256 ? 2 : 1);
-    if constexpr (HD <= 128) {
-        if (p.rows <= 16) {
-            // one 16-row tile per (batch, kv head, partition): the bandwidth kernel
-            p.n_row_blocks = 1;
-            const int64_t units = (int64_t)p.n_split * p.n_kv_h * p.batch;
-            if (units > 0x7fffffff) return hipErrorInvalidConfiguration;
-            p.n_units = (int)units;
-            p.xcd_remap = (p.n_units % 8 == 0) ? 1 : 0;
-            hipLaunchKernelGGL((fmha::decode_kernel<HD, SPLIT>), dim3(p.n_units), dim3(256), 0, stream, p);
-            return hipGetLastError();
-        }
-    }
-    int nwr, nwk;
-    if (p.rows <= 16) {
-        nwr = 1; nwk = NWK_MAX;
-    } else if (p.rows <= 32) {
-        nwr = 2; nwk = NWK_MAX >= 2 ? 2 : 1;
-    } else {
-        nwr = 4; nwk = 1;
-    }
-    p.n_row_blocks = (p.rows + 16 * nwr - 1) / (16 * nwr);
+    p.n_row_blocks = (p.rows + 15) / 16;
     const int64_t units = (int64_t)p.n_row_blocks * p.n_split * p.n_kv_h * p.batch;
     if (units > 0x7fffffff) return hipErrorInvalidConfiguration;
     p.n_units = (int)units;
     p.xcd_remap = (p.n_units % 8 == 0) ? 1 : 0;
-    const dim3 grid(p.n_units);
-    const dim3 block(64 * nwr * nwk);
-    if (nwr == 1 && nwk == NWK_MAX)
-        hipLaunchKernelGGL((fmha::fwd_kernel<HD, 1, NWK_MAX, SPLIT>), grid, block, 0, stream, p);
-    else if (nwr == 2 && nwk == 2 && NWK_MAX >= 2)
-        hipLaunchKernelGGL((fmha::fwd_kernel<HD, 2, (NWK_MAX >= 2 ? 2 : 1), SPLIT>), grid, block, 0, stream, p);
-    else if (nwr == 2)
-        hipLaunchKernelGGL((fmha::fwd_kernel<HD, 2, 1, SPLIT>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((fmha::fwd_kernel<HD, 4, 1, SPLIT>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((fmha::attn_kernel<HD, Waves<HD>::NK, Waves<HD>::NH, SPLIT>), dim3(p.n_units), dim3(256), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
