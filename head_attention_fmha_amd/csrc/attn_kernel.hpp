@@ -65,20 +65,25 @@ struct AttnShape {
     static constexpr int SLOTS = NB * 4 + 3;          // merge record per lane: m, l, lq, O^T
     static constexpr int V_BYTES = 4 * 32 * ROW_BYTES;
     static constexpr int M_BYTES = (NK - 1) * NH * SLOTS * 64 * 4;
-    static constexpr int S_BYTES = NH > 1 ? 2 * 4 * 8 * 64 * 4 : 0;  // two parity buffers
+    static constexpr int S_BUF = NH > 1 ? 4 * 8 * 64 * 4 : 0;  // one buffer of partial scores
     static constexpr int VM_BYTES = V_BYTES > M_BYTES ? V_BYTES : M_BYTES;
-    static constexpr int LDS_BYTES = VM_BYTES + S_BYTES;
     static constexpr int MIN_BLOCKS = NH > 1 ? 3 : 4;  // per CU: register budget
     static_assert(HDP == 64 || HDP == 128, "head-dim part of 64 or 128 columns");
 };
 
-template <int HD, int NK, int NH, bool SPLIT>
-__global__ __launch_bounds__(256, (AttnShape<HD, NK, NH>::MIN_BLOCKS)) void attn_kernel(const FwdParams p) {
+// ONE: every workgroup's key range fits one chunk of 32*NK keys (split-KV
+// decode with 128-key partitions, short caches).  The chunk loop collapses to
+// one pass, no state is carried in from an earlier slice, and the output
+// accumulator is born from the first PV product -- so nothing but Q is live
+// while the loads are in flight, which buys a fifth wave per SIMD.
+template <int HD, int NK, int NH, bool SPLIT, bool ONE>
+__global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : AttnShape<HD, NK, NH>::MIN_BLOCKS)) void attn_kernel(const FwdParams p) {
     using S = AttnShape<HD, NK, NH>;
     constexpr int HDP = S::HDP, KSTEPS = S::KSTEPS, NB = S::NB, CHUNKS = S::CHUNKS;
     constexpr int ROW_BYTES = S::ROW_BYTES, KEYS_PER_LOAD = S::KEYS_PER_LOAD, VLOADS = S::VLOADS;
     constexpr int SLOTS = S::SLOTS;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
+    // partial-score buffers alternate by slice parity (one suffices for ONE)
+    __shared__ __attribute__((aligned(16))) unsigned char smem[S::VM_BYTES + (ONE ? 1 : 2) * S::S_BUF];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -87,8 +92,11 @@ __global__ __launch_bounds__(256, (AttnShape<HD, NK, NH>::MIN_BLOCKS)) void attn
     const int lr = lane & 15;
     const int lg = lane >> 4;
 
-    // ---- work unit: row tiles fastest (they share K/V through L2), then KV
-    // heads (units reading the same cache rows run together) ------------------
+    // ---- work unit: row tiles fastest (they share K/V through L2), then
+    // partitions (consecutive key ranges of one KV head; their partial outputs
+    // are adjacent in memory), then KV heads and batches.  With several row
+    // tiles the units are regrouped so that one XCD (one L2) runs consecutive
+    // ones: blocks are dealt to the 8 XCDs round-robin ------------------------
     int bid = blockIdx.x;
     if (p.xcd_remap) {
         const int per = p.n_units >> 3;
@@ -96,10 +104,10 @@ __global__ __launch_bounds__(256, (AttnShape<HD, NK, NH>::MIN_BLOCKS)) void attn
     }
     const int rb = bid % p.n_row_blocks;
     bid /= p.n_row_blocks;
-    const int kvh = bid % p.n_kv_h;
-    bid /= p.n_kv_h;
     const int part = bid % p.n_split;
-    const int b = bid / p.n_split;
+    bid /= p.n_split;
+    const int kvh = bid % p.n_kv_h;
+    const int b = bid / p.n_kv_h;
 
     const int row0 = rb * 16;
     const int row_last = min(row0 + 16, p.rows) - 1;
@@ -145,6 +153,7 @@ __global__ __launch_bounds__(256, (AttnShape<HD, NK, NH>::MIN_BLOCKS)) void attn
 
     int iter = 0;
     for (int c = klo; c < khi; c += 32 * NK, ++iter) {
+        if (ONE && iter > 0) break;
         const int k0 = c + 32 * kg;
         const bool active = k0 < khi;  // uniform over the wave
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -179,7 +188,7 @@ __global__ __launch_bounds__(256, (AttnShape<HD, NK, NH>::MIN_BLOCKS)) void attn
         }
         if constexpr (NH > 1) {
             // sum the NH head-part scores of this key group (fixed order)
-            float *buf = sS + (iter & 1) * (4 * 8 * 64);
+            float *buf = sS + (ONE ? 0 : (iter & 1) * (4 * 8 * 64));
             if (active) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -217,9 +226,9 @@ __global__ __launch_bounds__(256, (AttnShape<HD, NK, NH>::MIN_BLOCKS)) void attn
             for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
             mx = fmaxf(mx, xor_shuffle(mx, 16));
             mx = fmaxf(mx, xor_shuffle(mx, 32));
-            const float m_new = fmaxf(m, mx);
+            const float m_new = ONE ? mx : fmaxf(m, mx);
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m - m_use);
+            const float alpha = ONE ? 0.f : fast_exp2(m - m_use);
             bf16x8 pt;
             float psum = 0.f, qsum = 0.f;
 #pragma unroll
@@ -230,8 +239,8 @@ __global__ __launch_bounds__(256, (AttnShape<HD, NK, NH>::MIN_BLOCKS)) void attn
                 psum += pj;
                 qsum += (float)pb;
             }
-            l = l * alpha + psum;
-            lq = lq * alpha + qsum;
+            l = ONE ? psum : l * alpha + psum;
+            lq = ONE ? qsum : lq * alpha + qsum;
             m = m_new;
             // ---- V has landed -------------------------------------------------------
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -251,8 +260,12 @@ __global__ __launch_bounds__(256, (AttnShape<HD, NK, NH>::MIN_BLOCKS)) void attn
                     vt[j] = *reinterpret_cast<const __bf16 *>(r0 + j * ROW_BYTES + off);
                     vt[4 + j] = *reinterpret_cast<const __bf16 *>(r1 + j * ROW_BYTES + off);
                 }
-                acc[nb] = acc[nb] * alpha;
-                acc[nb] = mfma_16x16x32(vt, pt, acc[nb]);
+                if constexpr (ONE) {
+                    acc[nb] = mfma_16x16x32(vt, pt, f32x4{0.f, 0.f, 0.f, 0.f});
+                } else {
+                    acc[nb] = acc[nb] * alpha;
+                    acc[nb] = mfma_16x16x32(vt, pt, acc[nb]);
+                }
             }
         }
     }

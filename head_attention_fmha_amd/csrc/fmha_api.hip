@@ -85,9 +85,19 @@ hipError_t launch_hd(FwdParams p, hipStream_t stream) {
     const int64_t units = (int64_t)p.n_row_blocks * p.n_split * p.n_kv_h * p.batch;
     if (units > 0x7fffffff) return hipErrorInvalidConfiguration;
     p.n_units = (int)units;
-    p.xcd_remap = (p.n_units % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((fmha::attn_kernel<HD, Waves<HD>::NK, Waves<HD>::NH, SPLIT>), dim3(p.n_units), dim3(256), 0,
-                       stream, p);
+    // only row tiles share data across workgroups; streaming units run best
+    // in plain order (neighbouring blocks read neighbouring memory)
+    p.xcd_remap = (p.n_row_blocks > 1 && p.n_units % 8 == 0) ? 1 : 0;
+    constexpr int NK = Waves<HD>::NK, NH = Waves<HD>::NH;
+    // the widest key range any workgroup can see: one chunk of 32*NK keys?
+    int span = p.split_len < p.s_k ? p.split_len : p.s_k;
+    // causal + window: a tile's rows span at most 16 positions, so at most
+    // window + 15 keys are visible to any of them
+    if (p.causal && p.window > 0 && p.window + 15 < span) span = p.window + 15;
+    if (span <= 32 * NK)
+        hipLaunchKernelGGL((fmha::attn_kernel<HD, NK, NH, SPLIT, true>), dim3(p.n_units), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fmha::attn_kernel<HD, NK, NH, SPLIT, false>), dim3(p.n_units), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
