@@ -23,6 +23,8 @@ Also reported on the same line:
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
 import argparse
+import glob
+import hashlib
 import json
 import math
 import os
@@ -40,6 +42,29 @@ METRIC = "decode KV-read GB/s + prefill attn TFLOP/s (bf16), % of MI355X rooflin
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources: ties counter results to the code they measured."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "head_attention_fmha_amd", "csrc", "*"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel_tag):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    summary is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def decode_bytes(w):
@@ -207,6 +232,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed region, copy 1 GiB twice (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the attention path "
@@ -222,10 +249,19 @@ def main():
         sys.exit(1)
     fa.load_library()
     res = run_decode(args, torch, fa, I)
+    if args.calibrate_copy:
+        src = torch.empty(2**30, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     prefill = None if args.no_prefill else run_prefill(torch, fa, I)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(res, args.cpu_seconds)
     w = res["w"]
     split_us = res["split_ms"] * 1e3
+    split_tag = "attn_kernel_hd128_split_gqa_decode"
     line = {
         "metric": METRIC,
         "value": round(res["value"], 2),
@@ -244,9 +280,9 @@ def main():
                    "step": "fmha_decode_splitkv + fmha_lse_merge",
                    "split_us": round(split_us, 2), "merge_us": round(res["merge_ms"] * 1e3, 2),
                    "merge_gbs": round(res["merge_gbs"], 1)},
-        "roofline": {"kernel": "fwd_kernel<128,1,4,split>", "bound": "hbm",
+        "roofline": {"kernel": "attn_kernel<128, NK=4, NH=1, split, one-slice>", "bound": "hbm",
                      "achieved": round(res["split_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(res["split_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(res["split_gbs"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(split_tag),
                      "alg_bytes_per_launch": res["split_bytes"], "launch_us": round(split_us, 2)},
         "cpu_baseline": cpu,
         "prefill": prefill,

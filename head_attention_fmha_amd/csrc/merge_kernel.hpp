@@ -6,7 +6,7 @@
 // which is O = sum_p exp(lse_p) O_p / sum_p exp(lse_p) with exp(M) factored
 // out ("Next steps", item 4, of the CURRENT_ISSUE.md page).
 //
-// HBM-bound streaming.  A row is served by PG groups of HD/4 lanes; a lane
+// Bandwidth-bound streaming.  A row is served by PG groups of HD/4 lanes; a lane
 // owns four adjacent columns, and group g takes partitions g, g+PG, ...,
 // reading each with one 16-byte load, UNROLL partitions in flight.  The PG
 // partial sums are combined through LDS in a fixed order (deterministic).
@@ -25,11 +25,13 @@ struct MergeParams {
     int n_h, T, rows, n_split;
 };
 
+// One row per workgroup: 256 / (HD/4) partition groups (16, 8, 4, 2 for hd
+// 64..512), so a 64-partition row is read in a single round of loads.
 template <int HD>
 struct MergeShape {
-    static constexpr int TPR = HD / 4;                         // lanes per row group
-    static constexpr int PG = (256 / TPR) >= 4 ? 4 : 256 / TPR;  // partition groups per row
-    static constexpr int RPW = 256 / (TPR * PG);                // rows per workgroup
+    static constexpr int TPR = HD / 4;     // lanes per row group
+    static constexpr int PG = 256 / TPR;   // partition groups per row
+    static constexpr int RPW = 1;          // rows per workgroup
 };
 
 template <int HD>
@@ -49,53 +51,69 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     const int row = blockIdx.x * RPW + rib;
     const bool live = row < p.rows;
 
+    // running maximum over this group's partitions (base-2 domain): a larger
+    // lse rescales what has been summed so far, so the partial outputs are
+    // loaded from the start without a separate pass over the lse values
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f, M = -INFINITY;
     if (live) {
         const float *lp = p.lse_part + (int64_t)row * p.n_split;
         const float *op = p.o_part + (int64_t)row * p.n_split * HD + col;
-        for (int i = 0; i < p.n_split; ++i) M = fmaxf(M, lp[i]);
-        if (M != -INFINITY) {
-            int i = g;
-            for (; i + (UNROLL - 1) * PG < p.n_split; i += UNROLL * PG) {
-                f32x4 ov[UNROLL];
-                float lv[UNROLL];
+        for (int i0 = g; i0 < p.n_split; i0 += UNROLL * PG) {
+            f32x4 ov[UNROLL];
+            float lv[UNROLL];
 #pragma unroll
-                for (int u = 0; u < UNROLL; ++u) {
-                    lv[u] = lp[i + u * PG];
-                    ov[u] = *reinterpret_cast<const f32x4 *>(op + (int64_t)(i + u * PG) * HD);
-                }
-#pragma unroll
-                for (int u = 0; u < UNROLL; ++u) {
-                    if (lv[u] != -INFINITY) {  // an empty partition carries no weight, whatever O_p holds
-                        const float w = fast_exp2((lv[u] - M) * kLog2e);
-                        den += w;
-                        acc += w * ov[u];
-                    }
-                }
+            for (int u = 0; u < UNROLL; ++u) {
+                const int i = i0 + u * PG;
+                const bool in = i < p.n_split;
+                lv[u] = in ? lp[i] * kLog2e : -INFINITY;
+                ov[u] = in ? *reinterpret_cast<const f32x4 *>(op + (int64_t)i * HD) : f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            for (; i < p.n_split; i += PG) {
-                const float li = lp[i];
-                if (li != -INFINITY) {
-                    const float w = fast_exp2((li - M) * kLog2e);
+            float mb = M;
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) mb = fmaxf(mb, lv[u]);
+            if (mb == -INFINITY) continue;  // nothing visible yet
+            if (mb > M) {
+                const float r = fast_exp2(M - mb);  // 0 when M = -inf
+                den *= r;
+                acc = acc * r;
+                M = mb;
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                if (lv[u] != -INFINITY) {  // an empty partition carries no weight, whatever O_p holds
+                    const float w = fast_exp2(lv[u] - M);
                     den += w;
-                    acc += w * *reinterpret_cast<const f32x4 *>(op + (int64_t)i * HD);
+                    acc += w * ov[u];
                 }
             }
         }
     }
     if constexpr (PG > 1) {
+        __shared__ float red_max[RPW][PG];
         red_acc[rib][g][lane_c] = acc;
-        if (lane_c == 0) red_den[rib][g] = den;
+        if (lane_c == 0) {
+            red_den[rib][g] = den;
+            red_max[rib][g] = M;
+        }
         __syncthreads();
         if (g != 0) return;
-        acc = red_acc[rib][0][lane_c];
-        den = red_den[rib][0];
+        float Mall = M;
 #pragma unroll
-        for (int gg = 1; gg < PG; ++gg) {
-            acc += red_acc[rib][gg][lane_c];
-            den += red_den[rib][gg];
+        for (int gg = 1; gg < PG; ++gg) Mall = fmaxf(Mall, red_max[rib][gg]);
+        if (Mall != -INFINITY) {
+            acc = {0.f, 0.f, 0.f, 0.f};
+            den = 0.f;
+#pragma unroll
+            for (int gg = 0; gg < PG; ++gg) {
+                const float mg = red_max[rib][gg];
+                if (mg == -INFINITY) continue;
+                const float r = fast_exp2(mg - Mall);
+                acc += r * red_acc[rib][gg][lane_c];
+                den += r * red_den[rib][gg];
+            }
         }
+        M = Mall;
     }
     if (!live) return;
 
@@ -108,7 +126,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     packed.x = (uint32_t)bf16_bits(acc[0] * inv) | ((uint32_t)bf16_bits(acc[1] * inv) << 16);
     packed.y = (uint32_t)bf16_bits(acc[2] * inv) | ((uint32_t)bf16_bits(acc[3] * inv) << 16);
     *reinterpret_cast<uint2 *>(p.o + (int64_t)b * p.o_sb + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + col) = packed;
-    if (col == 0 && p.lse != nullptr) p.lse[row] = den > 0.f ? M + __logf(den) : -INFINITY;
+    if (col == 0 && p.lse != nullptr) p.lse[row] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
 }
 
 }  // namespace fmha
