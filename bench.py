@@ -232,6 +232,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="time only the two prefill workloads (for profiler runs); prints no JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, copy 1 GiB twice (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -248,6 +250,9 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
     fa.load_library()
+    if args.only_prefill:
+        run_prefill(torch, fa, I)
+        return
     res = run_decode(args, torch, fa, I)
     if args.calibrate_copy:
         src = torch.empty(2**30, dtype=torch.uint8, device="cuda")

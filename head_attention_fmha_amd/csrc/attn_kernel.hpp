@@ -63,11 +63,8 @@ struct AttnShape {
     static constexpr int KEYS_PER_LOAD = 64 / CHUNKS;  // keys per wave-wide 16-byte load
     static constexpr int VLOADS = 32 / KEYS_PER_LOAD;
     static constexpr int SLOTS = NB * 4 + 3;          // merge record per lane: m, l, lq, O^T
-    static constexpr int V_BYTES = 4 * 32 * ROW_BYTES;
     static constexpr int M_BYTES = (NK - 1) * NH * SLOTS * 64 * 4;
     static constexpr int S_BUF = NH > 1 ? 4 * 8 * 64 * 4 : 0;  // one buffer of partial scores
-    static constexpr int VM_BYTES = V_BYTES > M_BYTES ? V_BYTES : M_BYTES;
-    static constexpr int MIN_BLOCKS = NH > 1 ? 3 : 4;  // per CU: register budget
     static_assert(HDP == 64 || HDP == 128, "head-dim part of 64 or 128 columns");
 };
 
@@ -77,13 +74,16 @@ struct AttnShape {
 // accumulator is born from the first PV product -- so nothing but Q is live
 // while the loads are in flight, which buys a fifth wave per SIMD.
 template <int HD, int NK, int NH, bool SPLIT, bool ONE>
-__global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : AttnShape<HD, NK, NH>::MIN_BLOCKS)) void attn_kernel(const FwdParams p) {
+__global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kernel(const FwdParams p) {
     using S = AttnShape<HD, NK, NH>;
     constexpr int HDP = S::HDP, KSTEPS = S::KSTEPS, NB = S::NB, CHUNKS = S::CHUNKS;
     constexpr int ROW_BYTES = S::ROW_BYTES, KEYS_PER_LOAD = S::KEYS_PER_LOAD, VLOADS = S::VLOADS;
     constexpr int SLOTS = S::SLOTS;
+    // one V slice per wave (the final key-group merge reuses that space);
     // partial-score buffers alternate by slice parity (one suffices for ONE)
-    __shared__ __attribute__((aligned(16))) unsigned char smem[S::VM_BYTES + (ONE ? 1 : 2) * S::S_BUF];
+    constexpr int V_BYTES = 4 * 32 * ROW_BYTES;
+    constexpr int VM_BYTES = V_BYTES > S::M_BYTES ? V_BYTES : S::M_BYTES;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[VM_BYTES + (ONE ? 1 : 2) * S::S_BUF];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -146,40 +146,31 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : AttnShape<HD, NK, N
 
     const uint16_t *kbase = p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh + col0;
     const uint16_t *vbase = p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh + col0;
-    unsigned char *sV = smem + wave * 32 * ROW_BYTES;
-    float *sS = reinterpret_cast<float *>(smem + S::VM_BYTES);
+    unsigned char *sVw = smem + wave * 32 * ROW_BYTES;  // this wave's V slice
+    float *sS = reinterpret_cast<float *>(smem + VM_BYTES);
     const int v_row_in_load = lane / CHUNKS;
     const int v_slot = lane % CHUNKS;
 
-    int iter = 0;
-    for (int c = klo; c < khi; c += 32 * NK, ++iter) {
-        if (ONE && iter > 0) break;
-        const int k0 = c + 32 * kg;
-        const bool active = k0 < khi;  // uniform over the wave
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // ---- K part of a slice: HBM -> QK A-operand registers (keys past khi read
+    // key khi-1; their scores are masked) ---------------------------------------
+    auto load_k = [&](int k0, bf16x8 (&kf)[2][KSTEPS]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int key = min(k0 + 16 * blk + lr, khi - 1);
+            const uint16_t *kp = kbase + (int64_t)key * p.k_st + 8 * lg;
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) kf[blk][s] = *reinterpret_cast<const bf16x8 *>(kp + 32 * s);
+        }
+    };
+    // LDS row r of the slice holds its 16-byte chunk c in slot (c + rot(r)) % CHUNKS:
+    // the 16 keys of one transposed read then cover the LDS banks evenly
+    auto rot_of = [](int r) __attribute__((always_inline)) { return (2 * (r & 7)) % CHUNKS; };
+
+    // ---- QK and (NH > 1) the fixed-order sum of the head-part scores -----------
+    auto scores = [&](int k0, bool active, int iter, const bf16x8 (&kf)[2][KSTEPS], f32x4 &s0, f32x4 &s1) __attribute__((always_inline)) {
+        s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+        s1 = f32x4{0.f, 0.f, 0.f, 0.f};
         if (active) {
-            // the previous slice's V reads are complete before new V lands
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-            // V part: HBM -> LDS; keys past khi read key khi-1 (weight 0)
-#pragma unroll
-            for (int it = 0; it < VLOADS; ++it) {
-                const int r = it * KEYS_PER_LOAD + v_row_in_load;
-                const int rot = (2 * ((r >> 2) & 3)) % CHUNKS;
-                const int chunk = (v_slot - rot + CHUNKS) % CHUNKS;
-                const int key = min(k0 + r, khi - 1);
-                load_lds_16(vbase + (int64_t)key * p.v_st + chunk * 8, sV + it * 64 * 16);
-            }
-            // K part: HBM -> QK A-operand registers; keys past khi are masked
-            bf16x8 kf[2][KSTEPS];
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                const int key = min(k0 + 16 * blk + lr, khi - 1);
-                const uint16_t *kp = kbase + (int64_t)key * p.k_st + 8 * lg;
-#pragma unroll
-                for (int s = 0; s < KSTEPS; ++s) kf[blk][s] = *reinterpret_cast<const bf16x8 *>(kp + 32 * s);
-            }
-            // every load of the slice is issued before the first wait
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < KSTEPS; ++s) {
                 s0 = mfma_16x16x32(kf[0][s], qf[s], s0);
@@ -187,7 +178,6 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : AttnShape<HD, NK, N
             }
         }
         if constexpr (NH > 1) {
-            // sum the NH head-part scores of this key group (fixed order)
             float *buf = sS + (ONE ? 0 : (iter & 1) * (4 * 8 * 64));
             if (active) {
 #pragma unroll
@@ -211,62 +201,151 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : AttnShape<HD, NK, N
                 }
             }
         }
-        if (active) {
-            // ---- mask, online softmax ---------------------------------------------
-            float x[8];
+    };
+
+    // ---- mask + online softmax: returns the rescale factor, fills P^T ----------
+    auto softmax = [&](int k0, const f32x4 &s0, const f32x4 &s1, bf16x8 &pt) __attribute__((always_inline)) -> float {
+        float x[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int ka = k0 + 4 * lg + j;
-                const int kb = ka + 16;
-                x[j] = (ka >= r_lo && ka < r_hi) ? s0[j] * p.scale_log2 : -INFINITY;
-                x[4 + j] = (kb >= r_lo && kb < r_hi) ? s1[j] * p.scale_log2 : -INFINITY;
+        for (int j = 0; j < 4; ++j) {
+            const int ka = k0 + 4 * lg + j;
+            const int kb = ka + 16;
+            x[j] = (ka >= r_lo && ka < r_hi) ? s0[j] * p.scale_log2 : -INFINITY;
+            x[4 + j] = (kb >= r_lo && kb < r_hi) ? s1[j] * p.scale_log2 : -INFINITY;
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+        mx = fmaxf(mx, xor_shuffle(mx, 16));
+        mx = fmaxf(mx, xor_shuffle(mx, 32));
+        const float m_new = ONE ? mx : fmaxf(m, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = ONE ? 0.f : fast_exp2(m - m_use);
+        float psum = 0.f, qsum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float pj = fast_exp2(x[j] - m_use);
+            const __bf16 pb = to_bf16(pj);
+            pt[j] = pb;
+            psum += pj;
+            qsum += (float)pb;
+        }
+        l = ONE ? psum : l * alpha + psum;
+        lq = ONE ? qsum : lq * alpha + qsum;
+        m = m_new;
+        return alpha;
+    };
+
+    // ---- O^T = alpha O^T + V^T . P^T from the wave's LDS slice.  Item j of
+    // lane (lr, lg) is key 4*lg + j (j < 4) or 16 + 4*lg + (j - 4), column
+    // 16*nb + lr.  Each half comes from one transposing read
+    // (ds_read_b64_tr_b16: within a 16-lane block, lane i item j receives
+    // element i%4 of the 8 bytes addressed by lane 4j + i/4), so lane s of
+    // block lg addresses key 4*lg + s/4 (+16), columns 16*nb + 4*(s%4) .. +3.
+    int tr_row[2], tr_col[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        tr_row[half] = 16 * half + 4 * lg + (lr >> 2);
+        tr_col[half] = 4 * (lr & 3);
+    }
+    auto pv = [&](float alpha, const bf16x8 &pt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            bf16x4 q[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int r = tr_row[half];
+                const int c = 16 * nb + tr_col[half];
+                const int off = r * ROW_BYTES + (((c >> 3) + rot_of(r)) % CHUNKS) * 16 + (c & 7) * 2;
+                q[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4 *)(sVw + off));
             }
-            float mx = x[0];
+            // whole-vector concatenation (element-wise inserts are mis-lowered)
+            const bf16x8 vt = __builtin_shufflevector(q[0], q[1], 0, 1, 2, 3, 4, 5, 6, 7);
+            if constexpr (ONE) {
+                acc[nb] = mfma_16x16x32(vt, pt, f32x4{0.f, 0.f, 0.f, 0.f});
+            } else {
+                acc[nb] = acc[nb] * alpha;
+                acc[nb] = mfma_16x16x32(vt, pt, acc[nb]);
+            }
+        }
+    };
+
+    const int chunk_keys = 32 * NK;
+    const int nslices = khi > klo ? (khi - klo + chunk_keys - 1) / chunk_keys : 0;  // uniform
+    if constexpr (ONE) {
+        // one slice: V goes HBM -> LDS directly (global_load_lds, no registers in flight)
+        if (nslices > 0) {
+            const int k0 = klo + 32 * kg;
+            const bool active = k0 < khi;
+            bf16x8 kf[2][KSTEPS];
+            if (active) {
 #pragma unroll
-            for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-            mx = fmaxf(mx, xor_shuffle(mx, 16));
-            mx = fmaxf(mx, xor_shuffle(mx, 32));
-            const float m_new = ONE ? mx : fmaxf(m, mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = ONE ? 0.f : fast_exp2(m - m_use);
+                for (int it = 0; it < VLOADS; ++it) {
+                    const int r = it * KEYS_PER_LOAD + v_row_in_load;
+                    const int chunk = (v_slot - rot_of(r) + CHUNKS) % CHUNKS;
+                    const int key = min(k0 + r, khi - 1);
+                    load_lds_16(vbase + (int64_t)key * p.v_st + chunk * 8, sVw + it * 64 * 16);
+                }
+                load_k(k0, kf);
+                __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
+            }
+            f32x4 s0, s1;
+            scores(k0, active, 0, kf, s0, s1);
+            if (active) {
+                bf16x8 pt;
+                const float alpha = softmax(k0, s0, s1, pt);
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // V has landed in LDS
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                pv(alpha, pt);
+            }
+        }
+    } else {
+        // pipelined: K and V of slice n+1 are loaded into registers while slice
+        // n is computed; V reaches LDS (rotated) just before its PV product.
+        // Plain register loads keep the compiler's wait counting exact, so the
+        // waits for slice n leave slice n+1's loads in flight.
+        auto load_v = [&](int k0, u32x4 (&vr)[VLOADS]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int it = 0; it < VLOADS; ++it) {
+                const int key = min(k0 + it * KEYS_PER_LOAD + v_row_in_load, khi - 1);
+                vr[it] = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)key * p.v_st + v_slot * 8);
+            }
+        };
+        auto step = [&](int n, const bf16x8 (&kf)[2][KSTEPS], const u32x4 (&vr)[VLOADS]) __attribute__((always_inline)) {
+            const int k0 = klo + n * chunk_keys + 32 * kg;
+            const bool active = k0 < khi;
+            f32x4 s0, s1;
+            scores(k0, active, n, kf, s0, s1);
+            if (!active) return;
             bf16x8 pt;
-            float psum = 0.f, qsum = 0.f;
+            const float alpha = softmax(k0, s0, s1, pt);
+            // the previous slice's V^T reads are done before its LDS slice is reused
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float pj = fast_exp2(x[j] - m_use);
-                const __bf16 pb = to_bf16(pj);
-                pt[j] = pb;
-                psum += pj;
-                qsum += (float)pb;
+            for (int it = 0; it < VLOADS; ++it) {
+                const int r = it * KEYS_PER_LOAD + v_row_in_load;
+                const int slot = (v_slot + rot_of(r)) % CHUNKS;
+                *reinterpret_cast<u32x4 *>(sVw + r * ROW_BYTES + slot * 16) = vr[it];
             }
-            l = ONE ? psum : l * alpha + psum;
-            lq = ONE ? qsum : lq * alpha + qsum;
-            m = m_new;
-            // ---- V has landed -------------------------------------------------------
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // ---- O^T = alpha O^T + V^T . P^T; item j of lane (lr, lg) is key
-            // 4*lg + j (j < 4) or 16 + 4*lg + (j - 4); both rows rotate by 2*lg -------
-            const int rot = (2 * lg) % CHUNKS;
-            const unsigned char *r0 = sV + (4 * lg) * ROW_BYTES;
-            const unsigned char *r1 = r0 + 16 * ROW_BYTES;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const int d = 16 * nb + lr;
-                const int off = (((d >> 3) + rot) % CHUNKS) * 16 + (d & 7) * 2;
-                bf16x8 vt;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    vt[j] = *reinterpret_cast<const __bf16 *>(r0 + j * ROW_BYTES + off);
-                    vt[4 + j] = *reinterpret_cast<const __bf16 *>(r1 + j * ROW_BYTES + off);
-                }
-                if constexpr (ONE) {
-                    acc[nb] = mfma_16x16x32(vt, pt, f32x4{0.f, 0.f, 0.f, 0.f});
-                } else {
-                    acc[nb] = acc[nb] * alpha;
-                    acc[nb] = mfma_16x16x32(vt, pt, acc[nb]);
-                }
-            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            pv(alpha, pt);
+        };
+        // two slices per iteration, both loaded up front: the second slice's
+        // loads are in flight while the first is computed.  The loads are
+        // unconditional (key indices clamp to khi-1, so a slice past the range
+        // reads valid memory and is then skipped) and no load target crosses
+        // the loop back-edge: both keep the compiler's wait counts exact, so it
+        // waits for the first slice only.
+        for (int n = 0; n < nslices; n += 2) {
+            bf16x8 kfA[2][KSTEPS], kfB[2][KSTEPS];
+            u32x4 vrA[VLOADS], vrB[VLOADS];
+            load_k(klo + n * chunk_keys + 32 * kg, kfA);
+            load_v(klo + n * chunk_keys + 32 * kg, vrA);
+            load_k(klo + (n + 1) * chunk_keys + 32 * kg, kfB);
+            load_v(klo + (n + 1) * chunk_keys + 32 * kg, vrB);
+            __builtin_amdgcn_sched_barrier(0);  // keep all 2 x (K + V) loads ahead of the math
+            step(n, kfA, vrA);
+            if (n + 1 < nslices) step(n + 1, kfB, vrB);
         }
     }
 
