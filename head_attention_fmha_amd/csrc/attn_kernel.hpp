@@ -1,21 +1,21 @@
 // attn_kernel.hpp -- the fused attention kernel for gfx950.
 //
-// One workgroup (4 waves) computes one 16-row tile of one (batch, kv head)
-// over one key range.  A row is one (query position t, query head h) that
-// reads this KV head, numbered r = t * group + (h - kv*group): the GQA/MQA
-// query heads sharing K/V are stacked into the same MFMA tile, and the rows
-// of a tile have the same or adjacent positions (tight mask ranges).
+// One workgroup (4 waves) computes MT adjacent 16-row tiles of one (batch,
+// kv head) over one key range.  A row is one (query position t, query head h)
+// that reads this KV head, numbered r = t * group + (h - kv*group): the
+// GQA/MQA query heads sharing K/V are stacked into the same MFMA tile, and
+// the rows of a tile have the same or adjacent positions (tight mask ranges).
 //
 // The four waves form NK key groups x NH head-dimension parts (HDP = HD/NH
-// columns each, 64 or 128):
+// columns each, 64 or 128); every wave covers all MT tiles:
 //   * key group g takes keys [c + 32g, c + 32g + 32) of every chunk of
 //     32*NK keys and keeps its own online-softmax state; the NK groups are
 //     merged once at the end, in a fixed order;
 //   * head part j loads only columns [j*HDP, (j+1)*HDP) of K and V, so every
-//     byte of K/V is fetched once per workgroup and the output accumulator
-//     is 16 rows x HDP columns per wave for every hd (<= 32 registers).
-//     The NH partial QK scores of a slice are summed through LDS in a fixed
-//     order, so the NH waves of a key group hold bit-identical scores and
+//     byte of K/V is fetched once per workgroup, and each loaded K operand
+//     and each gathered V operand feeds the MFMAs of all MT tiles.  The NH
+//     partial QK scores of a slice are summed through LDS in a fixed order,
+//     so the NH waves of a key group hold bit-identical scores and
 //     probabilities.
 //
 // Both products are taken transposed, keys in the MFMA M dimension
@@ -31,12 +31,15 @@
 // Data movement per 32-key slice and wave:
 //   * K: HBM -> QK A-operand registers (lane lr + 16*lg loads 16 bytes of
 //     key lr at column offset 32*s + 8*lg) -- no LDS round trip;
-//   * V: HBM -> a wave-private LDS slice with global_load_lds_dwordx4 (no
-//     registers held in flight); a run of lanes covers one whole key-row
-//     part, so loads stay coalesced.  The 16-byte chunks of LDS key row k
-//     are rotated by 2*((k/4) % 4) positions: the PV operand gathers V[k][d]
-//     for keys 4*lg + j across the four lane groups, and the rotation puts
-//     the four groups on disjoint LDS banks.
+//   * V: HBM -> a wave-private LDS slice, a run of lanes covering one whole
+//     key-row part (coalesced): directly with global_load_lds_dwordx4 when
+//     a workgroup has one slice, through registers when slices are
+//     pipelined (the compiler does not count LDS-direct loads, so it would
+//     wait for all of them).  The 16-byte chunks of LDS key row k are
+//     rotated by 2*(k mod 8) positions, so one transposing read of 16 keys
+//     spreads over the banks;
+//   * the PV operand V^T comes from ds_read_b64_tr_b16, gfx950's
+//     transposing LDS read (see pv below).
 //
 // Softmax: online (running max m, running sum l, rescale of the partial
 // output by exp(m_old - m_new) when a slice raises the max), as in the
@@ -52,7 +55,7 @@
 
 namespace fmha {
 
-template <int HD, int NK, int NH>
+template <int HD, int NK, int NH, int MT>
 struct AttnShape {
     static_assert(NK * NH == 4, "four waves per workgroup");
     static constexpr int HDP = HD / NH;               // head-dim columns per wave
@@ -62,9 +65,10 @@ struct AttnShape {
     static constexpr int ROW_BYTES = HDP * 2;         // LDS key-row part
     static constexpr int KEYS_PER_LOAD = 64 / CHUNKS;  // keys per wave-wide 16-byte load
     static constexpr int VLOADS = 32 / KEYS_PER_LOAD;
-    static constexpr int SLOTS = NB * 4 + 3;          // merge record per lane: m, l, lq, O^T
-    static constexpr int M_BYTES = (NK - 1) * NH * SLOTS * 64 * 4;
-    static constexpr int S_BUF = NH > 1 ? 4 * 8 * 64 * 4 : 0;  // one buffer of partial scores
+    static constexpr int SLOTS = NB * 4 + 3;          // merge record per lane and tile: m, l, lq, O^T
+    static constexpr int M_BYTES = (NK - 1) * NH * MT * SLOTS * 64 * 4;
+    static constexpr int S_FLOATS = MT * 4 * 8 * 64;  // one buffer of partial scores
+    static constexpr int S_BUF = NH > 1 ? S_FLOATS * 4 : 0;
     static_assert(HDP == 64 || HDP == 128, "head-dim part of 64 or 128 columns");
 };
 
@@ -73,9 +77,13 @@ struct AttnShape {
 // one pass, no state is carried in from an earlier slice, and the output
 // accumulator is born from the first PV product -- so nothing but Q is live
 // while the loads are in flight, which buys a fifth wave per SIMD.
-template <int HD, int NK, int NH, bool SPLIT, bool ONE>
+// MT: 16-row tiles per workgroup.  Two when a workgroup streams several
+// slices for more than 16 rows: each K/V byte brought on chip then serves
+// twice the rows.
+template <int HD, int NK, int NH, int MT, bool SPLIT, bool ONE>
 __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kernel(const FwdParams p) {
-    using S = AttnShape<HD, NK, NH>;
+    using S = AttnShape<HD, NK, NH, MT>;
+    static_assert(MT == 1 || !ONE, "one-slice work uses single tiles");
     constexpr int HDP = S::HDP, KSTEPS = S::KSTEPS, NB = S::NB, CHUNKS = S::CHUNKS;
     constexpr int ROW_BYTES = S::ROW_BYTES, KEYS_PER_LOAD = S::KEYS_PER_LOAD, VLOADS = S::VLOADS;
     constexpr int SLOTS = S::SLOTS;
@@ -92,10 +100,10 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
     const int lr = lane & 15;
     const int lg = lane >> 4;
 
-    // ---- work unit: row tiles fastest (they share K/V through L2), then
+    // ---- work unit: row blocks fastest (they share K/V through L2), then
     // partitions (consecutive key ranges of one KV head; their partial outputs
     // are adjacent in memory), then KV heads and batches.  With several row
-    // tiles the units are regrouped so that one XCD (one L2) runs consecutive
+    // blocks the units are regrouped so that one XCD (one L2) runs consecutive
     // ones: blocks are dealt to the 8 XCDs round-robin ------------------------
     int bid = blockIdx.x;
     if (p.xcd_remap) {
@@ -109,40 +117,52 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
     const int kvh = bid % p.n_kv_h;
     const int b = bid / p.n_kv_h;
 
-    const int row0 = rb * 16;
-    const int row_last = min(row0 + 16, p.rows) - 1;
+    const int row0 = rb * 16 * MT;
+    const int row_last = min(row0 + 16 * MT, p.rows) - 1;
     const int pos_lo = p.s_k - p.T + row0 / p.group;
     const int pos_hi = p.s_k - p.T + row_last / p.group;
-    // key range: the partition, cut to the union of the tile rows' masks
+    // key range: the partition, cut to the union of the block rows' masks
     int klo = part * p.split_len;
     int khi = min(klo + p.split_len, p.s_k);
     if (p.causal) khi = min(khi, pos_hi + 1);
     if (p.window > 0) klo = max(klo, pos_lo - p.window + 1);
 
-    const int row = row0 + lr;
-    const bool row_ok = row < p.rows;
-    const int t = row_ok ? row / p.group : 0;
-    const int h = kvh * p.group + (row_ok ? row % p.group : 0);
-    const int pos = p.s_k - p.T + t;
-    int r_hi = p.causal ? min(khi, pos + 1) : khi;
-    const int r_lo = p.window > 0 ? max(klo, pos - p.window + 1) : klo;
-    if (!row_ok) r_hi = r_lo;  // no visible key: the row stays at -inf
-
-    const int col0 = hp * HDP;  // first head-dim column of this wave
-    bf16x8 qf[KSTEPS];          // Q^T B operand: Q[row lr][col0 + 32*s + 8*lg + 0..7]
-    {
-        const uint16_t *qp = p.q + (int64_t)b * p.q_sb + (int64_t)t * p.q_st + (int64_t)h * p.q_sh + col0 + 8 * lg;
+    // ---- this lane's row in each tile ---------------------------------------------
+    bool row_ok[MT];
+    int t_of[MT], h_of[MT], r_lo[MT], r_hi[MT];
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-            qf[s] = row_ok ? *reinterpret_cast<const bf16x8 *>(qp + 32 * s) : bf16x8{};
+    for (int mt = 0; mt < MT; ++mt) {
+        const int row = row0 + 16 * mt + lr;
+        row_ok[mt] = row < p.rows;
+        t_of[mt] = row_ok[mt] ? row / p.group : 0;
+        h_of[mt] = kvh * p.group + (row_ok[mt] ? row % p.group : 0);
+        const int pos = p.s_k - p.T + t_of[mt];
+        r_hi[mt] = p.causal ? min(khi, pos + 1) : khi;
+        r_lo[mt] = p.window > 0 ? max(klo, pos - p.window + 1) : klo;
+        if (!row_ok[mt]) r_hi[mt] = r_lo[mt];  // no visible key: the row stays at -inf
     }
 
-    f32x4 acc[NB];
+    const int col0 = hp * HDP;  // first head-dim column of this wave
+    bf16x8 qf[MT][KSTEPS];      // Q^T B operand: Q[row lr][col0 + 32*s + 8*lg + 0..7]
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY;  // running max (base 2), equal in the 4 lanes of a row
-    float l = 0.f;        // this lane's share of the fp32 sum of weights (-> lse)
-    float lq = 0.f;       // the same over the bf16-rounded weights (-> O)
+    for (int mt = 0; mt < MT; ++mt) {
+        const uint16_t *qp = p.q + (int64_t)b * p.q_sb + (int64_t)t_of[mt] * p.q_st + (int64_t)h_of[mt] * p.q_sh +
+                             col0 + 8 * lg;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+            qf[mt][s] = row_ok[mt] ? *reinterpret_cast<const bf16x8 *>(qp + 32 * s) : bf16x8{};
+    }
+
+    f32x4 acc[MT][NB];
+    float m[MT], l[MT], lq[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mt][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[mt] = -INFINITY;  // running max (base 2), equal in the 4 lanes of a row
+        l[mt] = 0.f;        // this lane's share of the fp32 sum of weights (-> lse)
+        lq[mt] = 0.f;       // the same over the bf16-rounded weights (-> O)
+    }
 
     const uint16_t *kbase = p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh + col0;
     const uint16_t *vbase = p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh + col0;
@@ -166,61 +186,73 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
     // the 16 keys of one transposed read then cover the LDS banks evenly
     auto rot_of = [](int r) __attribute__((always_inline)) { return (2 * (r & 7)) % CHUNKS; };
 
-    // ---- QK and (NH > 1) the fixed-order sum of the head-part scores -----------
-    auto scores = [&](int k0, bool active, int iter, const bf16x8 (&kf)[2][KSTEPS], f32x4 &s0, f32x4 &s1) __attribute__((always_inline)) {
-        s0 = f32x4{0.f, 0.f, 0.f, 0.f};
-        s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    // ---- QK of every tile and (NH > 1) the fixed-order sum of the head-part
+    // scores ------------------------------------------------------------------------
+    auto scores = [&](bool active, int iter, const bf16x8 (&kf)[2][KSTEPS], f32x4 (&s0)[MT], f32x4 (&s1)[MT])
+                      __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            s0[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            s1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         if (active) {
 #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                s0 = mfma_16x16x32(kf[0][s], qf[s], s0);
-                s1 = mfma_16x16x32(kf[1][s], qf[s], s1);
-            }
+            for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    s0[mt] = mfma_16x16x32(kf[0][s], qf[mt][s], s0[mt]);
+                    s1[mt] = mfma_16x16x32(kf[1][s], qf[mt][s], s1[mt]);
+                }
         }
         if constexpr (NH > 1) {
-            float *buf = sS + (ONE ? 0 : (iter & 1) * (4 * 8 * 64));
+            float *buf = sS + (ONE ? 0 : (iter & 1) * S::S_FLOATS);
             if (active) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    buf[(wave * 8 + j) * 64 + lane] = s0[j];
-                    buf[(wave * 8 + 4 + j) * 64 + lane] = s1[j];
-                }
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        buf[((mt * 4 + wave) * 8 + j) * 64 + lane] = s0[mt][j];
+                        buf[((mt * 4 + wave) * 8 + 4 + j) * 64 + lane] = s1[mt][j];
+                    }
             }
             __syncthreads();
             if (active) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float a = 0.f, c2 = 0.f;
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int q = 0; q < NH; ++q) {
-                        a += buf[((kg * NH + q) * 8 + j) * 64 + lane];
-                        c2 += buf[((kg * NH + q) * 8 + 4 + j) * 64 + lane];
+                    for (int j = 0; j < 4; ++j) {
+                        float a = 0.f, c2 = 0.f;
+#pragma unroll
+                        for (int q = 0; q < NH; ++q) {
+                            a += buf[((mt * 4 + kg * NH + q) * 8 + j) * 64 + lane];
+                            c2 += buf[((mt * 4 + kg * NH + q) * 8 + 4 + j) * 64 + lane];
+                        }
+                        s0[mt][j] = a;
+                        s1[mt][j] = c2;
                     }
-                    s0[j] = a;
-                    s1[j] = c2;
-                }
             }
         }
     };
 
-    // ---- mask + online softmax: returns the rescale factor, fills P^T ----------
-    auto softmax = [&](int k0, const f32x4 &s0, const f32x4 &s1, bf16x8 &pt) __attribute__((always_inline)) -> float {
+    // ---- mask + online softmax of tile mt: returns the rescale factor, fills P^T
+    auto softmax = [&](int mt, int k0, const f32x4 &s0, const f32x4 &s1, bf16x8 &pt) __attribute__((always_inline))
+        -> float {
         float x[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int ka = k0 + 4 * lg + j;
             const int kb = ka + 16;
-            x[j] = (ka >= r_lo && ka < r_hi) ? s0[j] * p.scale_log2 : -INFINITY;
-            x[4 + j] = (kb >= r_lo && kb < r_hi) ? s1[j] * p.scale_log2 : -INFINITY;
+            x[j] = (ka >= r_lo[mt] && ka < r_hi[mt]) ? s0[j] * p.scale_log2 : -INFINITY;
+            x[4 + j] = (kb >= r_lo[mt] && kb < r_hi[mt]) ? s1[j] * p.scale_log2 : -INFINITY;
         }
         float mx = x[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
         mx = fmaxf(mx, xor_shuffle(mx, 16));
         mx = fmaxf(mx, xor_shuffle(mx, 32));
-        const float m_new = ONE ? mx : fmaxf(m, mx);
+        const float m_new = ONE ? mx : fmaxf(m[mt], mx);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = ONE ? 0.f : fast_exp2(m - m_use);
+        const float alpha = ONE ? 0.f : fast_exp2(m[mt] - m_use);
         float psum = 0.f, qsum = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -230,15 +262,15 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
             psum += pj;
             qsum += (float)pb;
         }
-        l = ONE ? psum : l * alpha + psum;
-        lq = ONE ? qsum : lq * alpha + qsum;
-        m = m_new;
+        l[mt] = ONE ? psum : l[mt] * alpha + psum;
+        lq[mt] = ONE ? qsum : lq[mt] * alpha + qsum;
+        m[mt] = m_new;
         return alpha;
     };
 
-    // ---- O^T = alpha O^T + V^T . P^T from the wave's LDS slice.  Item j of
-    // lane (lr, lg) is key 4*lg + j (j < 4) or 16 + 4*lg + (j - 4), column
-    // 16*nb + lr.  Each half comes from one transposing read
+    // ---- O^T = alpha O^T + V^T . P^T for every tile, from the wave's LDS slice.
+    // Item j of lane (lr, lg) is key 4*lg + j (j < 4) or 16 + 4*lg + (j - 4),
+    // column 16*nb + lr.  Each half comes from one transposing read
     // (ds_read_b64_tr_b16: within a 16-lane block, lane i item j receives
     // element i%4 of the 8 bytes addressed by lane 4j + i/4), so lane s of
     // block lg addresses key 4*lg + s/4 (+16), columns 16*nb + 4*(s%4) .. +3.
@@ -248,7 +280,7 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
         tr_row[half] = 16 * half + 4 * lg + (lr >> 2);
         tr_col[half] = 4 * (lr & 3);
     }
-    auto pv = [&](float alpha, const bf16x8 &pt) __attribute__((always_inline)) {
+    auto pv = [&](const float (&alpha)[MT], const bf16x8 (&pt)[MT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             bf16x4 q[2];
@@ -261,11 +293,14 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
             }
             // whole-vector concatenation (element-wise inserts are mis-lowered)
             const bf16x8 vt = __builtin_shufflevector(q[0], q[1], 0, 1, 2, 3, 4, 5, 6, 7);
-            if constexpr (ONE) {
-                acc[nb] = mfma_16x16x32(vt, pt, f32x4{0.f, 0.f, 0.f, 0.f});
-            } else {
-                acc[nb] = acc[nb] * alpha;
-                acc[nb] = mfma_16x16x32(vt, pt, acc[nb]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                if constexpr (ONE) {
+                    acc[mt][nb] = mfma_16x16x32(vt, pt[mt], f32x4{0.f, 0.f, 0.f, 0.f});
+                } else {
+                    acc[mt][nb] = acc[mt][nb] * alpha[mt];
+                    acc[mt][nb] = mfma_16x16x32(vt, pt[mt], acc[mt][nb]);
+                }
             }
         }
     };
@@ -289,21 +324,22 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
                 load_k(k0, kf);
                 __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
             }
-            f32x4 s0, s1;
-            scores(k0, active, 0, kf, s0, s1);
+            f32x4 s0[MT], s1[MT];
+            scores(active, 0, kf, s0, s1);
             if (active) {
-                bf16x8 pt;
-                const float alpha = softmax(k0, s0, s1, pt);
+                bf16x8 pt[MT];
+                float alpha[MT];
+                alpha[0] = softmax(0, k0, s0[0], s1[0], pt[0]);
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // V has landed in LDS
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 pv(alpha, pt);
             }
         }
     } else {
-        // pipelined: K and V of slice n+1 are loaded into registers while slice
-        // n is computed; V reaches LDS (rotated) just before its PV product.
-        // Plain register loads keep the compiler's wait counting exact, so the
-        // waits for slice n leave slice n+1's loads in flight.
+        // pipelined: K and V are loaded into registers ahead of their slice's
+        // math; V reaches LDS (rotated) just before its PV product.  Plain
+        // register loads keep the compiler's wait counting exact, so the waits
+        // for one slice leave later slices' loads in flight.
         auto load_v = [&](int k0, u32x4 (&vr)[VLOADS]) __attribute__((always_inline)) {
 #pragma unroll
             for (int it = 0; it < VLOADS; ++it) {
@@ -314,11 +350,13 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
         auto step = [&](int n, const bf16x8 (&kf)[2][KSTEPS], const u32x4 (&vr)[VLOADS]) __attribute__((always_inline)) {
             const int k0 = klo + n * chunk_keys + 32 * kg;
             const bool active = k0 < khi;
-            f32x4 s0, s1;
-            scores(k0, active, n, kf, s0, s1);
+            f32x4 s0[MT], s1[MT];
+            scores(active, n, kf, s0, s1);
             if (!active) return;
-            bf16x8 pt;
-            const float alpha = softmax(k0, s0, s1, pt);
+            bf16x8 pt[MT];
+            float alpha[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) alpha[mt] = softmax(mt, k0, s0[mt], s1[mt], pt[mt]);
             // the previous slice's V^T reads are done before its LDS slice is reused
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 #pragma unroll
@@ -330,90 +368,121 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
             pv(alpha, pt);
         };
-        // two slices per iteration, both loaded up front: the second slice's
-        // loads are in flight while the first is computed.  The loads are
-        // unconditional (key indices clamp to khi-1, so a slice past the range
-        // reads valid memory and is then skipped) and no load target crosses
-        // the loop back-edge: both keep the compiler's wait counts exact, so it
-        // waits for the first slice only.
-        for (int n = 0; n < nslices; n += 2) {
-            bf16x8 kfA[2][KSTEPS], kfB[2][KSTEPS];
-            u32x4 vrA[VLOADS], vrB[VLOADS];
-            load_k(klo + n * chunk_keys + 32 * kg, kfA);
-            load_v(klo + n * chunk_keys + 32 * kg, vrA);
-            load_k(klo + (n + 1) * chunk_keys + 32 * kg, kfB);
-            load_v(klo + (n + 1) * chunk_keys + 32 * kg, vrB);
-            __builtin_amdgcn_sched_barrier(0);  // keep all 2 x (K + V) loads ahead of the math
-            step(n, kfA, vrA);
-            if (n + 1 < nslices) step(n + 1, kfB, vrB);
+        if constexpr (MT == 1) {
+            // two slices per iteration, both loaded up front: the second
+            // slice's loads are in flight while the first is computed.  The
+            // loads are unconditional (key indices clamp to khi-1, so a slice
+            // past the range reads valid memory and is then skipped) and no
+            // load target crosses the loop back-edge: both keep the compiler's
+            // wait counts exact, so it waits for the first slice only.
+            for (int n = 0; n < nslices; n += 2) {
+                bf16x8 kfA[2][KSTEPS], kfB[2][KSTEPS];
+                u32x4 vrA[VLOADS], vrB[VLOADS];
+                load_k(klo + n * chunk_keys + 32 * kg, kfA);
+                load_v(klo + n * chunk_keys + 32 * kg, vrA);
+                load_k(klo + (n + 1) * chunk_keys + 32 * kg, kfB);
+                load_v(klo + (n + 1) * chunk_keys + 32 * kg, vrB);
+                __builtin_amdgcn_sched_barrier(0);  // keep all 2 x (K + V) loads ahead of the math
+                step(n, kfA, vrA);
+                if (n + 1 < nslices) step(n + 1, kfB, vrB);
+            }
+        } else {
+            // two tiles already double the math per loaded slice; one slice per
+            // iteration keeps the registers within two waves per SIMD
+            for (int n = 0; n < nslices; ++n) {
+                bf16x8 kf[2][KSTEPS];
+                u32x4 vr[VLOADS];
+                load_k(klo + n * chunk_keys + 32 * kg, kf);
+                load_v(klo + n * chunk_keys + 32 * kg, vr);
+                __builtin_amdgcn_sched_barrier(0);
+                step(n, kf, vr);
+            }
         }
     }
 
     // full row sums over the four lanes of a row
-    l += xor_shuffle(l, 16);
-    l += xor_shuffle(l, 32);
-    lq += xor_shuffle(lq, 16);
-    lq += xor_shuffle(lq, 32);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        l[mt] += xor_shuffle(l[mt], 16);
+        l[mt] += xor_shuffle(l[mt], 32);
+        lq[mt] += xor_shuffle(lq[mt], 16);
+        lq[mt] += xor_shuffle(lq[mt], 32);
+    }
 
-    // ---- merge the NK key groups of each head part (fixed order) -----------------
+    // ---- merge the NK key groups of each head part and tile (fixed order) ----------
     if constexpr (NK > 1) {
         __syncthreads();  // all V slices and score buffers are consumed
         float *red = reinterpret_cast<float *>(smem);
+        auto slot_of = [&](int g, int mt) __attribute__((always_inline)) {
+            return red + ((((g - 1) * NH + hp) * MT + mt) * SLOTS) * 64 + lane;
+        };
         if (kg != 0) {
-            float *mine = red + ((kg - 1) * NH + hp) * SLOTS * 64 + lane;
-            mine[0] = m;
-            mine[64] = l;
-            mine[128] = lq;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+            for (int mt = 0; mt < MT; ++mt) {
+                float *mine = slot_of(kg, mt);
+                mine[0] = m[mt];
+                mine[64] = l[mt];
+                mine[128] = lq[mt];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) mine[(3 + nb * 4 + j) * 64] = acc[nb][j];
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) mine[(3 + nb * 4 + j) * 64] = acc[mt][nb][j];
+            }
         }
         __syncthreads();
         if (kg != 0) return;
-        float M = m;
 #pragma unroll
-        for (int g = 1; g < NK; ++g) M = fmaxf(M, red[((g - 1) * NH + hp) * SLOTS * 64 + lane]);
-        const float M_use = (M == -INFINITY) ? 0.f : M;
-        const float w0 = fast_exp2(m - M_use);
-        l *= w0;
-        lq *= w0;
+        for (int mt = 0; mt < MT; ++mt) {
+            float M = m[mt];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] = acc[nb] * w0;
+            for (int g = 1; g < NK; ++g) M = fmaxf(M, slot_of(g, mt)[0]);
+            const float M_use = (M == -INFINITY) ? 0.f : M;
+            const float w0 = fast_exp2(m[mt] - M_use);
+            l[mt] *= w0;
+            lq[mt] *= w0;
 #pragma unroll
-        for (int g = 1; g < NK; ++g) {
-            const float *src = red + ((g - 1) * NH + hp) * SLOTS * 64 + lane;
-            const float wgt = fast_exp2(src[0] - M_use);
-            l += wgt * src[64];
-            lq += wgt * src[128];
+            for (int nb = 0; nb < NB; ++nb) acc[mt][nb] = acc[mt][nb] * w0;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+            for (int g = 1; g < NK; ++g) {
+                const float *src = slot_of(g, mt);
+                const float wgt = fast_exp2(src[0] - M_use);
+                l[mt] += wgt * src[64];
+                lq[mt] += wgt * src[128];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[nb][j] += wgt * src[(3 + nb * 4 + j) * 64];
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[mt][nb][j] += wgt * src[(3 + nb * 4 + j) * 64];
+            }
+            m[mt] = M;
         }
-        m = M;
     }
-    if (!row_ok) return;
 
     // ---- epilogue: one division; lse = (m + log2 l) ln 2 -------------------------
-    const float inv = lq > 0.f ? 1.f / lq : 0.f;
-    const float lse_val = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
-    if constexpr (SPLIT) {
-        const int64_t r = (((int64_t)b * p.n_h + h) * p.T + t) * p.n_split + part;
-        float *op = p.o_part + r * HD + col0 + 4 * lg;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f32x4 *>(op + 16 * nb) = acc[nb] * inv;
-        if (hp == 0 && lg == 0) p.lse_part[r] = lse_val;
-    } else {
-        uint16_t *op = p.o + (int64_t)b * p.o_sb + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + col0 + 4 * lg;
+    for (int mt = 0; mt < MT; ++mt) {
+        if (!row_ok[mt]) continue;
+        const int t = t_of[mt], h = h_of[mt];
+        const float inv = lq[mt] > 0.f ? 1.f / lq[mt] : 0.f;
+        const float lse_val = l[mt] > 0.f ? (m[mt] + __log2f(l[mt])) * kLn2 : -INFINITY;
+        if constexpr (SPLIT) {
+            const int64_t r = (((int64_t)b * p.n_h + h) * p.T + t) * p.n_split + part;
+            float *op = p.o_part + r * HD + col0 + 4 * lg;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            uint2 packed;
-            packed.x = (uint32_t)bf16_bits(acc[nb][0] * inv) | ((uint32_t)bf16_bits(acc[nb][1] * inv) << 16);
-            packed.y = (uint32_t)bf16_bits(acc[nb][2] * inv) | ((uint32_t)bf16_bits(acc[nb][3] * inv) << 16);
-            *reinterpret_cast<uint2 *>(op + 16 * nb) = packed;
+            for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f32x4 *>(op + 16 * nb) = acc[mt][nb] * inv;
+            if (hp == 0 && lg == 0) p.lse_part[r] = lse_val;
+        } else {
+            uint16_t *op = p.o + (int64_t)b * p.o_sb + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + col0 + 4 * lg;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                uint2 packed;
+                packed.x = (uint32_t)bf16_bits(acc[mt][nb][0] * inv) |
+                           ((uint32_t)bf16_bits(acc[mt][nb][1] * inv) << 16);
+                packed.y = (uint32_t)bf16_bits(acc[mt][nb][2] * inv) |
+                           ((uint32_t)bf16_bits(acc[mt][nb][3] * inv) << 16);
+                *reinterpret_cast<uint2 *>(op + 16 * nb) = packed;
+            }
+            if (hp == 0 && lg == 0 && p.lse != nullptr) p.lse[((int64_t)b * p.n_h + h) * p.T + t] = lse_val;
         }
-        if (hp == 0 && lg == 0 && p.lse != nullptr) p.lse[((int64_t)b * p.n_h + h) * p.T + t] = lse_val;
     }
 }
 

@@ -69,9 +69,12 @@ FwdParams make_params(const void *q, const void *k, const void *v, int batch, in
     return p;
 }
 
-// One workgroup per (16-row tile, KV head, partition, batch).  The four
-// waves split keys (NK groups) and head-dim columns (NH parts of 64 or 128):
-// hd 64/128 -> 4 key groups, hd 256 -> 2 x 2, hd 512 -> 4 head parts.
+// One workgroup per (block of MT 16-row tiles, KV head, partition, batch).
+// The four waves split keys (NK groups) and head-dim columns (NH parts of 64
+// or 128): hd 64/128 -> 4 key groups, hd 256 -> 2 x 2, hd 512 -> 4 head parts.
+// compute units of an MI355X (8 XCDs x 32)
+constexpr int kComputeUnits = 256;
+
 template <int HD>
 struct Waves;
 template <> struct Waves<64> { static constexpr int NK = 4, NH = 1; };
@@ -79,26 +82,35 @@ template <> struct Waves<128> { static constexpr int NK = 4, NH = 1; };
 template <> struct Waves<256> { static constexpr int NK = 2, NH = 2; };
 template <> struct Waves<512> { static constexpr int NK = 1, NH = 4; };
 
-template <int HD, bool SPLIT>
-hipError_t launch_hd(FwdParams p, hipStream_t stream) {
-    p.n_row_blocks = (p.rows + 15) / 16;
+template <int HD, int MT, bool SPLIT, bool ONE>
+hipError_t launch_tiles(FwdParams p, hipStream_t stream) {
+    p.n_row_blocks = (p.rows + 16 * MT - 1) / (16 * MT);
     const int64_t units = (int64_t)p.n_row_blocks * p.n_split * p.n_kv_h * p.batch;
     if (units > 0x7fffffff) return hipErrorInvalidConfiguration;
     p.n_units = (int)units;
-    // only row tiles share data across workgroups; streaming units run best
+    // only row blocks share data across workgroups; streaming units run best
     // in plain order (neighbouring blocks read neighbouring memory)
     p.xcd_remap = (p.n_row_blocks > 1 && p.n_units % 8 == 0) ? 1 : 0;
     constexpr int NK = Waves<HD>::NK, NH = Waves<HD>::NH;
-    // the widest key range any workgroup can see: one chunk of 32*NK keys?
+    hipLaunchKernelGGL((fmha::attn_kernel<HD, NK, NH, MT, SPLIT, ONE>), dim3(p.n_units), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int HD, bool SPLIT>
+hipError_t launch_hd(const FwdParams &p, hipStream_t stream) {
+    constexpr int NK = Waves<HD>::NK;
+    // the widest key range any 16-row tile can see: one chunk of 32*NK keys?
     int span = p.split_len < p.s_k ? p.split_len : p.s_k;
     // causal + window: a tile's rows span at most 16 positions, so at most
     // window + 15 keys are visible to any of them
     if (p.causal && p.window > 0 && p.window + 15 < span) span = p.window + 15;
-    if (span <= 32 * NK)
-        hipLaunchKernelGGL((fmha::attn_kernel<HD, NK, NH, SPLIT, true>), dim3(p.n_units), dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL((fmha::attn_kernel<HD, NK, NH, SPLIT, false>), dim3(p.n_units), dim3(256), 0, stream, p);
-    return hipGetLastError();
+    if (span <= 32 * NK) return launch_tiles<HD, 1, SPLIT, true>(p, stream);
+    // several slices per workgroup: two tiles per workgroup share every K/V
+    // load, worth it while that still leaves two workgroups per compute unit
+    // (the multi-slice kernel's occupancy); below that, parallelism wins
+    const int64_t blocks2 = (int64_t)((p.rows + 31) / 32) * p.n_split * p.n_kv_h * p.batch;
+    if (p.rows > 16 && blocks2 >= 2 * kComputeUnits) return launch_tiles<HD, 2, SPLIT, false>(p, stream);
+    return launch_tiles<HD, 1, SPLIT, false>(p, stream);
 }
 
 template <bool SPLIT>

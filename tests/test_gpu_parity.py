@@ -260,6 +260,25 @@ def test_results_are_deterministic():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 40)])
+def test_two_tile_workgroups_ragged(hd, causal, window):
+    """Shapes with many row blocks and multi-slice key ranges, where a
+    workgroup takes two 16-row tiles: 200 stacked rows per KV head (GQA
+    group 2, T = 100), so the last block holds 8 rows in its first tile and
+    none in its second; also through split-KV with two partitions."""
+    b, T, n_h, n_kv_h, s_k = 4, 100, 64, 32, 300
+    q = I.randn_bf16((b, T, n_h, hd), 300 + hd)
+    k = I.randn_bf16((b, s_k, n_kv_h, hd), 301 + hd)
+    v = I.randn_bf16((b, s_k, n_kv_h, hd), 302 + hd)
+    scale = 1.0 / math.sqrt(hd)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=causal, window=window)
+    o, lse = gpu_forward(q, k, v, scale, causal, window)
+    check_attention(o, lse, o_ref, lse_ref, what="two-tile forward")
+    o, lse, _, _ = gpu_split(q, k, v, scale, 160, causal, window)
+    check_attention(o, lse, o_ref, lse_ref, what="two-tile split+merge")
+
+
 # ---------------------------------------------------------------------------
 # Split-KV and the merge kernel
 # ---------------------------------------------------------------------------
