@@ -80,10 +80,15 @@ struct AttnShape {
 // MT: 16-row tiles per workgroup.  Two when a workgroup streams several
 // slices for more than 16 rows: each K/V byte brought on chip then serves
 // twice the rows.
-template <int HD, int NK, int NH, int MT, bool SPLIT, bool ONE>
+// STREAM (one-slice work with a single row block per KV head): no other
+// workgroup reads this workgroup's V, so it is fetched with the non-temporal
+// hint.  Split partials are always stored with it: the merge reads them in a
+// later launch.
+template <int HD, int NK, int NH, int MT, bool SPLIT, bool ONE, bool STREAM>
 __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kernel(const FwdParams p) {
     using S = AttnShape<HD, NK, NH, MT>;
     static_assert(MT == 1 || !ONE, "one-slice work uses single tiles");
+    static_assert(ONE || !STREAM, "only one-slice work streams");
     constexpr int HDP = S::HDP, KSTEPS = S::KSTEPS, NB = S::NB, CHUNKS = S::CHUNKS;
     constexpr int ROW_BYTES = S::ROW_BYTES, KEYS_PER_LOAD = S::KEYS_PER_LOAD, VLOADS = S::VLOADS;
     constexpr int SLOTS = S::SLOTS;
@@ -319,7 +324,7 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
                     const int r = it * KEYS_PER_LOAD + v_row_in_load;
                     const int chunk = (v_slot - rot_of(r) + CHUNKS) % CHUNKS;
                     const int key = min(k0 + r, khi - 1);
-                    load_lds_16(vbase + (int64_t)key * p.v_st + chunk * 8, sVw + it * 64 * 16);
+                    load_lds_16<STREAM>(vbase + (int64_t)key * p.v_st + chunk * 8, sVw + it * 64 * 16);
                 }
                 load_k(k0, kf);
                 __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
@@ -468,7 +473,8 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
             const int64_t r = (((int64_t)b * p.n_h + h) * p.T + t) * p.n_split + part;
             float *op = p.o_part + r * HD + col0 + 4 * lg;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f32x4 *>(op + 16 * nb) = acc[mt][nb] * inv;
+            for (int nb = 0; nb < NB; ++nb)
+                __builtin_nontemporal_store(acc[mt][nb] * inv, reinterpret_cast<f32x4 *>(op + 16 * nb));
             if (hp == 0 && lg == 0) p.lse_part[r] = lse_val;
         } else {
             uint16_t *op = p.o + (int64_t)b * p.o_sb + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + col0 + 4 * lg;

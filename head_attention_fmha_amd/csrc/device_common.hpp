@@ -46,8 +46,11 @@ constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 // (global_load_lds_dwordx4): lane L's data lands at lds_base + 16*L.  The
 // LDS write completes asynchronously and is tracked by vmcnt, not by the
 // compiler: wait with s_waitcnt vmcnt before reading the destination.
+// NT: non-temporal hint (the nt cache-policy bit) for data that no other
+// workgroup will read again, so it does not displace data that will be.
+template <bool NT = false>
 __device__ __forceinline__ void load_lds_16(const void *gptr, void *lds_base) {
-    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 16, 0, NT ? 2 : 0);
 }
 
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).

@@ -92,7 +92,10 @@ hipError_t launch_tiles(FwdParams p, hipStream_t stream) {
     // in plain order (neighbouring blocks read neighbouring memory)
     p.xcd_remap = (p.n_row_blocks > 1 && p.n_units % 8 == 0) ? 1 : 0;
     constexpr int NK = Waves<HD>::NK, NH = Waves<HD>::NH;
-    hipLaunchKernelGGL((fmha::attn_kernel<HD, NK, NH, MT, SPLIT, ONE>), dim3(p.n_units), dim3(256), 0, stream, p);
+    if (ONE && p.n_row_blocks == 1)
+        hipLaunchKernelGGL((fmha::attn_kernel<HD, NK, NH, MT, SPLIT, ONE, ONE>), dim3(p.n_units), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fmha::attn_kernel<HD, NK, NH, MT, SPLIT, ONE, false>), dim3(p.n_units), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
