@@ -12,6 +12,7 @@ Entry points carry the C names:
   fmha_decode_splitkv(q, k, v, o_part, lse_part, *, split_len, scale=None, window=0, causal=False)
   fmha_lse_merge(o_part, lse_part, o, lse=None)
   fmha_status_string(status)
+  fmha_attention_plan(batch, n_h, n_kv_h, T, s_k, hd, *, window=0, causal=False, split_len=0, mqa_stride0=False)
 Layouts: q, o [batch, T, n_h, hd]; k, v [batch, s_k, n_kv_h, hd] (a head
 stride of 0 expresses MQA); lse [batch, n_h, T];
 o_part [batch, n_h, T, n_split, hd]; lse_part [batch, n_h, T, n_split].
@@ -26,7 +27,7 @@ from typing import Optional
 import torch
 
 __all__ = ["FmhaError", "fmha_forward", "fmha_decode_splitkv", "fmha_lse_merge", "fmha_status_string",
-           "n_split_for", "library_path", "load_library", "FmhaStrides"]
+           "fmha_attention_plan", "n_split_for", "library_path", "load_library", "FmhaStrides", "FmhaPlan"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfmha.so")
@@ -41,6 +42,11 @@ class FmhaError(RuntimeError):
 
 class FmhaStrides(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("token", ctypes.c_int64), ("head", ctypes.c_int64)]
+
+
+class FmhaPlan(ctypes.Structure):
+    _fields_ = [("waves_per_group", ctypes.c_int), ("tiles_per_group", ctypes.c_int),
+                ("one_slice", ctypes.c_int), ("streaming", ctypes.c_int), ("workgroups", ctypes.c_int64)]
 
 
 def library_path() -> str:
@@ -62,6 +68,8 @@ def load_library():
     lib.fmha_decode_splitkv.restype = I
     lib.fmha_lse_merge.argtypes = [P, P, P, P, I, I, I, I, I, S, P]
     lib.fmha_lse_merge.restype = I
+    lib.fmha_attention_plan.argtypes = [I, I, I, I, I, I, S, S, I, I, I, ctypes.POINTER(FmhaPlan)]
+    lib.fmha_attention_plan.restype = I
     lib.fmha_status_string.argtypes = [I]
     lib.fmha_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -166,3 +174,15 @@ def fmha_lse_merge(o_part, lse_part, o, lse=None, *, stream=None) -> None:
     _dense(lse, (b, n_h, T), "lse")
     _check(load_library().fmha_lse_merge(
         _ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), b, n_h, T, hd, ns, _st(o), _stream(stream)))
+
+
+def fmha_attention_plan(batch, n_h, n_kv_h, T, s_k, hd, *, window=0, causal=False, split_len=0,
+                        mqa_stride0=False) -> dict:
+    """How a call of these sizes would run (host-only; see include/fmha.h).
+    split_len = 0 asks about fmha_forward, > 0 about fmha_decode_splitkv;
+    mqa_stride0 describes K/V given with head stride 0."""
+    kv_st = FmhaStrides(0, 0, 0 if mqa_stride0 else hd)
+    plan = FmhaPlan()
+    _check(load_library().fmha_attention_plan(batch, n_h, n_kv_h, T, s_k, hd, kv_st, kv_st, int(window),
+                                              int(bool(causal)), int(split_len), ctypes.byref(plan)))
+    return {name: getattr(plan, name) for name, _ in FmhaPlan._fields_}

@@ -1,12 +1,12 @@
 // attn_kernel.hpp -- the fused attention kernel for gfx950.
 //
-// One workgroup (4 waves) computes MT adjacent 16-row tiles of one (batch,
-// kv head) over one key range.  A row is one (query position t, query head h)
+// One workgroup (NW = 4 or 8 waves) computes MT adjacent 16-row tiles of one
+// (batch, kv head) over one key range.  A row is one (query position t, query head h)
 // that reads this KV head, numbered r = t * group + (h - kv*group): the
 // GQA/MQA query heads sharing K/V are stacked into the same MFMA tile, and
 // the rows of a tile have the same or adjacent positions (tight mask ranges).
 //
-// The four waves form NK key groups x NH head-dimension parts (HDP = HD/NH
+// The NW waves form NK key groups x NH head-dimension parts (HDP = HD/NH
 // columns each, 64 or 128); every wave covers all MT tiles:
 //   * key group g takes keys [c + 32g, c + 32g + 32) of every chunk of
 //     32*NK keys and keeps its own online-softmax state; the NK groups are
@@ -55,9 +55,9 @@
 
 namespace fmha {
 
-template <int HD, int NK, int NH, int MT>
+template <int HD, int NW, int NK, int NH, int MT>
 struct AttnShape {
-    static_assert(NK * NH == 4, "four waves per workgroup");
+    static_assert(NK * NH == NW && (NW == 4 || NW == 8), "four or eight waves per workgroup");
     static constexpr int HDP = HD / NH;               // head-dim columns per wave
     static constexpr int KSTEPS = HDP / 32;           // QK MFMA steps
     static constexpr int NB = HDP / 16;               // 16-column blocks of O^T
@@ -67,7 +67,7 @@ struct AttnShape {
     static constexpr int VLOADS = 32 / KEYS_PER_LOAD;
     static constexpr int SLOTS = NB * 4 + 3;          // merge record per lane and tile: m, l, lq, O^T
     static constexpr int M_BYTES = (NK - 1) * NH * MT * SLOTS * 64 * 4;
-    static constexpr int S_FLOATS = MT * 4 * 8 * 64;  // one buffer of partial scores
+    static constexpr int S_FLOATS = MT * NW * 8 * 64;  // one buffer of partial scores
     static constexpr int S_BUF = NH > 1 ? S_FLOATS * 4 : 0;
     static_assert(HDP == 64 || HDP == 128, "head-dim part of 64 or 128 columns");
 };
@@ -84,9 +84,13 @@ struct AttnShape {
 // workgroup reads this workgroup's V, so it is fetched with the non-temporal
 // hint.  Split partials are always stored with it: the merge reads them in a
 // later launch.
-template <int HD, int NK, int NH, int MT, bool SPLIT, bool ONE, bool STREAM>
-__global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kernel(const FwdParams p) {
-    using S = AttnShape<HD, NK, NH, MT>;
+// NW = 8: for grids too small to fill the chip twice, twice the key groups
+// per workgroup halve the slices each wave walks through in sequence.
+constexpr int attn_min_waves(int nw, int nh, bool one) { return one ? (nw == 4 && nh == 1 ? 5 : 4) : 2; }
+
+template <int HD, int NW, int NK, int NH, int MT, bool SPLIT, bool ONE, bool STREAM>
+__global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_kernel(const FwdParams p) {
+    using S = AttnShape<HD, NW, NK, NH, MT>;
     static_assert(MT == 1 || !ONE, "one-slice work uses single tiles");
     static_assert(ONE || !STREAM, "only one-slice work streams");
     constexpr int HDP = S::HDP, KSTEPS = S::KSTEPS, NB = S::NB, CHUNKS = S::CHUNKS;
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
     constexpr int SLOTS = S::SLOTS;
     // one V slice per wave (the final key-group merge reuses that space);
     // partial-score buffers alternate by slice parity (one suffices for ONE)
-    constexpr int V_BYTES = 4 * 32 * ROW_BYTES;
+    constexpr int V_BYTES = NW * 32 * ROW_BYTES;
     constexpr int VM_BYTES = V_BYTES > S::M_BYTES ? V_BYTES : S::M_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char smem[VM_BYTES + (ONE ? 1 : 2) * S::S_BUF];
 
@@ -216,8 +220,8 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        buf[((mt * 4 + wave) * 8 + j) * 64 + lane] = s0[mt][j];
-                        buf[((mt * 4 + wave) * 8 + 4 + j) * 64 + lane] = s1[mt][j];
+                        buf[((mt * NW + wave) * 8 + j) * 64 + lane] = s0[mt][j];
+                        buf[((mt * NW + wave) * 8 + 4 + j) * 64 + lane] = s1[mt][j];
                     }
             }
             __syncthreads();
@@ -229,8 +233,8 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
                         float a = 0.f, c2 = 0.f;
 #pragma unroll
                         for (int q = 0; q < NH; ++q) {
-                            a += buf[((mt * 4 + kg * NH + q) * 8 + j) * 64 + lane];
-                            c2 += buf[((mt * 4 + kg * NH + q) * 8 + 4 + j) * 64 + lane];
+                            a += buf[((mt * NW + kg * NH + q) * 8 + j) * 64 + lane];
+                            c2 += buf[((mt * NW + kg * NH + q) * 8 + 4 + j) * 64 + lane];
                         }
                         s0[mt][j] = a;
                         s1[mt][j] = c2;
@@ -373,7 +377,7 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
             pv(alpha, pt);
         };
-        if constexpr (MT == 1) {
+        if constexpr (MT == 1 && NW == 4) {
             // two slices per iteration, both loaded up front: the second
             // slice's loads are in flight while the first is computed.  The
             // loads are unconditional (key indices clamp to khi-1, so a slice
@@ -392,7 +396,8 @@ __global__ __launch_bounds__(256, (ONE ? (NH == 1 ? 5 : 4) : 2)) void attn_kerne
                 if (n + 1 < nslices) step(n + 1, kfB, vrB);
             }
         } else {
-            // two tiles already double the math per loaded slice; one slice per
+            // two tiles already double the math per loaded slice, and eight
+            // waves already overlap one another's loads; one slice per
             // iteration keeps the registers within two waves per SIMD
             for (int n = 0; n < nslices; ++n) {
                 bf16x8 kf[2][KSTEPS];

@@ -28,18 +28,25 @@ bool strides_ok(const fmha_strides &st) {
 
 bool hd_supported(int hd) { return hd == 64 || hd == 128 || hd == 256 || hd == 512; }
 
-// Shared validation of fmha_forward / fmha_decode_splitkv.
-int validate_attention(const void *q, const void *k, const void *v, const void *out0, const void *out1,
-                       bool out1_required, int batch, int n_h, int n_kv_h, int T, int s_k, int hd,
-                       const fmha_strides &q_st, const fmha_strides &k_st, const fmha_strides &v_st,
-                       const fmha_strides *o_st, int window, int causal) {
-    if (!q || !k || !v || !out0 || (out1_required && !out1)) return FMHA_ERR_INVALID_ARG;
+// Sizes and mask arguments of an attention call.
+int validate_dims(int batch, int n_h, int n_kv_h, int T, int s_k, int hd, int window, int causal) {
     if (batch <= 0 || n_h <= 0 || n_kv_h <= 0 || T <= 0 || s_k <= 0 || hd <= 0) return FMHA_ERR_INVALID_ARG;
     if (n_h % n_kv_h != 0) return FMHA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FMHA_ERR_INVALID_ARG;
     if (window < 0) return FMHA_ERR_INVALID_ARG;
     if ((causal || window > 0) && T > s_k) return FMHA_ERR_INVALID_ARG;
     if (!hd_supported(hd) || T > 128) return FMHA_ERR_UNSUPPORTED;
+    return FMHA_OK;
+}
+
+// Shared validation of fmha_forward / fmha_decode_splitkv.
+int validate_attention(const void *q, const void *k, const void *v, const void *out0, const void *out1,
+                       bool out1_required, int batch, int n_h, int n_kv_h, int T, int s_k, int hd,
+                       const fmha_strides &q_st, const fmha_strides &k_st, const fmha_strides &v_st,
+                       const fmha_strides *o_st, int window, int causal) {
+    if (!q || !k || !v || !out0 || (out1_required && !out1)) return FMHA_ERR_INVALID_ARG;
+    const int rc = validate_dims(batch, n_h, n_kv_h, T, s_k, hd, window, causal);
+    if (rc != FMHA_OK) return rc;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out0) || (out1 && !aligned16(out1)))
         return FMHA_ERR_ALIGNMENT;
     if (!strides_ok(q_st) || !strides_ok(k_st) || !strides_ok(v_st) || (o_st && !strides_ok(*o_st)))
@@ -69,64 +76,88 @@ FwdParams make_params(const void *q, const void *k, const void *v, int batch, in
     return p;
 }
 
-// One workgroup per (block of MT 16-row tiles, KV head, partition, batch).
-// The four waves split keys (NK groups) and head-dim columns (NH parts of 64
-// or 128): hd 64/128 -> 4 key groups, hd 256 -> 2 x 2, hd 512 -> 4 head parts.
 // compute units of an MI355X (8 XCDs x 32)
 constexpr int kComputeUnits = 256;
 
-template <int HD>
-struct Waves;
-template <> struct Waves<64> { static constexpr int NK = 4, NH = 1; };
-template <> struct Waves<128> { static constexpr int NK = 4, NH = 1; };
-template <> struct Waves<256> { static constexpr int NK = 2, NH = 2; };
-template <> struct Waves<512> { static constexpr int NK = 1, NH = 4; };
+// Head-dim parts per workgroup: one up to hd 128, two at 256, four at 512
+// (64 or 128 columns per wave).
+int head_parts(int hd) { return hd <= 128 ? 1 : hd / 128; }
 
-template <int HD, int MT, bool SPLIT, bool ONE>
-hipError_t launch_tiles(FwdParams p, hipStream_t stream) {
-    p.n_row_blocks = (p.rows + 16 * MT - 1) / (16 * MT);
-    const int64_t units = (int64_t)p.n_row_blocks * p.n_split * p.n_kv_h * p.batch;
-    if (units > 0x7fffffff) return hipErrorInvalidConfiguration;
-    p.n_units = (int)units;
-    // only row blocks share data across workgroups; streaming units run best
-    // in plain order (neighbouring blocks read neighbouring memory)
-    p.xcd_remap = (p.n_row_blocks > 1 && p.n_units % 8 == 0) ? 1 : 0;
-    constexpr int NK = Waves<HD>::NK, NH = Waves<HD>::NH;
-    if (ONE && p.n_row_blocks == 1)
-        hipLaunchKernelGGL((fmha::attn_kernel<HD, NK, NH, MT, SPLIT, ONE, ONE>), dim3(p.n_units), dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL((fmha::attn_kernel<HD, NK, NH, MT, SPLIT, ONE, false>), dim3(p.n_units), dim3(256), 0, stream, p);
-    return hipGetLastError();
-}
-
-template <int HD, bool SPLIT>
-hipError_t launch_hd(const FwdParams &p, hipStream_t stream) {
-    constexpr int NK = Waves<HD>::NK;
-    // the widest key range any 16-row tile can see: one chunk of 32*NK keys?
+// The kernel variant and grid for one call.  A workgroup serves MT 16-row
+// tiles of one (batch, KV head, partition); its NW waves split head-dim
+// columns (NH parts) and keys (NK = NW / NH groups of 32-key slices).
+fmha_plan plan_attention(const FwdParams &p, int hd) {
+    fmha_plan pl{};
+    // the widest key range any 16-row tile can see
     int span = p.split_len < p.s_k ? p.split_len : p.s_k;
     // causal + window: a tile's rows span at most 16 positions, so at most
     // window + 15 keys are visible to any of them
     if (p.causal && p.window > 0 && p.window + 15 < span) span = p.window + 15;
-    if (span <= 32 * NK) return launch_tiles<HD, 1, SPLIT, true>(p, stream);
+    // too few 16-row units to give every compute unit two workgroups, at head
+    // dims whose four waves hold only one or two key groups, and keys enough
+    // for several slices per wave even with eight: eight waves per workgroup,
+    // so each walks half as many slices in sequence (at hd <= 128 four key
+    // groups already share the keys, and eight only add merge work)
+    const int64_t units1 = (int64_t)((p.rows + 15) / 16) * p.n_split * p.n_kv_h * p.batch;
+    const bool few_units = units1 < 2 * kComputeUnits;
+    pl.waves_per_group = (hd >= 256 && few_units && span > 32 * (8 / head_parts(hd))) ? 8 : 4;
+    const int nk = pl.waves_per_group / head_parts(hd);
+    // one chunk of 32*NK keys covers every range: the one-slice variant
+    pl.one_slice = span <= 32 * nk ? 1 : 0;
     // several slices per workgroup: two tiles per workgroup share every K/V
     // load, worth it while that still leaves two workgroups per compute unit
     // (the multi-slice kernel's occupancy); below that, parallelism wins
-    const int64_t blocks2 = (int64_t)((p.rows + 31) / 32) * p.n_split * p.n_kv_h * p.batch;
-    if (p.rows > 16 && blocks2 >= 2 * kComputeUnits) return launch_tiles<HD, 2, SPLIT, false>(p, stream);
-    return launch_tiles<HD, 1, SPLIT, false>(p, stream);
+    pl.tiles_per_group = 1;
+    if (!pl.one_slice && pl.waves_per_group == 4 && p.rows > 16) {
+        const int64_t blocks2 = (int64_t)((p.rows + 31) / 32) * p.n_split * p.n_kv_h * p.batch;
+        if (blocks2 >= 2 * kComputeUnits) pl.tiles_per_group = 2;
+    }
+    const int rows_per_group = 16 * pl.tiles_per_group;
+    const int row_blocks = (p.rows + rows_per_group - 1) / rows_per_group;
+    // one slice and one row block per KV head: nothing another workgroup reads
+    pl.streaming = (pl.one_slice && row_blocks == 1) ? 1 : 0;
+    pl.workgroups = (int64_t)row_blocks * p.n_split * p.n_kv_h * p.batch;
+    return pl;
+}
+
+template <int HD, int NW, int MT, bool SPLIT, bool ONE, bool STREAM>
+void launch_kernel(const FwdParams &p, hipStream_t stream) {
+    constexpr int NH = HD <= 128 ? 1 : HD / 128;
+    constexpr int NK = NW / NH;
+    hipLaunchKernelGGL((fmha::attn_kernel<HD, NW, NK, NH, MT, SPLIT, ONE, STREAM>), dim3(p.n_units), dim3(64 * NW),
+                       0, stream, p);
+}
+
+template <int HD, bool SPLIT>
+void launch_hd(const FwdParams &p, const fmha_plan &pl, hipStream_t s) {
+    if (pl.waves_per_group == 8) {
+        // chosen only for several slices per wave (never one-slice), hd >= 256
+        if constexpr (HD >= 256) launch_kernel<HD, 8, 1, SPLIT, false, false>(p, s);
+    } else {
+        if (pl.one_slice && pl.streaming) launch_kernel<HD, 4, 1, SPLIT, true, true>(p, s);
+        else if (pl.one_slice) launch_kernel<HD, 4, 1, SPLIT, true, false>(p, s);
+        else if (pl.tiles_per_group == 2) launch_kernel<HD, 4, 2, SPLIT, false, false>(p, s);
+        else launch_kernel<HD, 4, 1, SPLIT, false, false>(p, s);
+    }
 }
 
 template <bool SPLIT>
-int launch_attention(const FwdParams &p, int hd, void *stream) {
+int launch_attention(FwdParams p, int hd, void *stream) {
+    const fmha_plan pl = plan_attention(p, hd);
+    if (pl.workgroups > 0x7fffffff) return FMHA_ERR_UNSUPPORTED;
+    p.n_row_blocks = (p.rows + 16 * pl.tiles_per_group - 1) / (16 * pl.tiles_per_group);
+    p.n_units = (int)pl.workgroups;
+    // only row blocks share data across workgroups; streaming units run best
+    // in plain order (neighbouring blocks read neighbouring memory)
+    p.xcd_remap = (p.n_row_blocks > 1 && p.n_units % 8 == 0) ? 1 : 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t err;
     switch (hd) {
-        case 64: err = launch_hd<64, SPLIT>(p, s); break;
-        case 128: err = launch_hd<128, SPLIT>(p, s); break;
-        case 256: err = launch_hd<256, SPLIT>(p, s); break;
-        default: err = launch_hd<512, SPLIT>(p, s); break;
+        case 64: launch_hd<64, SPLIT>(p, pl, s); break;
+        case 128: launch_hd<128, SPLIT>(p, pl, s); break;
+        case 256: launch_hd<256, SPLIT>(p, pl, s); break;
+        default: launch_hd<512, SPLIT>(p, pl, s); break;
     }
-    return err == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+    return hipGetLastError() == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -200,6 +231,20 @@ int fmha_lse_merge(const float *o_part, const float *lse_part, void *o, float *l
         default: hipLaunchKernelGGL(fmha::merge_kernel<512>, grid, block, 0, s, p); break;
     }
     return hipGetLastError() == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+}
+
+int fmha_attention_plan(int batch, int n_h, int n_kv_h, int T, int s_k, int hd, fmha_strides k_st,
+                        fmha_strides v_st, int window, int causal, int split_len, fmha_plan *plan) {
+    if (!plan || split_len < 0) return FMHA_ERR_INVALID_ARG;
+    const int rc = validate_dims(batch, n_h, n_kv_h, T, s_k, hd, window, causal);
+    if (rc != FMHA_OK) return rc;
+    const fmha_strides none{0, 0, 0};
+    FwdParams p = make_params(nullptr, nullptr, nullptr, batch, n_h, n_kv_h, T, s_k, none, k_st, v_st, 1.f,
+                              window, causal);
+    p.split_len = split_len == 0 ? s_k : split_len;
+    p.n_split = (int)(((int64_t)s_k + p.split_len - 1) / p.split_len);
+    *plan = plan_attention(p, hd);
+    return FMHA_OK;
 }
 
 const char *fmha_status_string(int status) {

@@ -146,6 +146,36 @@ int fmha_lse_merge(const float *o_part, const float *lse_part, void *o, float *l
                    int batch, int n_h, int T, int hd, int n_split,
                    fmha_strides o_st, void *stream);
 
+/*
+ * How fmha_forward (split_len = 0) or fmha_decode_splitkv (split_len > 0)
+ * would run a call of these sizes: a host-only query that launches nothing
+ * and needs no device, for diagnostics and tests that must reach every
+ * kernel variant.  The work decomposition (one unit per batch, KV head,
+ * row block and key partition) refines the per-(head, batch) grid of the
+ * commit log at e4ee9fdc for this hardware.
+ *
+ *   waves_per_group  4 or 8: wavefronts per workgroup; 8 when fewer than
+ *                    two 16-row units per compute unit exist
+ *   tiles_per_group  1 or 2: 16-row tiles per workgroup
+ *   one_slice        1 when every workgroup's key range fits one pass
+ *   streaming        1 when no two workgroups read the same K/V rows
+ *   workgroups       grid size
+ * k_st / v_st matter only through their head strides (both 0 = MQA).
+ * Errors: as fmha_forward for sizes and mask arguments;
+ * FMHA_ERR_INVALID_ARG for a null plan or split_len < 0.
+ */
+typedef struct {
+    int waves_per_group;
+    int tiles_per_group;
+    int one_slice;
+    int streaming;
+    int64_t workgroups;
+} fmha_plan;
+
+int fmha_attention_plan(int batch, int n_h, int n_kv_h, int T, int s_k, int hd,
+                        fmha_strides k_st, fmha_strides v_st, int window, int causal,
+                        int split_len, fmha_plan *plan);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *fmha_status_string(int status);
 

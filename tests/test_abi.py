@@ -28,8 +28,9 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(fmha_[a-z_]+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_four_entry_points():
-    assert declared_functions() == ["fmha_decode_splitkv", "fmha_forward", "fmha_lse_merge", "fmha_status_string"]
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["fmha_attention_plan", "fmha_decode_splitkv", "fmha_forward", "fmha_lse_merge",
+                                    "fmha_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -107,3 +108,50 @@ def test_splitkv_rejects(lib, kw, code):
 ])
 def test_merge_rejects(lib, kw, code):
     assert merge(lib, **kw) == code
+
+
+# ---------------------------------------------------------------------------
+# The plan query: host-only, so the chosen kernel variant of each workload can
+# be checked here
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("args,kw,want", [
+    # split-KV GQA decode, 64 partitions of 128 keys: one slice, streamed
+    ((32, 64, 8, 1, 8192, 128), dict(split_len=128), (4, 1, 1, 1, 16384)),
+    # MQA decode (128 heads on one KV head), 512 keys: few units, eight waves
+    ((8, 128, 1, 1, 512, 512), {}, (8, 1, 0, 0, 64)),
+    # the same through a head stride of 0 with n_kv_h = n_h: planned as MQA
+    ((8, 128, 128, 1, 512, 512), dict(mqa_stride0=True), (8, 1, 0, 0, 64)),
+    # causal prefill T = 128, s_k = 512: two tiles per workgroup
+    ((4, 32, 32, 128, 512, 512), dict(causal=True), (4, 2, 0, 0, 512)),
+    # causal prefill T = 32: 256 units, eight waves at hd 256 and 512 only
+    ((4, 32, 32, 32, 512, 256), dict(causal=True), (8, 1, 0, 0, 256)),
+    ((4, 32, 32, 32, 512, 128), dict(causal=True), (4, 1, 0, 0, 256)),
+    # single-head decode
+    ((1, 1, 1, 1, 128, 64), {}, (4, 1, 1, 1, 1)),
+    # sliding window MQA prefill: span window + 15 = 143 keys > 2 x 32
+    ((2, 16, 1, 128, 4096, 512), dict(causal=True, window=128), (8, 1, 0, 0, 256)),
+])
+def test_plan_of_each_workload(lib, args, kw, want):
+    got = fa.fmha_attention_plan(*args, **kw)
+    assert (got["waves_per_group"], got["tiles_per_group"], got["one_slice"], got["streaming"],
+            got["workgroups"]) == want
+
+
+@pytest.mark.parametrize("args,kw,code", [
+    ((1, 1, 1, 1, 128, 96), {}, UNSUPPORTED),
+    ((1, 1, 1, 129, 256, 64), {}, UNSUPPORTED),
+    ((1, 3, 2, 1, 128, 64), {}, INVALID),
+    ((1, 1, 1, 4, 2, 64), dict(causal=True), INVALID),
+    ((1, 1, 1, 1, 128, 64), dict(split_len=-1), INVALID),
+    ((0, 1, 1, 1, 128, 64), {}, INVALID),
+])
+def test_plan_rejects(lib, args, kw, code):
+    with pytest.raises(fa.FmhaError) as e:
+        fa.fmha_attention_plan(*args, **kw)
+    assert e.value.status == code
+
+
+def test_plan_rejects_null_output(lib):
+    st = FmhaStrides(0, 0, 64)
+    assert lib.fmha_attention_plan(1, 1, 1, 1, 128, 64, st, st, 0, 0, 0, None) == INVALID

@@ -279,6 +279,43 @@ def test_two_tile_workgroups_ragged(hd, causal, window):
     check_attention(o, lse, o_ref, lse_ref, what="two-tile split+merge")
 
 
+# Every kernel variant the host can choose, each with a shape that selects it
+# (checked through the plan query) and a parity check at every head dim:
+# (name, (batch, n_h, n_kv_h, T, s_k), split_len or 0, causal, window, plan)
+VARIANTS = [
+    ("4w-one-stream-small", (2, 4, 2, 3, 50), 0, True, 0, dict(waves_per_group=4, one_slice=1, streaming=1)),
+    ("4w-one-shared-small", (2, 8, 1, 5, 50), 0, False, 0, dict(waves_per_group=4, one_slice=1, streaming=0)),
+    ("8w-multi", (2, 8, 2, 20, 300), 0, True, 0, dict(waves_per_group=8, one_slice=0, tiles_per_group=1)),
+    ("4w-one-stream", (4, 8, 8, 1, 2048), 32, False, 0, dict(waves_per_group=4, one_slice=1, streaming=1)),
+    ("4w-one-shared", (4, 32, 2, 2, 1024), 32, True, 0, dict(waves_per_group=4, one_slice=1, streaming=0)),
+    ("4w-multi-1tile", (8, 64, 64, 1, 700), 0, True, 300, dict(waves_per_group=4, one_slice=0, tiles_per_group=1)),
+    ("4w-multi-2tile", (4, 64, 32, 100, 300), 0, True, 0, dict(waves_per_group=4, one_slice=0, tiles_per_group=2)),
+]
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+@pytest.mark.parametrize("name,dims,split_len,causal,window,plan", VARIANTS, ids=[v[0] for v in VARIANTS])
+def test_every_kernel_variant(name, dims, split_len, causal, window, plan, hd):
+    if plan["waves_per_group"] == 8 and hd < 256:
+        plan = dict(plan, waves_per_group=4)   # eight-wave groups serve hd 256 and 512 only
+    if hd == 512 and name.endswith("-small"):
+        plan = dict(plan, one_slice=0, streaming=0)  # 50 keys: more than one 32-key pass at hd 512
+    b, n_h, n_kv_h, T, s_k = dims
+    got = fa.fmha_attention_plan(b, n_h, n_kv_h, T, s_k, hd, window=window, causal=causal, split_len=split_len)
+    assert {k: got[k] for k in plan} == plan, got
+    seed = 400 + 7 * hd + len(name)
+    q = I.randn_bf16((b, T, n_h, hd), seed)
+    k = I.randn_bf16((b, s_k, n_kv_h, hd), seed + 1)
+    v = I.randn_bf16((b, s_k, n_kv_h, hd), seed + 2)
+    scale = 1.0 / math.sqrt(hd)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=causal, window=window)
+    if split_len:
+        o, lse, _, _ = gpu_split(q, k, v, scale, split_len, causal, window)
+    else:
+        o, lse = gpu_forward(q, k, v, scale, causal, window)
+    check_attention(o, lse, o_ref, lse_ref, what=name)
+
+
 # ---------------------------------------------------------------------------
 # Split-KV and the merge kernel
 # ---------------------------------------------------------------------------
