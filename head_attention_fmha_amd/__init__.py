@@ -46,7 +46,8 @@ class FmhaStrides(ctypes.Structure):
 
 class FmhaPlan(ctypes.Structure):
     _fields_ = [("waves_per_group", ctypes.c_int), ("tiles_per_group", ctypes.c_int),
-                ("one_slice", ctypes.c_int), ("streaming", ctypes.c_int), ("workgroups", ctypes.c_int64)]
+                ("one_slice", ctypes.c_int), ("streaming", ctypes.c_int), ("row_parallel", ctypes.c_int),
+                ("workgroups", ctypes.c_int64)]
 
 
 def library_path() -> str:

@@ -53,6 +53,20 @@ __device__ __forceinline__ void load_lds_16(const void *gptr, void *lds_base) {
     __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 16, 0, NT ? 2 : 0);
 }
 
+// Workgroup barrier for LDS staged by global_load_lds.  The caller has
+// already waited (vmcnt) for its own LDS-direct loads that others will read;
+// this waits for the wave's LDS reads and writes, then meets the other
+// waves.  A memory fence here would also wait for every global load in
+// flight -- the next chunk's prefetch -- as __syncthreads() does, because
+// LDS-direct loads count as LDS writes.  The signal fences keep the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 

@@ -11,6 +11,7 @@
 
 #include "fmha.h"
 #include "attn_kernel.hpp"
+#include "rows_kernel.hpp"
 #include "merge_kernel.hpp"
 
 namespace {
@@ -83,6 +84,13 @@ constexpr int kComputeUnits = 256;
 // (64 or 128 columns per wave).
 int head_parts(int hd) { return hd <= 128 ? 1 : hd / 128; }
 
+// Row-parallel kernel: one 16-row tile per wave (64 rows per workgroup, so
+// the short-prefill grids still give every compute unit a workgroup) and
+// keys per LDS chunk.  Used up to hd 256: at 512 the full-width Q and output
+// tiles crowd one wave's registers and the per-wave kernel is faster.
+constexpr int rows_tiles_per_wave(int) { return 1; }
+constexpr int rows_chunk_keys(int hd) { return hd <= 128 ? 64 : 32; }
+
 // The kernel variant and grid for one call.  A workgroup serves MT 16-row
 // tiles of one (batch, KV head, partition); its NW waves split head-dim
 // columns (NH parts) and keys (NK = NW / NH groups of 32-key slices).
@@ -112,6 +120,17 @@ fmha_plan plan_attention(const FwdParams &p, int hd) {
         const int64_t blocks2 = (int64_t)((p.rows + 31) / 32) * p.n_split * p.n_kv_h * p.batch;
         if (blocks2 >= 2 * kComputeUnits) pl.tiles_per_group = 2;
     }
+    // many rows per KV head and several passes over the keys: the row-parallel
+    // kernel, whose four waves share every K/V chunk through LDS
+    if (!pl.one_slice && p.rows >= 64 && hd <= 256) {
+        const int rows_rp = 64 * rows_tiles_per_wave(hd);
+        const int64_t groups_rp = (int64_t)((p.rows + rows_rp - 1) / rows_rp) * p.n_split * p.n_kv_h * p.batch;
+        if (groups_rp >= kComputeUnits) {
+            pl.row_parallel = 1;
+            pl.waves_per_group = 4;
+            pl.tiles_per_group = 4 * rows_tiles_per_wave(hd);
+        }
+    }
     const int rows_per_group = 16 * pl.tiles_per_group;
     const int row_blocks = (p.rows + rows_per_group - 1) / rows_per_group;
     // one slice and one row block per KV head: nothing another workgroup reads
@@ -130,7 +149,11 @@ void launch_kernel(const FwdParams &p, hipStream_t stream) {
 
 template <int HD, bool SPLIT>
 void launch_hd(const FwdParams &p, const fmha_plan &pl, hipStream_t s) {
-    if (pl.waves_per_group == 8) {
+    if (pl.row_parallel) {
+        if constexpr (HD <= 256)
+            hipLaunchKernelGGL((fmha::rows_kernel<HD, rows_tiles_per_wave(HD), rows_chunk_keys(HD), SPLIT>),
+                               dim3(p.n_units), dim3(256), 0, s, p);
+    } else if (pl.waves_per_group == 8) {
         // chosen only for several slices per wave (never one-slice), hd >= 256
         if constexpr (HD >= 256) launch_kernel<HD, 8, 1, SPLIT, false, false>(p, s);
     } else {

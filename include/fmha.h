@@ -156,9 +156,11 @@ int fmha_lse_merge(const float *o_part, const float *lse_part, void *o, float *l
  *
  *   waves_per_group  4 or 8: wavefronts per workgroup; 8 when fewer than
  *                    two 16-row units per compute unit exist
- *   tiles_per_group  1 or 2: 16-row tiles per workgroup
+ *   tiles_per_group  16-row tiles per workgroup (1 or 2; 4 or 8 row-parallel)
  *   one_slice        1 when every workgroup's key range fits one pass
  *   streaming        1 when no two workgroups read the same K/V rows
+ *   row_parallel     1 when each wave owns whole rows and the waves share
+ *                    K/V chunks staged in LDS (many rows per KV head)
  *   workgroups       grid size
  * k_st / v_st matter only through their head strides (both 0 = MQA).
  * Errors: as fmha_forward for sizes and mask arguments;
@@ -169,6 +171,7 @@ typedef struct {
     int tiles_per_group;
     int one_slice;
     int streaming;
+    int row_parallel;
     int64_t workgroups;
 } fmha_plan;
 

@@ -9,6 +9,7 @@ import pytest
 
 import head_attention_fmha_amd as fa
 from head_attention_fmha_amd import FmhaStrides
+import variant_shapes as VS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, INVALID, UNSUPPORTED, ALIGN, LAUNCH = 0, 1, 2, 3, 4
@@ -155,3 +156,13 @@ def test_plan_rejects(lib, args, kw, code):
 def test_plan_rejects_null_output(lib):
     st = FmhaStrides(0, 0, 64)
     assert lib.fmha_attention_plan(1, 1, 1, 1, 128, 64, st, st, 0, 0, 0, None) == INVALID
+
+
+@pytest.mark.parametrize("hd", list(VS.HEAD_DIMS))
+def test_variant_shapes_reach_every_kernel(lib, hd):
+    """The GPU variant table covers every kernel the dispatcher can launch."""
+    seen = set()
+    for name, dims, split_len, causal, window in VS.SHAPES:
+        plan = fa.fmha_attention_plan(*dims, hd, window=window, causal=causal, split_len=split_len)
+        seen.add(VS.branch(plan))
+    assert seen == VS.EXPECTED[hd]

@@ -12,6 +12,7 @@ import oracle
 import head_attention_fmha_amd as fa
 from head_attention_fmha_amd import inputs as I
 from attn_compare import check_attention
+import variant_shapes as VS
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -263,10 +264,12 @@ def test_results_are_deterministic():
 @pytest.mark.parametrize("hd", [64, 128, 256, 512])
 @pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 40)])
 def test_two_tile_workgroups_ragged(hd, causal, window):
-    """Shapes with many row blocks and multi-slice key ranges, where a
-    workgroup takes two 16-row tiles: 200 stacked rows per KV head (GQA
-    group 2, T = 100), so the last block holds 8 rows in its first tile and
-    none in its second; also through split-KV with two partitions."""
+    """Shapes with many row blocks and multi-slice key ranges: 200 stacked
+    rows per KV head (GQA group 2, T = 100).  At hd 512 a workgroup takes
+    two 16-row tiles, so the last block holds 8 rows in its first tile and
+    none in its second; up to hd 256 the row-parallel kernel runs, its last
+    64-row block holding 8 rows (three of its waves without a row).  Also
+    through split-KV with two partitions."""
     b, T, n_h, n_kv_h, s_k = 4, 100, 64, 32, 300
     q = I.randn_bf16((b, T, n_h, hd), 300 + hd)
     k = I.randn_bf16((b, s_k, n_kv_h, hd), 301 + hd)
@@ -279,30 +282,14 @@ def test_two_tile_workgroups_ragged(hd, causal, window):
     check_attention(o, lse, o_ref, lse_ref, what="two-tile split+merge")
 
 
-# Every kernel variant the host can choose, each with a shape that selects it
-# (checked through the plan query) and a parity check at every head dim:
-# (name, (batch, n_h, n_kv_h, T, s_k), split_len or 0, causal, window, plan)
-VARIANTS = [
-    ("4w-one-stream-small", (2, 4, 2, 3, 50), 0, True, 0, dict(waves_per_group=4, one_slice=1, streaming=1)),
-    ("4w-one-shared-small", (2, 8, 1, 5, 50), 0, False, 0, dict(waves_per_group=4, one_slice=1, streaming=0)),
-    ("8w-multi", (2, 8, 2, 20, 300), 0, True, 0, dict(waves_per_group=8, one_slice=0, tiles_per_group=1)),
-    ("4w-one-stream", (4, 8, 8, 1, 2048), 32, False, 0, dict(waves_per_group=4, one_slice=1, streaming=1)),
-    ("4w-one-shared", (4, 32, 2, 2, 1024), 32, True, 0, dict(waves_per_group=4, one_slice=1, streaming=0)),
-    ("4w-multi-1tile", (8, 64, 64, 1, 700), 0, True, 300, dict(waves_per_group=4, one_slice=0, tiles_per_group=1)),
-    ("4w-multi-2tile", (4, 64, 32, 100, 300), 0, True, 0, dict(waves_per_group=4, one_slice=0, tiles_per_group=2)),
-]
-
-
-@pytest.mark.parametrize("hd", [64, 128, 256, 512])
-@pytest.mark.parametrize("name,dims,split_len,causal,window,plan", VARIANTS, ids=[v[0] for v in VARIANTS])
-def test_every_kernel_variant(name, dims, split_len, causal, window, plan, hd):
-    if plan["waves_per_group"] == 8 and hd < 256:
-        plan = dict(plan, waves_per_group=4)   # eight-wave groups serve hd 256 and 512 only
-    if hd == 512 and name.endswith("-small"):
-        plan = dict(plan, one_slice=0, streaming=0)  # 50 keys: more than one 32-key pass at hd 512
+@pytest.mark.parametrize("hd", list(VS.HEAD_DIMS))
+@pytest.mark.parametrize("name,dims,split_len,causal,window", VS.SHAPES, ids=[v[0] for v in VS.SHAPES])
+def test_every_kernel_variant(name, dims, split_len, causal, window, hd):
+    """Each shape of the variant table (which, over all shapes, reaches every
+    kernel variant at every head dim) against the oracle."""
     b, n_h, n_kv_h, T, s_k = dims
-    got = fa.fmha_attention_plan(b, n_h, n_kv_h, T, s_k, hd, window=window, causal=causal, split_len=split_len)
-    assert {k: got[k] for k in plan} == plan, got
+    plan = fa.fmha_attention_plan(b, n_h, n_kv_h, T, s_k, hd, window=window, causal=causal, split_len=split_len)
+    sys.stderr.write(f"[gpu-case] plan {VS.branch(plan)} {plan}\n")
     seed = 400 + 7 * hd + len(name)
     q = I.randn_bf16((b, T, n_h, hd), seed)
     k = I.randn_bf16((b, s_k, n_kv_h, hd), seed + 1)

@@ -1,0 +1,40 @@
+"""Shapes that together reach every kernel variant the host dispatch can
+choose, at every head dimension.  The CPU suite checks the coverage through
+the plan query (no GPU needed); the GPU suite runs each shape against the
+oracle.  Entries: (name, (batch, n_h, n_kv_h, T, s_k), split_len (0 =
+fmha_forward), causal, window)."""
+
+SHAPES = [
+    ("one-slice-streamed-small", (2, 4, 2, 3, 50), 0, True, 0),
+    ("one-slice-shared-small", (2, 8, 1, 5, 50), 0, False, 0),
+    ("multi-few-units", (2, 8, 2, 20, 300), 0, True, 0),
+    ("one-slice-streamed-split", (4, 8, 8, 1, 2048), 32, False, 0),
+    ("one-slice-shared-split", (4, 32, 2, 2, 1024), 32, True, 0),
+    ("multi-one-tile", (8, 64, 64, 1, 700), 0, True, 300),
+    ("multi-two-tiles", (32, 16, 8, 20, 300), 0, True, 0),
+    ("row-parallel-gqa", (4, 64, 32, 100, 300), 0, True, 0),
+    ("row-parallel-window", (4, 64, 64, 100, 300), 0, True, 70),
+]
+
+HEAD_DIMS = (64, 128, 256, 512)
+
+
+def branch(plan: dict) -> str:
+    """The kernel variant a plan launches."""
+    if plan["row_parallel"]:
+        return "row-parallel"
+    if plan["waves_per_group"] == 8:
+        return "eight-waves"
+    if plan["one_slice"]:
+        return "one-slice-streamed" if plan["streaming"] else "one-slice-shared"
+    return "multi-two-tiles" if plan["tiles_per_group"] == 2 else "multi-one-tile"
+
+
+# every variant instantiated for a head dimension
+EXPECTED = {
+    64: {"row-parallel", "one-slice-streamed", "one-slice-shared", "multi-one-tile", "multi-two-tiles"},
+    128: {"row-parallel", "one-slice-streamed", "one-slice-shared", "multi-one-tile", "multi-two-tiles"},
+    256: {"row-parallel", "eight-waves", "one-slice-streamed", "one-slice-shared", "multi-one-tile",
+          "multi-two-tiles"},
+    512: {"eight-waves", "one-slice-streamed", "one-slice-shared", "multi-one-tile", "multi-two-tiles"},
+}
