@@ -193,7 +193,10 @@ def run_prefill(torch, fa, I):
         us = graph_time_us(torch, [mk(bf) for bf in bufs], reps=max(3, 200 // reps))
         t_roof_us = max(byts / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFS * 1e12)) * 1e6
         tfs = flops / (us * 1e-6) / 1e12
+        plan = fa.fmha_attention_plan(w.batch, w.n_h, w.n_kv_h, w.T, w.s_k, w.hd, window=w.window,
+                                      causal=w.causal)
         out.append({"workload": w.name, "us_per_call": round(us, 2), "tflops": round(tfs, 1),
+                    "plan": plan,
                     "frac_of_mfma_peak": round(tfs / MFMA_BF16_PEAK_TFS, 4),
                     "frac_of_roofline": round(t_roof_us / us, 4), "roofline_bound": "hbm",
                     "alg_gflop": round(flops / 1e9, 3), "alg_mib": round(byts / 2**20, 2),
@@ -250,11 +253,8 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
     fa.load_library()
-    if args.only_prefill:
-        run_prefill(torch, fa, I)
-        return
-    res = run_decode(args, torch, fa, I)
-    if args.calibrate_copy:
+
+    def calibrate_copy():
         src = torch.empty(2**30, dtype=torch.uint8, device="cuda")
         src.fill_(1)
         dst = torch.empty_like(src)
@@ -262,6 +262,15 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.only_prefill:
+        run_prefill(torch, fa, I)
+        if args.calibrate_copy:
+            calibrate_copy()
+        return
+    res = run_decode(args, torch, fa, I)
+    if args.calibrate_copy:
+        calibrate_copy()
     prefill = None if args.no_prefill else run_prefill(torch, fa, I)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(res, args.cpu_seconds)
     w = res["w"]
@@ -285,7 +294,8 @@ def main():
                    "step": "fmha_decode_splitkv + fmha_lse_merge",
                    "split_us": round(split_us, 2), "merge_us": round(res["merge_ms"] * 1e3, 2),
                    "merge_gbs": round(res["merge_gbs"], 1)},
-        "roofline": {"kernel": "attn_kernel<128, NK=4, NH=1, split, one-slice>", "bound": "hbm",
+        "roofline": {"kernel": "attn_kernel<128, 4, 4, 1, 1, true, true, true> (hd 128; 4 waves = 4 key groups x 1 "
+                               "head part; 1 tile; split; one slice; streamed)", "bound": "hbm",
                      "achieved": round(res["split_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(res["split_gbs"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(split_tag),
                      "alg_bytes_per_launch": res["split_bytes"], "launch_us": round(split_us, 2)},
