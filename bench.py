@@ -14,11 +14,13 @@ Also reported on the same line:
                 each launch on the launch stream, against 8 TB/s.
   cpu_baseline  the fp64 CPU oracle computing the same workload (split +
                 merge) on the host cores, as KV-read GB/s.
-  prefill       the largest causal MHA prefill point and the sliding-window
-                MQA prefill: fused-kernel TFLOP/s (algorithmic flops) against
-                the dense bf16 MFMA peak and against the bandwidth roofline,
-                timed from graph replays over input replicas rotated through
-                more than the Infinity Cache.
+  prefill       the largest causal MHA prefill point, the sliding-window
+                MQA prefill and a long causal GQA prefill (T = s_k = 4096):
+                fused-kernel TFLOP/s (algorithmic flops) against the dense
+                bf16 MFMA peak and against the roofline (bandwidth for the
+                first two, MFMA for the long one), timed from graph replays
+                over input replicas rotated through more than the Infinity
+                Cache.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -175,7 +177,7 @@ def graph_time_us(torch, calls, reps):
 
 def run_prefill(torch, fa, I):
     out = []
-    for w in (I.mha_causal_prefill(128, 512, 512), I.SWA_MQA_PREFILL):
+    for w in (I.mha_causal_prefill(128, 512, 512), I.SWA_MQA_PREFILL, I.LONG_PREFILL):
         flops, byts = prefill_work(w)
         foot = 2 * (w.batch * w.T * w.n_h * w.hd * 2) + 2 * (w.batch * w.s_k * w.n_kv_h * w.hd * 2)
         reps = max(1, min(64, math.ceil(512 * 2**20 / foot)))  # rotate >= 512 MiB
@@ -198,7 +200,9 @@ def run_prefill(torch, fa, I):
         out.append({"workload": w.name, "us_per_call": round(us, 2), "tflops": round(tfs, 1),
                     "plan": plan,
                     "frac_of_mfma_peak": round(tfs / MFMA_BF16_PEAK_TFS, 4),
-                    "frac_of_roofline": round(t_roof_us / us, 4), "roofline_bound": "hbm",
+                    "frac_of_roofline": round(t_roof_us / us, 4),
+                    "roofline_bound": "hbm" if byts / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFS * 1e12)
+                    else "mfma",
                     "alg_gflop": round(flops / 1e9, 3), "alg_mib": round(byts / 2**20, 2),
                     "rotated_replicas": reps})
         log(f"prefill {w.name}: {us:.2f} us, {tfs:.1f} TFLOP/s, {t_roof_us / us:.1%} of roofline")
@@ -236,7 +240,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only-prefill", action="store_true",
-                    help="time only the two prefill workloads (for profiler runs); prints no JSON line")
+                    help="time only the prefill workloads (for profiler runs); prints no JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, copy 1 GiB twice (reference for HBM byte counters)")
     args = ap.parse_args()

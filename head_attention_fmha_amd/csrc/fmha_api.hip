@@ -29,6 +29,11 @@ bool strides_ok(const fmha_strides &st) {
 
 bool hd_supported(int hd) { return hd == 64 || hd == 128 || hd == 256 || hd == 512; }
 
+// Size limits: keep every row, key and partition index inside int.
+constexpr int kMaxT = 1 << 20;
+constexpr int kMaxKeys = 1 << 30;
+constexpr int64_t kMaxRows = int64_t(1) << 30;  // stacked rows (group * T) per KV head
+
 // Sizes and mask arguments of an attention call.
 int validate_dims(int batch, int n_h, int n_kv_h, int T, int s_k, int hd, int window, int causal) {
     if (batch <= 0 || n_h <= 0 || n_kv_h <= 0 || T <= 0 || s_k <= 0 || hd <= 0) return FMHA_ERR_INVALID_ARG;
@@ -36,7 +41,8 @@ int validate_dims(int batch, int n_h, int n_kv_h, int T, int s_k, int hd, int wi
     if (causal != 0 && causal != 1) return FMHA_ERR_INVALID_ARG;
     if (window < 0) return FMHA_ERR_INVALID_ARG;
     if ((causal || window > 0) && T > s_k) return FMHA_ERR_INVALID_ARG;
-    if (!hd_supported(hd) || T > 128) return FMHA_ERR_UNSUPPORTED;
+    if (!hd_supported(hd) || T > kMaxT || s_k > kMaxKeys || (int64_t)(n_h / n_kv_h) * T > kMaxRows)
+        return FMHA_ERR_UNSUPPORTED;
     return FMHA_OK;
 }
 
@@ -84,11 +90,9 @@ constexpr int kComputeUnits = 256;
 // (64 or 128 columns per wave).
 int head_parts(int hd) { return hd <= 128 ? 1 : hd / 128; }
 
-// Row-parallel kernel: one 16-row tile per wave (64 rows per workgroup, so
-// the short-prefill grids still give every compute unit a workgroup) and
-// keys per LDS chunk.  Used up to hd 256: at 512 the full-width Q and output
-// tiles crowd one wave's registers and the per-wave kernel is faster.
-constexpr int rows_tiles_per_wave(int) { return 1; }
+// Row-parallel kernel: keys per LDS chunk.  Used up to hd 256: at 512 the
+// full-width Q and output tiles crowd one wave's registers and the per-wave
+// kernel is faster.
 constexpr int rows_chunk_keys(int hd) { return hd <= 128 ? 64 : 32; }
 
 // The kernel variant and grid for one call.  A workgroup serves MT 16-row
@@ -121,14 +125,20 @@ fmha_plan plan_attention(const FwdParams &p, int hd) {
         if (blocks2 >= 2 * kComputeUnits) pl.tiles_per_group = 2;
     }
     // many rows per KV head and several passes over the keys: the row-parallel
-    // kernel, whose four waves share every K/V chunk through LDS
+    // kernel, whose four waves share every K/V chunk through LDS.  One 16-row
+    // tile per wave while that is needed to give every compute unit a
+    // workgroup (short prefill); two -- every K operand read from LDS then
+    // feeds two MFMAs -- once the grid has two workgroups per compute unit
+    // even so (long prefill)
     if (!pl.one_slice && p.rows >= 64 && hd <= 256) {
-        const int rows_rp = 64 * rows_tiles_per_wave(hd);
-        const int64_t groups_rp = (int64_t)((p.rows + rows_rp - 1) / rows_rp) * p.n_split * p.n_kv_h * p.batch;
-        if (groups_rp >= kComputeUnits) {
+        const int64_t per_kv = (int64_t)p.n_split * p.n_kv_h * p.batch;
+        const int64_t groups1 = (int64_t)((p.rows + 63) / 64) * per_kv;
+        const int64_t groups2 = (int64_t)((p.rows + 127) / 128) * per_kv;
+        if (groups1 >= kComputeUnits) {
             pl.row_parallel = 1;
             pl.waves_per_group = 4;
-            pl.tiles_per_group = 4 * rows_tiles_per_wave(hd);
+            // (two tiles of 256 columns would spill: hd 256 keeps one)
+            pl.tiles_per_group = (hd <= 128 && groups2 >= 2 * kComputeUnits) ? 8 : 4;
         }
     }
     const int rows_per_group = 16 * pl.tiles_per_group;
@@ -150,9 +160,14 @@ void launch_kernel(const FwdParams &p, hipStream_t stream) {
 template <int HD, bool SPLIT>
 void launch_hd(const FwdParams &p, const fmha_plan &pl, hipStream_t s) {
     if (pl.row_parallel) {
-        if constexpr (HD <= 256)
-            hipLaunchKernelGGL((fmha::rows_kernel<HD, rows_tiles_per_wave(HD), rows_chunk_keys(HD), SPLIT>),
-                               dim3(p.n_units), dim3(256), 0, s, p);
+        if constexpr (HD <= 256) {
+            if (HD <= 128 && pl.tiles_per_group == 8)
+                hipLaunchKernelGGL((fmha::rows_kernel<HD, HD <= 128 ? 2 : 1, rows_chunk_keys(HD), SPLIT>),
+                                   dim3(p.n_units), dim3(256), 0, s, p);
+            else
+                hipLaunchKernelGGL((fmha::rows_kernel<HD, 1, rows_chunk_keys(HD), SPLIT>), dim3(p.n_units), dim3(256),
+                                   0, s, p);
+        }
     } else if (pl.waves_per_group == 8) {
         // chosen only for several slices per wave (never one-slice), hd >= 256
         if constexpr (HD >= 256) launch_kernel<HD, 8, 1, SPLIT, false, false>(p, s);
@@ -275,7 +290,8 @@ const char *fmha_status_string(int status) {
         case FMHA_OK: return "FMHA_OK: success";
         case FMHA_ERR_INVALID_ARG: return "FMHA_ERR_INVALID_ARG: null pointer, non-positive size, n_h not a "
                                           "multiple of n_kv_h, bad mask arguments or split_len";
-        case FMHA_ERR_UNSUPPORTED: return "FMHA_ERR_UNSUPPORTED: head dim must be 64, 128, 256 or 512 and T at most 128";
+        case FMHA_ERR_UNSUPPORTED: return "FMHA_ERR_UNSUPPORTED: head dim must be 64, 128, 256 or 512, T at most 2^20, "
+                                          "s_k at most 2^30 and (n_h / n_kv_h) * T at most 2^30";
         case FMHA_ERR_ALIGNMENT: return "FMHA_ERR_ALIGNMENT: pointers must be 16-byte aligned and strides multiples of 8 elements";
         case FMHA_ERR_LAUNCH: return "FMHA_ERR_LAUNCH: the HIP kernel launch failed";
         default: return "unknown fmha status";

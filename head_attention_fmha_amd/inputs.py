@@ -118,3 +118,17 @@ SWA_MQA_PREFILL = Workload("swa_mqa_prefill_b2_h16_T128_sk4096_hd512_w128", 2, 1
 
 ALL_WORKLOADS: List[Workload] = ([SINGLE_HEAD_DECODE] + MQA_DECODE_GRID + [GQA_SPLITKV_DECODE]
                                  + MHA_PREFILL_GRID + [SWA_MQA_PREFILL])
+
+# ---------------------------------------------------------------------------
+# Beyond the five: long prefill (T up to s_k, full causal), where the
+# arithmetic intensity passes the MFMA ridge.
+# ---------------------------------------------------------------------------
+
+
+def gqa_causal_prefill_long(T: int, hd: int, batch: int = 2, n_h: int = 32, n_kv_h: int = 8) -> Workload:
+    """GQA (group 4), a whole causal prompt: T = s_k."""
+    return Workload(f"gqa_causal_prefill_long_b{batch}_h{n_h}_kv{n_kv_h}_T{T}_sk{T}_hd{hd}", batch, n_h, n_kv_h,
+                    T, T, hd, causal=True)
+
+
+LONG_PREFILL = gqa_causal_prefill_long(4096, 128)

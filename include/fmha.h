@@ -53,9 +53,11 @@
  *   - Alignment: every pointer must be 16-byte aligned and every batch,
  *     token and head stride a multiple of 8 elements (0 is allowed for a
  *     K/V head stride): the kernels move 16-byte vectors.
- *   - Supported sizes: hd in {64, 128, 256, 512}; 1 <= T <= 128;
- *     s_k >= 1; n_h a multiple of n_kv_h.  With causal or window set, T
- *     must not exceed s_k.
+ *   - Supported sizes: hd in {64, 128, 256, 512}; 1 <= T <= 2^20;
+ *     1 <= s_k <= 2^30; n_h a multiple of n_kv_h with (n_h / n_kv_h) * T
+ *     <= 2^30.  With causal or window set, T must not exceed s_k.  Decode
+ *     (T = 1), short prefill and long prefill (T up to s_k, the prefill the
+ *     "Next steps" of CURRENT_ISSUE.md call for) share the entry points.
  */
 #ifndef FMHA_H
 #define FMHA_H
@@ -77,7 +79,7 @@ typedef enum {
     FMHA_OK = 0,
     FMHA_ERR_INVALID_ARG = 1, /* null pointer, size <= 0, n_h % n_kv_h != 0, bad mask
                                  arguments, T > s_k with a mask, split_len <= 0 */
-    FMHA_ERR_UNSUPPORTED = 2, /* hd not in {64,128,256,512}, or T > 128 */
+    FMHA_ERR_UNSUPPORTED = 2, /* hd not in {64,128,256,512}, or a size over its limit */
     FMHA_ERR_ALIGNMENT = 3,   /* pointer not 16-byte aligned or stride not a multiple of 8 */
     FMHA_ERR_LAUNCH = 4       /* the HIP launch failed */
 } fmha_status;
@@ -113,7 +115,8 @@ int fmha_forward(const void *q, const void *k, const void *v, void *o, float *ls
  * p = 0 .. n_split-1 with n_split = ceil(s_k / split_len).  For each
  * (b, h, i, p) it writes the attention restricted to that range, NORMALISED
  * within the partition, and its lse; a partition with no visible key gets
- * O_p = 0 and lse_p = -inf.  Any T in 1..128 is accepted (decode is T = 1).
+ * O_p = 0 and lse_p = -inf.  Any T within the size limits is accepted
+ * (decode is T = 1).
  *
  *   o_part   [batch][n_h][T][n_split][hd] fp32, dense (written)
  *   lse_part [batch][n_h][T][n_split]     fp32, dense (written)

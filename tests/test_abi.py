@@ -82,7 +82,8 @@ def merge(lib, o_part=QP, lse_part=KP, o=OP, b=2, n_h=8, T=1, hd=128, n_split=4,
     (dict(s_k=0), INVALID), (dict(hd=0), INVALID), (dict(n_h=8, n_kv_h=3), INVALID),
     (dict(causal=2), INVALID), (dict(window=-1), INVALID), (dict(T=65, s_k=64), INVALID),
     (dict(T=65, s_k=64, causal=0, window=4), INVALID),
-    (dict(hd=96), UNSUPPORTED), (dict(hd=1024), UNSUPPORTED), (dict(T=129, s_k=256), UNSUPPORTED),
+    (dict(hd=96), UNSUPPORTED), (dict(hd=1024), UNSUPPORTED), (dict(T=(1 << 20) + 1, s_k=(1 << 20) + 1), UNSUPPORTED),
+    (dict(s_k=(1 << 30) + 1), UNSUPPORTED), (dict(n_h=2048, n_kv_h=1, T=1 << 20, s_k=1 << 20), UNSUPPORTED),
     (dict(q=ctypes.c_void_p(0x10008)), ALIGN), (dict(o=ctypes.c_void_p(0x50004)), ALIGN),
     (dict(lse=ctypes.c_void_p(0x50002)), ALIGN),
     (dict(q_st=FmhaStrides(4 * 8 * 128, 8 * 128 + 4, 128)), ALIGN),
@@ -141,7 +142,7 @@ def test_plan_of_each_workload(lib, args, kw, want):
 
 @pytest.mark.parametrize("args,kw,code", [
     ((1, 1, 1, 1, 128, 96), {}, UNSUPPORTED),
-    ((1, 1, 1, 129, 256, 64), {}, UNSUPPORTED),
+    ((1, 1, 1, (1 << 20) + 1, (1 << 20) + 1, 64), {}, UNSUPPORTED),
     ((1, 3, 2, 1, 128, 64), {}, INVALID),
     ((1, 1, 1, 4, 2, 64), dict(causal=True), INVALID),
     ((1, 1, 1, 1, 128, 64), dict(split_len=-1), INVALID),

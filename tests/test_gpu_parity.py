@@ -304,6 +304,43 @@ def test_every_kernel_variant(name, dims, split_len, causal, window, hd):
 
 
 # ---------------------------------------------------------------------------
+# Long prefill: T in the thousands, up to T = s_k
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+@pytest.mark.parametrize("dims,causal,window", [((1, 4, 2, 1024, 1024), True, 0),
+                                                ((1, 4, 1, 700, 900), False, 0),
+                                                ((2, 2, 2, 1000, 1000), True, 300)],
+                         ids=["gqa-causal-T1024", "mqa-nomask-T700", "mha-window300-T1000"])
+def test_long_prefill_full_compare(dims, causal, window, hd):
+    b, n_h, n_kv_h, T, s_k = dims
+    seed = 900 + hd + T
+    q = I.randn_bf16((b, T, n_h, hd), seed)
+    k = I.randn_bf16((b, s_k, n_kv_h, hd), seed + 1)
+    v = I.randn_bf16((b, s_k, n_kv_h, hd), seed + 2)
+    scale = 1.0 / math.sqrt(hd)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=causal, window=window)
+    o, lse = gpu_forward(q, k, v, scale, causal, window)
+    check_attention(o, lse, o_ref, lse_ref, what=f"long prefill {dims}")
+
+
+def test_long_prefill_full_size_sampled_rows():
+    """The timed long-prefill workload at full size; the oracle recomputes
+    sampled rows one by one (a causal row at position p is the T = 1 problem
+    over keys 0..p)."""
+    w = I.LONG_PREFILL
+    q, k, v = I.make_qkv(w, device="cuda")
+    o, lse = gpu_forward(q, k, v, w.scale, True)
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    oh, lh = o.cpu(), lse.cpu()
+    for t in (0, 1, 63, 64, 127, 128, 1000, 2047, 2048, 3333, w.T - 2, w.T - 1):
+        pos = w.s_k - w.T + t
+        o_ref, lse_ref = oracle.attention(qh[:, t:t + 1].contiguous(), kh[:, :pos + 1].contiguous(),
+                                          vh[:, :pos + 1].contiguous(), w.scale, causal=True)
+        check_attention(oh[:, t:t + 1], lh[:, :, t:t + 1], o_ref, lse_ref, what=f"{w.name} row {t}")
+
+
+# ---------------------------------------------------------------------------
 # Split-KV and the merge kernel
 # ---------------------------------------------------------------------------
 

@@ -14,6 +14,7 @@ SHAPES = [
     ("multi-two-tiles", (32, 16, 8, 20, 300), 0, True, 0),
     ("row-parallel-gqa", (4, 64, 32, 100, 300), 0, True, 0),
     ("row-parallel-window", (4, 64, 64, 100, 300), 0, True, 70),
+    ("row-parallel-two-tiles", (4, 128, 128, 100, 200), 0, True, 0),
 ]
 
 HEAD_DIMS = (64, 128, 256, 512)
@@ -22,7 +23,7 @@ HEAD_DIMS = (64, 128, 256, 512)
 def branch(plan: dict) -> str:
     """The kernel variant a plan launches."""
     if plan["row_parallel"]:
-        return "row-parallel"
+        return "row-parallel-two-tiles" if plan["tiles_per_group"] == 8 else "row-parallel"
     if plan["waves_per_group"] == 8:
         return "eight-waves"
     if plan["one_slice"]:
@@ -32,8 +33,10 @@ def branch(plan: dict) -> str:
 
 # every variant instantiated for a head dimension
 EXPECTED = {
-    64: {"row-parallel", "one-slice-streamed", "one-slice-shared", "multi-one-tile", "multi-two-tiles"},
-    128: {"row-parallel", "one-slice-streamed", "one-slice-shared", "multi-one-tile", "multi-two-tiles"},
+    64: {"row-parallel", "row-parallel-two-tiles", "one-slice-streamed", "one-slice-shared", "multi-one-tile",
+         "multi-two-tiles"},
+    128: {"row-parallel", "row-parallel-two-tiles", "one-slice-streamed", "one-slice-shared", "multi-one-tile",
+          "multi-two-tiles"},
     256: {"row-parallel", "eight-waves", "one-slice-streamed", "one-slice-shared", "multi-one-tile",
           "multi-two-tiles"},
     512: {"eight-waves", "one-slice-streamed", "one-slice-shared", "multi-one-tile", "multi-two-tiles"},
