@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
 
     // ---- this wave's tiles: rows, masks, and the key range of each tile ----
     bool row_ok[RT];
-    int t_of[RT], h_of[RT], r_lo[RT], r_hi[RT], tile_lo[RT], tile_hi[RT];
+    int t_of[RT], h_of[RT], r_lo[RT], r_hi[RT], tile_lo[RT], tile_hi[RT], full_lo[RT], full_hi[RT];
 #pragma unroll
     for (int mt = 0; mt < RT; ++mt) {
         const int first = row0 + 16 * (wave * RT + mt);
@@ -101,11 +101,17 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
         if (first > row_last) {
             tile_lo[mt] = khi;
             tile_hi[mt] = klo;  // empty tile
+            full_lo[mt] = khi;
+            full_hi[mt] = klo;
         } else {
             const int pos_first = p.s_k - p.T + first / p.group;
             const int pos_last = p.s_k - p.T + last / p.group;
             tile_hi[mt] = p.causal ? min(khi, pos_last + 1) : khi;
             tile_lo[mt] = p.window > 0 ? max(klo, pos_first - p.window + 1) : klo;
+            // keys visible to EVERY row of the tile: chunks inside need no mask
+            // (rows past the end of the block hold Q = 0 and are never stored)
+            full_hi[mt] = p.causal ? min(khi, pos_first + 1) : khi;
+            full_lo[mt] = p.window > 0 ? max(klo, pos_last - p.window + 1) : klo;
         }
     }
 
@@ -120,15 +126,21 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
     }
 
     f32x4 acc[RT][NB];
-    float m[RT], l[RT], lq[RT];
+    f32x4 accq[RT];  // every element: the running sum of row lr's bf16 weights (-> O)
+    float m[RT], l[RT];
 #pragma unroll
     for (int mt = 0; mt < RT; ++mt) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mt][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m[mt] = -INFINITY;
-        l[mt] = 0.f;
-        lq[mt] = 0.f;
+        accq[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[mt] = -INFINITY;  // running max (base 2), equal in the 4 lanes of a row
+        l[mt] = 0.f;        // this lane's share of the fp32 sum of weights (-> lse)
     }
+    // A operand of ones: one MFMA per 32-key slice sums the bf16 weights the PV
+    // product consumes, already complete in every lane of the row
+    bf16x8 ones;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ones[j] = (__bf16)1.0f;
 
     const uint16_t *kbase = p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
     const uint16_t *vbase = p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh;
@@ -177,40 +189,54 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
                     sc[kb] = mfma_16x16x32(kf, qf[mt][s], sc[kb]);
                 }
             }
-            // ---- mask + online softmax over the chunk's keys
+            // ---- mask (only chunks that cut through some row's range) + online
+            // softmax over the chunk's keys
             float x[KB][4];
             float mx = -INFINITY;
+            if (k0 >= full_lo[mt] && k0 + KC <= full_hi[mt]) {  // wave-uniform
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int key = k0 + 16 * kb + 4 * lg + j;
-                    x[kb][j] = (key >= r_lo[mt] && key < r_hi[mt]) ? sc[kb][j] * p.scale_log2 : -INFINITY;
-                    mx = fmaxf(mx, x[kb][j]);
-                }
+                    for (int j = 0; j < 4; ++j) {
+                        x[kb][j] = sc[kb][j] * p.scale_log2;
+                        mx = fmaxf(mx, x[kb][j]);
+                    }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int key = k0 + 16 * kb + 4 * lg + j;
+                        x[kb][j] = (key >= r_lo[mt] && key < r_hi[mt]) ? sc[kb][j] * p.scale_log2 : -INFINITY;
+                        mx = fmaxf(mx, x[kb][j]);
+                    }
+            }
             mx = fmaxf(mx, xor_shuffle(mx, 16));
             mx = fmaxf(mx, xor_shuffle(mx, 32));
             const float m_new = fmaxf(m[mt], mx);
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
             const float alpha = fast_exp2(m[mt] - m_use);
             bf16x8 pt[KS];
-            float psum = 0.f, qsum = 0.f;
+            float psum = 0.f;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const float pj = fast_exp2(x[kb][j] - m_use);
-                    const __bf16 pb = to_bf16(pj);
-                    pt[kb >> 1][(kb & 1) * 4 + j] = pb;
+                    pt[kb >> 1][(kb & 1) * 4 + j] = to_bf16(pj);
                     psum += pj;
-                    qsum += (float)pb;
                 }
-            l[mt] = l[mt] * alpha + psum;
-            lq[mt] = lq[mt] * alpha + qsum;
             m[mt] = m_new;
-            // ---- O^T = alpha O^T + V^T . P^T
+            // ---- O^T = alpha O^T + V^T . P^T; the rescale is skipped when no
+            // row of the wave raised its maximum (alpha = 1 exactly)
+            l[mt] = l[mt] * alpha + psum;
+            if (__any(alpha != 1.f)) {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[mt][nb] = acc[mt][nb] * alpha;
+                for (int nb = 0; nb < NB; ++nb) acc[mt][nb] = acc[mt][nb] * alpha;
+                accq[mt] = accq[mt] * alpha;
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) accq[mt] = mfma_16x16x32(ones, pt[ks], accq[mt]);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
@@ -265,11 +291,10 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
     for (int mt = 0; mt < RT; ++mt) {
         l[mt] += xor_shuffle(l[mt], 16);
         l[mt] += xor_shuffle(l[mt], 32);
-        lq[mt] += xor_shuffle(lq[mt], 16);
-        lq[mt] += xor_shuffle(lq[mt], 32);
         if (!row_ok[mt]) continue;
         const int t = t_of[mt], h = h_of[mt];
-        const float inv = lq[mt] > 0.f ? 1.f / lq[mt] : 0.f;
+        const float lq = accq[mt][0];
+        const float inv = lq > 0.f ? 1.f / lq : 0.f;
         const float lse_val = l[mt] > 0.f ? (m[mt] + __log2f(l[mt])) * kLn2 : -INFINITY;
         if constexpr (SPLIT) {
             const int64_t r = (((int64_t)b * p.n_h + h) * p.T + t) * p.n_split + part;
