@@ -27,6 +27,10 @@
 
 namespace fmha {
 
+// The running maximum moves only when a score exceeds it by more than this
+// (base-2 units): weights stay below 2^8, far inside bf16 and fp32 range.
+constexpr float kRescaleLog2 = 8.f;
+
 template <int HD, int RT, int KC>
 struct RowsShape {
     static constexpr int KSTEPS = HD / 32;         // QK MFMA steps
@@ -115,14 +119,23 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
         }
     }
 
+    // Scores enter the softmax as s * c with c = |scale| log2 e >= 0: a
+    // negative scale flips the sign of Q instead (exact in bf16), so the
+    // running maximum can be kept on raw scores and the scaling folded into
+    // the exponent's fma.
+    const float c_scale = fabsf(p.scale_log2);
+    const unsigned q_flip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
     bf16x8 qf[RT][KSTEPS];  // Q^T B operand: Q[row lr][32*s + 8*lg + 0..7]
 #pragma unroll
     for (int mt = 0; mt < RT; ++mt) {
         const uint16_t *qp =
             p.q + (int64_t)b * p.q_sb + (int64_t)t_of[mt] * p.q_st + (int64_t)h_of[mt] * p.q_sh + 8 * lg;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-            qf[mt][s] = row_ok[mt] ? *reinterpret_cast<const bf16x8 *>(qp + 32 * s) : bf16x8{};
+        for (int s = 0; s < KSTEPS; ++s) {
+            u32x4 raw = row_ok[mt] ? *reinterpret_cast<const u32x4 *>(qp + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+            raw ^= q_flip;
+            qf[mt][s] = __builtin_bit_cast(bf16x8, raw);
+        }
     }
 
     f32x4 acc[RT][NB];
@@ -148,18 +161,39 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
 
     // ---- one chunk HBM -> LDS stage: wave w fills bytes [w*LOADS*1 KiB, ...)
     // of each part; the lane writing LDS byte x of a part fetches the global
-    // chunk that belongs at x under the rotation (keys past khi read key khi-1)
+    // chunk that belongs at x under the rotation.  The lane's row and chunk
+    // are fixed, so its byte offset from the chunk's first key is computed
+    // once; a chunk then costs one scalar base per tensor.  The last chunk
+    // of a range clamps keys past khi to key khi-1 instead.
+    int ld_row[LOADS], ld_col[LOADS];
+    unsigned ld_koff[LOADS], ld_voff[LOADS];
+    const bool offsets32 = (int64_t)(KC - 1) * (p.k_st > p.v_st ? p.k_st : p.v_st) * 2 + ROW_BYTES < (1ll << 31);
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+        const int x = ((wave * LOADS + it) * 64 + lane) * 16;  // LDS byte of this lane
+        ld_row[it] = x / ROW_BYTES;
+        ld_col[it] = ((x % ROW_BYTES) / 16 - rot_of(ld_row[it]) + CHUNKS) % CHUNKS;
+        ld_koff[it] = (unsigned)(((int64_t)ld_row[it] * p.k_st + ld_col[it] * 8) * 2);
+        ld_voff[it] = (unsigned)(((int64_t)ld_row[it] * p.v_st + ld_col[it] * 8) * 2);
+    }
     auto issue_chunk = [&](int k0, unsigned char *stage) __attribute__((always_inline)) {
         unsigned char *sK = stage;
         unsigned char *sV = stage + PART_BYTES;
+        if (offsets32 && k0 + KC <= khi) {  // wave-uniform
+            const char *kc = reinterpret_cast<const char *>(kbase + (int64_t)k0 * p.k_st);
+            const char *vc = reinterpret_cast<const char *>(vbase + (int64_t)k0 * p.v_st);
 #pragma unroll
-        for (int it = 0; it < LOADS; ++it) {
-            const int x = ((wave * LOADS + it) * 64 + lane) * 16;  // LDS byte of this lane
-            const int r = x / ROW_BYTES;
-            const int c = ((x % ROW_BYTES) / 16 - rot_of(r) + CHUNKS) % CHUNKS;
-            const int key = min(k0 + r, khi - 1);
-            load_lds_16(kbase + (int64_t)key * p.k_st + c * 8, sK + (wave * LOADS + it) * 1024);
-            load_lds_16(vbase + (int64_t)key * p.v_st + c * 8, sV + (wave * LOADS + it) * 1024);
+            for (int it = 0; it < LOADS; ++it) {
+                load_lds_16(kc + ld_koff[it], sK + (wave * LOADS + it) * 1024);
+                load_lds_16(vc + ld_voff[it], sV + (wave * LOADS + it) * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < LOADS; ++it) {
+                const int key = min(k0 + ld_row[it], khi - 1);
+                load_lds_16(kbase + (int64_t)key * p.k_st + ld_col[it] * 8, sK + (wave * LOADS + it) * 1024);
+                load_lds_16(vbase + (int64_t)key * p.v_st + ld_col[it] * 8, sV + (wave * LOADS + it) * 1024);
+            }
         }
     };
 
@@ -168,91 +202,110 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
     const int tr_row0 = 4 * lg + (lr >> 2);
     const int tr_col = 4 * (lr & 3);
 
-    // ---- the products of one staged chunk for every tile of this wave
+    // ---- the products of one staged chunk for every tile of this wave.  Each
+    // K operand and each V^T operand read from LDS feeds the MFMAs of all
+    // tiles that see the chunk.
     auto compute_chunk = [&](int k0, const unsigned char *sK) __attribute__((always_inline)) {
         const unsigned char *sV = sK + PART_BYTES;
+        bool live[RT];  // wave-uniform: does any row of the tile see a key of the chunk?
+        bool any_live = false;
 #pragma unroll
         for (int mt = 0; mt < RT; ++mt) {
-            // wave-uniform: does any row of this tile see a key of the chunk?
-            if (k0 >= tile_hi[mt] || k0 + KC <= tile_lo[mt]) continue;
-            // ---- S^T for the chunk: KB blocks of 16 keys
-            f32x4 sc[KB];
+            live[mt] = k0 < tile_hi[mt] && k0 + KC > tile_lo[mt];
+            any_live = any_live || live[mt];
+        }
+        if (!any_live) return;
+        // ---- S^T for the chunk: KB blocks of 16 keys
+        f32x4 sc[RT][KB];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const int r = 16 * kb + lr;
-                const unsigned char *krow = sK + r * ROW_BYTES;
+        for (int kb = 0; kb < KB; ++kb) {
+            const int r = 16 * kb + lr;
+            const unsigned char *krow = sK + r * ROW_BYTES;
 #pragma unroll
-                for (int s = 0; s < KSTEPS; ++s) {
-                    const int slot = (4 * s + lg + rot_of(r)) % CHUNKS;
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(krow + slot * 16);
-                    sc[kb] = mfma_16x16x32(kf, qf[mt][s], sc[kb]);
-                }
+            for (int mt = 0; mt < RT; ++mt) sc[mt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+                const int slot = (4 * s + lg + rot_of(r)) % CHUNKS;
+                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(krow + slot * 16);
+#pragma unroll
+                for (int mt = 0; mt < RT; ++mt)
+                    if (live[mt]) sc[mt][kb] = mfma_16x16x32(kf, qf[mt][s], sc[mt][kb]);
             }
-            // ---- mask (only chunks that cut through some row's range) + online
-            // softmax over the chunk's keys
-            float x[KB][4];
-            float mx = -INFINITY;
-            if (k0 >= full_lo[mt] && k0 + KC <= full_hi[mt]) {  // wave-uniform
+        }
+        // ---- online softmax over the chunk's keys, per tile.  The maximum is
+        // taken on raw scores (masked keys excluded only in chunks that cut
+        // through some row's range); the reference point m moves -- rescaling
+        // the accumulators -- only when some row of the wave exceeds it by
+        // more than 2^8, so weights stay below 256 and most chunks rescale
+        // nothing
+        bf16x8 pt[RT][KS];
+#pragma unroll
+        for (int mt = 0; mt < RT; ++mt) {
+            if (!live[mt]) continue;
+            const bool full = k0 >= full_lo[mt] && k0 + KC <= full_hi[mt];  // wave-uniform
+            bool vis[KB][4];
+            float mr = -INFINITY;
+            if (full) {
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        x[kb][j] = sc[kb][j] * p.scale_log2;
-                        mx = fmaxf(mx, x[kb][j]);
-                    }
+                    for (int j = 0; j < 4; ++j) mr = fmaxf(mr, sc[mt][kb][j]);
             } else {
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int key = k0 + 16 * kb + 4 * lg + j;
-                        x[kb][j] = (key >= r_lo[mt] && key < r_hi[mt]) ? sc[kb][j] * p.scale_log2 : -INFINITY;
-                        mx = fmaxf(mx, x[kb][j]);
+                        vis[kb][j] = key >= r_lo[mt] && key < r_hi[mt];
+                        mr = fmaxf(mr, vis[kb][j] ? sc[mt][kb][j] : -INFINITY);
                     }
             }
-            mx = fmaxf(mx, xor_shuffle(mx, 16));
-            mx = fmaxf(mx, xor_shuffle(mx, 32));
-            const float m_new = fmaxf(m[mt], mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m[mt] - m_use);
-            bf16x8 pt[KS];
+            mr = fmaxf(mr, xor_shuffle(mr, 16));
+            mr = fmaxf(mr, xor_shuffle(mr, 32));
+            const float mx = mr * c_scale;  // NaN (ignored by fmaxf) for a fully masked row when c = 0
+            if (__any(mx > m[mt] + kRescaleLog2)) {
+                const float m_new = fmaxf(m[mt], mx);
+                const float alpha = fast_exp2(m[mt] - ((m_new == -INFINITY) ? 0.f : m_new));
+                l[mt] *= alpha;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) acc[mt][nb] = acc[mt][nb] * alpha;
+                accq[mt] = accq[mt] * alpha;
+                m[mt] = m_new;
+            }
+            const float neg_m = (m[mt] == -INFINITY) ? 0.f : -m[mt];
             float psum = 0.f;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float pj = fast_exp2(x[kb][j] - m_use);
-                    pt[kb >> 1][(kb & 1) * 4 + j] = to_bf16(pj);
+                    float xj = fmaf(sc[mt][kb][j], c_scale, neg_m);
+                    if (!full) xj = vis[kb][j] ? xj : -INFINITY;
+                    const float pj = fast_exp2(xj);
+                    pt[mt][kb >> 1][(kb & 1) * 4 + j] = to_bf16(pj);
                     psum += pj;
                 }
-            m[mt] = m_new;
-            // ---- O^T = alpha O^T + V^T . P^T; the rescale is skipped when no
-            // row of the wave raised its maximum (alpha = 1 exactly)
-            l[mt] = l[mt] * alpha + psum;
-            if (__any(alpha != 1.f)) {
+            l[mt] += psum;
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) acc[mt][nb] = acc[mt][nb] * alpha;
-                accq[mt] = accq[mt] * alpha;
-            }
+            for (int ks = 0; ks < KS; ++ks) accq[mt] = mfma_16x16x32(ones, pt[mt][ks], accq[mt]);
+        }
+        // ---- O^T += V^T . P^T
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) accq[mt] = mfma_16x16x32(ones, pt[ks], accq[mt]);
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+            for (int nb = 0; nb < NB; ++nb) {
+                bf16x4 q2[2];
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    bf16x4 q2[2];
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        const int r = 32 * ks + 16 * half + tr_row0;
-                        const int c = 16 * nb + tr_col;
-                        const int off = r * ROW_BYTES + (((c >> 3) + rot_of(r)) % CHUNKS) * 16 + (c & 7) * 2;
-                        q2[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                            (__attribute__((address_space(3))) bf16x4 *)(sV + off));
-                    }
-                    const bf16x8 vt = __builtin_shufflevector(q2[0], q2[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                    acc[mt][nb] = mfma_16x16x32(vt, pt[ks], acc[mt][nb]);
+                for (int half = 0; half < 2; ++half) {
+                    const int r = 32 * ks + 16 * half + tr_row0;
+                    const int c = 16 * nb + tr_col;
+                    const int off = r * ROW_BYTES + (((c >> 3) + rot_of(r)) % CHUNKS) * 16 + (c & 7) * 2;
+                    q2[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (__attribute__((address_space(3))) bf16x4 *)(sV + off));
                 }
+                const bf16x8 vt = __builtin_shufflevector(q2[0], q2[1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                for (int mt = 0; mt < RT; ++mt)
+                    if (live[mt]) acc[mt][nb] = mfma_16x16x32(vt, pt[mt][ks], acc[mt][nb]);
             }
         }
     };
