@@ -11,6 +11,8 @@ Entry points carry the C names:
   fmha_forward(q, k, v, o, lse=None, *, scale=None, window=0, causal=False)
   fmha_decode_splitkv(q, k, v, o_part, lse_part, *, split_len, scale=None, window=0, causal=False)
   fmha_lse_merge(o_part, lse_part, o, lse=None)
+  fmha_forward_varlen(q, k, v, seqlens_k, o, lse=None, *, scale=None, window=0, causal=False)
+  fmha_decode_splitkv_segment(q, k, v, o_part, lse_part, *, split_len, part_offset, seqlens_k=None, ...)
   fmha_status_string(status)
   fmha_attention_plan(batch, n_h, n_kv_h, T, s_k, hd, *, window=0, causal=False, split_len=0, mqa_stride0=False)
 Layouts: q, o [batch, T, n_h, hd]; k, v [batch, s_k, n_kv_h, hd] (a head
@@ -26,7 +28,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["FmhaError", "fmha_forward", "fmha_decode_splitkv", "fmha_lse_merge", "fmha_status_string",
+__all__ = ["FmhaError", "fmha_forward", "fmha_forward_varlen", "fmha_decode_splitkv", "fmha_decode_splitkv_segment",
+           "fmha_lse_merge", "fmha_status_string",
            "fmha_attention_plan", "n_split_for", "library_path", "load_library", "FmhaStrides", "FmhaPlan"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +70,11 @@ def load_library():
     lib.fmha_forward.restype = I
     lib.fmha_decode_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, S, S, S, F, I, I, I, P]
     lib.fmha_decode_splitkv.restype = I
+    lib.fmha_forward_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, S, S, S, S, F, I, I, P]
+    lib.fmha_forward_varlen.restype = I
+    lib.fmha_decode_splitkv_segment.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, S, S, S, F, I, I, I, I, I,
+                                                P]
+    lib.fmha_decode_splitkv_segment.restype = I
     lib.fmha_lse_merge.argtypes = [P, P, P, P, I, I, I, I, I, S, P]
     lib.fmha_lse_merge.restype = I
     lib.fmha_attention_plan.argtypes = [I, I, I, I, I, I, S, S, I, I, I, ctypes.POINTER(FmhaPlan)]
@@ -160,6 +168,57 @@ def fmha_decode_splitkv(q, k, v, o_part, lse_part, *, split_len, scale=None, win
         _ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), b, n_h, n_kv_h, T, s_k, hd,
         _st(q), _st(k), _st(v), _scale(scale, hd), int(window), int(bool(causal)), int(split_len),
         _stream(stream)))
+
+
+def _seqlens(t, b):
+    if t is None:
+        return None
+    if (not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.device.type != "cuda"
+            or not t.is_contiguous() or tuple(t.shape) != (b,)):
+        raise ValueError(f"seqlens_k must be a contiguous int32 device tensor of shape ({b},)")
+    return t
+
+
+def fmha_forward_varlen(q, k, v, seqlens_k, o, lse=None, *, scale=None, window=0, causal=False,
+                        stream=None) -> None:
+    """fmha_forward over a ragged batch: row b holds seqlens_k[b] keys of the
+    s_k_max = k.shape[1] allocated; see include/fmha.h."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _dev4(t, n)
+    b, T, n_h, hd = q.shape
+    _, s_k, n_kv_h, _ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape) or k.shape[0] != b or k.shape[3] != hd:
+        raise ValueError("shape mismatch between q, k, v, o")
+    if seqlens_k is None:
+        raise ValueError("seqlens_k is required")
+    _seqlens(seqlens_k, b)
+    _dense(lse, (b, n_h, T), "lse")
+    _check(load_library().fmha_forward_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens_k), _ptr(o), _ptr(lse), b, n_h, n_kv_h, T, s_k, hd,
+        _st(q), _st(k), _st(v), _st(o), _scale(scale, hd), int(window), int(bool(causal)), _stream(stream)))
+
+
+def fmha_decode_splitkv_segment(q, k, v, o_part, lse_part, *, split_len, part_offset, seqlens_k=None, scale=None,
+                                window=0, causal=False, stream=None) -> None:
+    """Partitions of one key segment into slots [part_offset, ...) of o_part /
+    lse_part ([batch, n_h, T, n_split_total, hd] / [..., n_split_total]);
+    see include/fmha.h."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev4(t, n)
+    b, T, n_h, hd = q.shape
+    _, s_k, n_kv_h, _ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != b or k.shape[3] != hd:
+        raise ValueError("shape mismatch between q, k, v")
+    if o_part.dim() != 5:
+        raise ValueError("o_part must be [batch, n_h, T, n_split_total, hd]")
+    ns_total = o_part.shape[3]
+    _dense(o_part, (b, n_h, T, ns_total, hd), "o_part")
+    _dense(lse_part, (b, n_h, T, ns_total), "lse_part")
+    _seqlens(seqlens_k, b)
+    _check(load_library().fmha_decode_splitkv_segment(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens_k), _ptr(o_part), _ptr(lse_part), b, n_h, n_kv_h, T, s_k, hd,
+        _st(q), _st(k), _st(v), _scale(scale, hd), int(window), int(bool(causal)), int(split_len),
+        int(part_offset), int(ns_total), _stream(stream)))
 
 
 def fmha_lse_merge(o_part, lse_part, o, lse=None, *, stream=None) -> None:

@@ -125,14 +125,17 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
     bid /= p.n_split;
     const int kvh = bid % p.n_kv_h;
     const int b = bid / p.n_kv_h;
+    // keys of this batch row: s_k, or the row's own length in a ragged batch
+    // (clamped to the cache capacity s_k)
+    const int s_k = p.seqlens ? min(max(p.seqlens[b], 0), p.s_k) : p.s_k;
 
     const int row0 = rb * 16 * MT;
     const int row_last = min(row0 + 16 * MT, p.rows) - 1;
-    const int pos_lo = p.s_k - p.T + row0 / p.group;
-    const int pos_hi = p.s_k - p.T + row_last / p.group;
+    const int pos_lo = s_k - p.T + row0 / p.group;
+    const int pos_hi = s_k - p.T + row_last / p.group;
     // key range: the partition, cut to the union of the block rows' masks
     int klo = part * p.split_len;
-    int khi = min(klo + p.split_len, p.s_k);
+    int khi = min(klo + p.split_len, s_k);
     if (p.causal) khi = min(khi, pos_hi + 1);
     if (p.window > 0) klo = max(klo, pos_lo - p.window + 1);
 
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
         row_ok[mt] = row < p.rows;
         t_of[mt] = row_ok[mt] ? row / p.group : 0;
         h_of[mt] = kvh * p.group + (row_ok[mt] ? row % p.group : 0);
-        const int pos = p.s_k - p.T + t_of[mt];
+        const int pos = s_k - p.T + t_of[mt];
         r_hi[mt] = p.causal ? min(khi, pos + 1) : khi;
         r_lo[mt] = p.window > 0 ? max(klo, pos - p.window + 1) : klo;
         if (!row_ok[mt]) r_hi[mt] = r_lo[mt];  // no visible key: the row stays at -inf
@@ -475,7 +478,7 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
         const float inv = lq[mt] > 0.f ? 1.f / lq[mt] : 0.f;
         const float lse_val = l[mt] > 0.f ? (m[mt] + __log2f(l[mt])) * kLn2 : -INFINITY;
         if constexpr (SPLIT) {
-            const int64_t r = (((int64_t)b * p.n_h + h) * p.T + t) * p.n_split + part;
+            const int64_t r = (((int64_t)b * p.n_h + h) * p.T + t) * p.n_split_total + p.part_offset + part;
             float *op = p.o_part + r * HD + col0 + 4 * lg;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)

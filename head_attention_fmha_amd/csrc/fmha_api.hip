@@ -214,22 +214,60 @@ int fmha_forward(const void *q, const void *k, const void *v, void *o, float *ls
     p.o_sb = o_st.batch; p.o_st = o_st.token; p.o_sh = o_st.head;
     p.split_len = s_k;
     p.n_split = 1;
+    p.n_split_total = 1;
     return launch_attention<false>(p, hd, stream);
+}
+
+int fmha_forward_varlen(const void *q, const void *k, const void *v, const int *seqlens_k, void *o, float *lse,
+                        int batch, int n_h, int n_kv_h, int T, int s_k_max, int hd, fmha_strides q_st,
+                        fmha_strides k_st, fmha_strides v_st, fmha_strides o_st, float scale, int window, int causal,
+                        void *stream) {
+    if (!seqlens_k) return FMHA_ERR_INVALID_ARG;
+    int rc = validate_attention(q, k, v, o, lse, false, batch, n_h, n_kv_h, T, s_k_max, hd, q_st, k_st, v_st,
+                                &o_st, window, causal);
+    if (rc != FMHA_OK) return rc;
+    if ((reinterpret_cast<uintptr_t>(seqlens_k) & 3u) != 0) return FMHA_ERR_ALIGNMENT;
+    FwdParams p = make_params(q, k, v, batch, n_h, n_kv_h, T, s_k_max, q_st, k_st, v_st, scale, window, causal);
+    p.seqlens = seqlens_k;
+    p.o = static_cast<uint16_t *>(o);
+    p.lse = lse;
+    p.o_sb = o_st.batch; p.o_st = o_st.token; p.o_sh = o_st.head;
+    p.split_len = s_k_max;
+    p.n_split = 1;
+    p.n_split_total = 1;
+    return launch_attention<false>(p, hd, stream);
+}
+
+int fmha_decode_splitkv_segment(const void *q, const void *k, const void *v, const int *seqlens_k, float *o_part,
+                                float *lse_part, int batch, int n_h, int n_kv_h, int T, int s_k, int hd,
+                                fmha_strides q_st, fmha_strides k_st, fmha_strides v_st, float scale, int window,
+                                int causal, int split_len, int part_offset, int n_split_total, void *stream) {
+    if (split_len <= 0 || part_offset < 0) return FMHA_ERR_INVALID_ARG;
+    int rc = validate_attention(q, k, v, o_part, lse_part, true, batch, n_h, n_kv_h, T, s_k, hd, q_st, k_st, v_st,
+                                nullptr, window, causal);
+    if (rc != FMHA_OK) return rc;
+    const int64_t n_split = ((int64_t)s_k + split_len - 1) / split_len;
+    if ((int64_t)part_offset + n_split > n_split_total) return FMHA_ERR_INVALID_ARG;
+    if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) != 0) return FMHA_ERR_ALIGNMENT;
+    FwdParams p = make_params(q, k, v, batch, n_h, n_kv_h, T, s_k, q_st, k_st, v_st, scale, window, causal);
+    p.seqlens = seqlens_k;
+    p.o_part = o_part;
+    p.lse_part = lse_part;
+    p.split_len = split_len;
+    p.n_split = (int)n_split;
+    p.part_offset = part_offset;
+    p.n_split_total = n_split_total;
+    return launch_attention<true>(p, hd, stream);
 }
 
 int fmha_decode_splitkv(const void *q, const void *k, const void *v, float *o_part, float *lse_part, int batch,
                         int n_h, int n_kv_h, int T, int s_k, int hd, fmha_strides q_st, fmha_strides k_st,
                         fmha_strides v_st, float scale, int window, int causal, int split_len, void *stream) {
     if (split_len <= 0) return FMHA_ERR_INVALID_ARG;
-    int rc = validate_attention(q, k, v, o_part, lse_part, true, batch, n_h, n_kv_h, T, s_k, hd, q_st, k_st, v_st,
-                                nullptr, window, causal);
-    if (rc != FMHA_OK) return rc;
-    FwdParams p = make_params(q, k, v, batch, n_h, n_kv_h, T, s_k, q_st, k_st, v_st, scale, window, causal);
-    p.o_part = o_part;
-    p.lse_part = lse_part;
-    p.split_len = split_len;
-    p.n_split = (int)(((int64_t)s_k + split_len - 1) / split_len);
-    return launch_attention<true>(p, hd, stream);
+    const int64_t n_split = ((int64_t)s_k + split_len - 1) / split_len;
+    return fmha_decode_splitkv_segment(q, k, v, nullptr, o_part, lse_part, batch, n_h, n_kv_h, T, s_k, hd, q_st,
+                                       k_st, v_st, scale, window, causal, split_len, 0,
+                                       n_split > 0x7fffffff ? 0x7fffffff : (int)n_split, stream);
 }
 
 int fmha_lse_merge(const float *o_part, const float *lse_part, void *o, float *lse, int batch, int n_h, int T,

@@ -20,6 +20,9 @@ struct FwdParams {
     int rows;         // group * T rows per (batch, kv_head)
     int window, causal;
     int split_len, n_split;
+    const int *seqlens;  // device [batch] keys per batch row (ragged batch), or null: s_k for all
+    int part_offset;     // split mode: first partition slot this call writes
+    int n_split_total;   // split mode: partition slots per row in o_part / lse_part
     int n_row_blocks;
     int n_units;      // gridDim.x
     int xcd_remap;    // 1: n_units % 8 == 0, give each XCD a contiguous unit range

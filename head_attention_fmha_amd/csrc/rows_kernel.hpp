@@ -77,14 +77,17 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
     bid /= p.n_split;
     const int kvh = bid % p.n_kv_h;
     const int b = bid / p.n_kv_h;
+    // keys of this batch row: s_k, or the row's own length in a ragged batch
+    // (clamped to the cache capacity s_k)
+    const int s_k = p.seqlens ? min(max(p.seqlens[b], 0), p.s_k) : p.s_k;
 
     const int row0 = rb * S::ROWS;
     const int row_last = min(row0 + S::ROWS, p.rows) - 1;
     // key range: the partition, cut to the union of the block rows' masks
     int klo = part * p.split_len;
-    int khi = min(klo + p.split_len, p.s_k);
-    if (p.causal) khi = min(khi, p.s_k - p.T + row_last / p.group + 1);
-    if (p.window > 0) klo = max(klo, p.s_k - p.T + row0 / p.group - p.window + 1);
+    int khi = min(klo + p.split_len, s_k);
+    if (p.causal) khi = min(khi, s_k - p.T + row_last / p.group + 1);
+    if (p.window > 0) klo = max(klo, s_k - p.T + row0 / p.group - p.window + 1);
 
     // ---- this wave's tiles: rows, masks, and the key range of each tile ----
     bool row_ok[RT];
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
         row_ok[mt] = row <= row_last;
         t_of[mt] = row_ok[mt] ? row / p.group : 0;
         h_of[mt] = kvh * p.group + (row_ok[mt] ? row % p.group : 0);
-        const int pos = p.s_k - p.T + t_of[mt];
+        const int pos = s_k - p.T + t_of[mt];
         r_hi[mt] = p.causal ? min(khi, pos + 1) : khi;
         r_lo[mt] = p.window > 0 ? max(klo, pos - p.window + 1) : klo;
         if (!row_ok[mt]) r_hi[mt] = r_lo[mt];
@@ -108,8 +111,8 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
             full_lo[mt] = khi;
             full_hi[mt] = klo;
         } else {
-            const int pos_first = p.s_k - p.T + first / p.group;
-            const int pos_last = p.s_k - p.T + last / p.group;
+            const int pos_first = s_k - p.T + first / p.group;
+            const int pos_last = s_k - p.T + last / p.group;
             tile_hi[mt] = p.causal ? min(khi, pos_last + 1) : khi;
             tile_lo[mt] = p.window > 0 ? max(klo, pos_first - p.window + 1) : klo;
             // keys visible to EVERY row of the tile: chunks inside need no mask
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
         const float inv = lq > 0.f ? 1.f / lq : 0.f;
         const float lse_val = l[mt] > 0.f ? (m[mt] + __log2f(l[mt])) * kLn2 : -INFINITY;
         if constexpr (SPLIT) {
-            const int64_t r = (((int64_t)b * p.n_h + h) * p.T + t) * p.n_split + part;
+            const int64_t r = (((int64_t)b * p.n_h + h) * p.T + t) * p.n_split_total + p.part_offset + part;
             float *op = p.o_part + r * HD + 4 * lg;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)

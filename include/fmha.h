@@ -130,6 +130,57 @@ int fmha_decode_splitkv(const void *q, const void *k, const void *v,
                         float scale, int window, int causal, int split_len, void *stream);
 
 /*
+ * fmha_forward_varlen -- fmha_forward over a ragged batch in a padded cache:
+ * batch row b holds seqlens_k[b] keys (positions 0 .. seqlens_k[b] - 1 of
+ * k and v, which are allocated for s_k_max keys), and its T queries sit at
+ * positions seqlens_k[b] - T + i.  Everything else is as fmha_forward with
+ * s_k = seqlens_k[b] for that row; a query at a negative position under a
+ * causal mask, or a row of length 0, sees no key (O = 0, lse = -inf).
+ * Lengths are read on the device and clamped to [0, s_k_max].
+ * The per-row length generalises the single-segment decode of the commit
+ * log at e4ee9fdc, whose fast path took one uniform length per call.
+ *
+ *   seqlens_k  [batch] int32, DEVICE memory, 4-byte aligned (read)
+ * Errors: as fmha_forward with s_k = s_k_max (T <= s_k_max when masked);
+ * FMHA_ERR_INVALID_ARG for a null seqlens_k, FMHA_ERR_ALIGNMENT for a
+ * misaligned one.
+ */
+int fmha_forward_varlen(const void *q, const void *k, const void *v, const int *seqlens_k,
+                        void *o, float *lse,
+                        int batch, int n_h, int n_kv_h, int T, int s_k_max, int hd,
+                        fmha_strides q_st, fmha_strides k_st, fmha_strides v_st, fmha_strides o_st,
+                        float scale, int window, int causal, void *stream);
+
+/*
+ * fmha_decode_splitkv_segment -- fmha_decode_splitkv for one key segment of
+ * several (for example a few global "sink" keys in one cache and a sliding
+ * window in another), writing its partitions into slots
+ * [part_offset, part_offset + ceil(s_k / split_len)) of partial buffers that
+ * hold n_split_total slots per row.  One fmha_lse_merge over all
+ * n_split_total slots then yields attention over the union of the segments:
+ * the D5 merge ("Next steps", item 4 of CURRENT_ISSUE.md) applies to any
+ * set of disjoint key sets, and the commit log at e4ee9fdc names
+ * multi-segment calls as the case its fast path left to a slower one.
+ * Masks and query positions are taken within the segment (positions
+ * s - T + i for a segment of s keys).  seqlens_k (nullable, device int32
+ * [batch]) gives per-row segment lengths as in fmha_forward_varlen; slots
+ * whose keys lie past a row's length are written empty (O_p = 0,
+ * lse_p = -inf).  Slots outside this call's range are not touched.
+ *
+ *   o_part   [batch][n_h][T][n_split_total][hd] fp32 (slots written)
+ *   lse_part [batch][n_h][T][n_split_total]     fp32 (slots written)
+ * Errors: as fmha_decode_splitkv; FMHA_ERR_INVALID_ARG for part_offset < 0
+ * or part_offset + ceil(s_k / split_len) > n_split_total;
+ * FMHA_ERR_ALIGNMENT for a misaligned seqlens_k.
+ */
+int fmha_decode_splitkv_segment(const void *q, const void *k, const void *v, const int *seqlens_k,
+                                float *o_part, float *lse_part,
+                                int batch, int n_h, int n_kv_h, int T, int s_k, int hd,
+                                fmha_strides q_st, fmha_strides k_st, fmha_strides v_st,
+                                float scale, int window, int causal, int split_len,
+                                int part_offset, int n_split_total, void *stream);
+
+/*
  * fmha_lse_merge -- the D5 merge ("Next steps", item 4 of CURRENT_ISSUE.md):
  *   O   = sum_p exp(lse_p) O_p / sum_p exp(lse_p)
  *   lse = ln sum_p exp(lse_p)

@@ -7,6 +7,7 @@ leg import this package.  It shares no code with the GPU path.
 Every function takes host bf16 tensors (torch.bfloat16 on the CPU, any
 strides with a contiguous head dimension) and returns float64 tensors:
   attention -> (o [b, T, n_h, hd], lse [b, n_h, T])
+  attention_varlen -> the same for a ragged batch (per-row key counts)
   split     -> (o_part [b, n_h, T, n_split, hd], lse_part [b, n_h, T, n_split])
   merge     -> (o [rows, hd], lse [rows])
   weights   -> w [b, n_h, T, s_k]
@@ -93,6 +94,24 @@ def attention(q, k, v, scale, *, causal=False, window=0, threads=None):
                               threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_attention failed ({rc})")
+    return o, lse
+
+
+def attention_varlen(q, k, v, seqlens, scale, *, causal=False, window=0, threads=None):
+    """Ragged batch in a padded cache: batch row b attends to its first
+    seqlens[b] keys, its T queries at positions seqlens[b] - T + i -- the
+    plain definition applied to each row's own cache.  A row without keys
+    gives O = 0, lse = -inf.  Returns (o [b, T, n_h, hd], lse [b, n_h, T])."""
+    b, n_h, n_kv_h, T, s_k, hd = _dims(q, k, v)
+    o = torch.zeros((b, T, n_h, hd), dtype=torch.float64)
+    lse = torch.full((b, n_h, T), float("-inf"), dtype=torch.float64)
+    for r in range(b):
+        L = max(0, min(int(seqlens[r]), s_k))
+        if L == 0:
+            continue
+        o_r, lse_r = attention(q[r:r + 1], k[r:r + 1, :L], v[r:r + 1, :L], scale, causal=causal, window=window,
+                               threads=threads)
+        o[r], lse[r] = o_r[0], lse_r[0]
     return o, lse
 
 

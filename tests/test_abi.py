@@ -30,8 +30,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fmha_attention_plan", "fmha_decode_splitkv", "fmha_forward", "fmha_lse_merge",
-                                    "fmha_status_string"]
+    assert declared_functions() == ["fmha_attention_plan", "fmha_decode_splitkv", "fmha_decode_splitkv_segment",
+                                    "fmha_forward", "fmha_forward_varlen", "fmha_lse_merge", "fmha_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -101,6 +101,40 @@ def test_forward_rejects(lib, kw, code):
 ])
 def test_splitkv_rejects(lib, kw, code):
     assert split(lib, **kw) == code
+
+
+SLP = ctypes.c_void_p(0x60000)  # fake device address of a seqlens array
+
+
+def fwd_varlen(lib, seqlens=SLP, T=4, s_k=64, hd=128, causal=1, window=0):
+    st_q = dense(T, 8, hd)
+    st_k = dense(s_k, 2, hd)
+    return lib.fmha_forward_varlen(QP, KP, VP, seqlens, OP, LP, 2, 8, 2, T, s_k, hd, st_q, st_k, st_k, st_q,
+                                   0.1, window, causal, None)
+
+
+def segment(lib, seqlens=None, split_len=16, part_offset=0, n_split_total=4, s_k=64, hd=128, T=1):
+    st_q = dense(T, 8, hd)
+    st_k = dense(s_k, 2, hd)
+    return lib.fmha_decode_splitkv_segment(QP, KP, VP, seqlens, OP, LP, 2, 8, 2, T, s_k, hd, st_q, st_k, st_k,
+                                           0.1, 0, 0, split_len, part_offset, n_split_total, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(seqlens=None), INVALID), (dict(seqlens=ctypes.c_void_p(0x60002)), ALIGN), (dict(hd=96), UNSUPPORTED),
+    (dict(T=65, s_k=64), INVALID),
+])
+def test_forward_varlen_rejects(lib, kw, code):
+    assert fwd_varlen(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(part_offset=-1), INVALID), (dict(part_offset=1), INVALID), (dict(n_split_total=3), INVALID),
+    (dict(split_len=0), INVALID), (dict(seqlens=ctypes.c_void_p(0x60001)), ALIGN), (dict(hd=48), UNSUPPORTED),
+])
+def test_segment_rejects(lib, kw, code):
+    # 64 keys in partitions of 16 fill exactly the 4 slots at offset 0
+    assert segment(lib, **kw) == code
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -382,3 +382,110 @@ def test_merge_kernel_against_oracle_merge(hd, n_split):
     fa.fmha_lse_merge(o_part.to(DEV), lse_part.to(DEV), o, lse)
     torch.cuda.synchronize()
     check_attention(o, lse, o_ref.permute(0, 2, 1, 3), lse_ref, lse_tol=1e-5, what="merge")
+
+
+# ---------------------------------------------------------------------------
+# Ragged batches (per-row key counts) and multi-segment split + merge
+# ---------------------------------------------------------------------------
+
+def _poison_past(t, lens):
+    """NaN in every cache slot past each row's length: such keys must never
+    reach a result."""
+    t = t.clone()
+    for r, L in enumerate(lens):
+        t[r, L:] = float("nan")
+    return t
+
+
+VARLEN = [
+    ("decode-gqa", (6, 8, 2, 1, 600), [1, 0, 77, 300, 600, 513], False, 0),
+    ("prefill-causal-short-rows", (4, 4, 4, 40, 300), [300, 39, 7, 150], True, 0),
+    ("prefill-mqa-window", (3, 16, 1, 20, 500), [500, 130, 21], True, 64),
+    ("prefill-row-parallel", (4, 64, 64, 100, 300), [300, 250, 100, 77], True, 0),
+]
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+@pytest.mark.parametrize("name,dims,lens,causal,window", VARLEN, ids=[c[0] for c in VARLEN])
+def test_varlen_forward(name, dims, lens, causal, window, hd):
+    b, n_h, n_kv_h, T, s_max = dims
+    seed = 700 + hd + len(name)
+    q = I.randn_bf16((b, T, n_h, hd), seed)
+    k = I.randn_bf16((b, s_max, n_kv_h, hd), seed + 1)
+    v = I.randn_bf16((b, s_max, n_kv_h, hd), seed + 2)
+    scale = 1.0 / math.sqrt(hd)
+    o_ref, lse_ref = oracle.attention_varlen(q, k, v, lens, scale, causal=causal, window=window)
+    seqlens = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o = nan_bf16(b, T, n_h, hd)
+    lse = nan_f32(b, n_h, T)
+    fa.fmha_forward_varlen(q.to(DEV), _poison_past(k, lens).to(DEV), _poison_past(v, lens).to(DEV), seqlens, o,
+                           lse, scale=scale, window=window, causal=causal)
+    torch.cuda.synchronize()
+    check_attention(o, lse, o_ref, lse_ref, what=f"varlen {name}")
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+def test_varlen_split_then_merge(hd):
+    lens = [1, 0, 129, 1000, 4096]
+    b, n_h, n_kv_h, T, s_max, split_len = len(lens), 8, 1, 1, 4096, 128
+    q = I.randn_bf16((b, T, n_h, hd), 800 + hd)
+    k = I.randn_bf16((b, s_max, n_kv_h, hd), 801 + hd)
+    v = I.randn_bf16((b, s_max, n_kv_h, hd), 802 + hd)
+    scale = 1.0 / math.sqrt(hd)
+    o_ref, lse_ref = oracle.attention_varlen(q, k, v, lens, scale)
+    ns = fa.n_split_for(s_max, split_len)
+    o_part = nan_f32(b, n_h, T, ns, hd)
+    lse_part = nan_f32(b, n_h, T, ns)
+    fa.fmha_decode_splitkv_segment(q.to(DEV), _poison_past(k, lens).to(DEV), _poison_past(v, lens).to(DEV), o_part,
+                                   lse_part, split_len=split_len, part_offset=0,
+                                   seqlens_k=torch.tensor(lens, dtype=torch.int32, device=DEV), scale=scale)
+    o = nan_bf16(b, T, n_h, hd)
+    lse = nan_f32(b, n_h, T)
+    fa.fmha_lse_merge(o_part, lse_part, o, lse)
+    torch.cuda.synchronize()
+    check_attention(o, lse, o_ref, lse_ref, what="varlen split+merge")
+    # slots past a row's length are empty
+    lp = lse_part.cpu()
+    for r, L in enumerate(lens):
+        assert torch.all(lp[r, :, :, fa.n_split_for(max(L, 1), split_len) if L else 0:] == -math.inf)
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+@pytest.mark.parametrize("varlen", [False, True])
+def test_multi_segment_sink_plus_window(hd, varlen):
+    """A few global keys in one cache and a sliding window over a second cache,
+    each split into its own slots of one partial buffer, merged in one pass:
+    attention over the union of the two key sets."""
+    b, T, n_h, n_kv_h, s_sink, s_win = 3, 4, 8, 2, 4, 800
+    q = I.randn_bf16((b, T, n_h, hd), 850 + hd)
+    ks = I.randn_bf16((b, s_sink, n_kv_h, hd), 851 + hd)
+    vs = I.randn_bf16((b, s_sink, n_kv_h, hd), 852 + hd)
+    kw = I.randn_bf16((b, s_win, n_kv_h, hd), 853 + hd)
+    vw = I.randn_bf16((b, s_win, n_kv_h, hd), 854 + hd)
+    scale = 1.0 / math.sqrt(hd)
+    lens = [800, 333, 57] if varlen else [s_win] * b
+    # expected: the oracle's own partitions of each segment, merged in fp64
+    op_s, lp_s = oracle.split(q, ks, vs, scale, 32)
+    parts_w = [oracle.split(q[r:r + 1], kw[r:r + 1, :lens[r]], vw[r:r + 1, :lens[r]], scale, 128, causal=True,
+                            window=100) for r in range(b)]
+    ns_w = fa.n_split_for(s_win, 128)
+    op_w = torch.zeros((b, n_h, T, ns_w, hd), dtype=torch.float64)
+    lp_w = torch.full((b, n_h, T, ns_w), -math.inf, dtype=torch.float64)
+    for r, (op, lp) in enumerate(parts_w):
+        op_w[r, :, :, :op.shape[3]] = op[0]
+        lp_w[r, :, :, :lp.shape[3]] = lp[0]
+    o_ref, lse_ref = oracle.merge(torch.cat([op_s, op_w], 3), torch.cat([lp_s, lp_w], 3))
+    ns_s = fa.n_split_for(s_sink, 32)
+    o_part = nan_f32(b, n_h, T, ns_s + ns_w, hd)
+    lse_part = nan_f32(b, n_h, T, ns_s + ns_w)
+    qd = q.to(DEV)
+    fa.fmha_decode_splitkv_segment(qd, ks.to(DEV), vs.to(DEV), o_part, lse_part, split_len=32, part_offset=0,
+                                   scale=scale)
+    fa.fmha_decode_splitkv_segment(qd, _poison_past(kw, lens).to(DEV), _poison_past(vw, lens).to(DEV), o_part,
+                                   lse_part, split_len=128, part_offset=ns_s, scale=scale, causal=True, window=100,
+                                   seqlens_k=torch.tensor(lens, dtype=torch.int32, device=DEV) if varlen else None)
+    o = nan_bf16(b, T, n_h, hd)
+    lse = nan_f32(b, n_h, T)
+    fa.fmha_lse_merge(o_part, lse_part, o, lse)
+    torch.cuda.synchronize()
+    check_attention(o, lse, o_ref.permute(0, 2, 1, 3), lse_ref, what="sink + window segments")

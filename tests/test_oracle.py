@@ -381,3 +381,56 @@ def test_large_scores_do_not_overflow():
     assert torch.all(torch.isfinite(o)) and torch.isfinite(lse).all()
     j = int(torch.argmax(k[0, :, 0].double().sum(-1)))
     assert (o[0, 0, 0] - v[0, j, 0].double()).abs().max().item() < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# Ragged batches and multi-segment merges
+# ---------------------------------------------------------------------------
+
+def test_varlen_single_key_row_is_that_value_and_empty_row_is_zero():
+    """Per-row lengths: a row with one key returns that key's V exactly (the
+    softmax of one score is 1) and lse = scale * q.k; a row with no key
+    returns O = 0, lse = -inf; a full-length row equals plain attention."""
+    b, T, n_h, s_k, hd = 3, 1, 2, 20, 16
+    q, k, v = qkv(b, T, n_h, 1, s_k, hd, seed=500)
+    o, lse = oracle.attention_varlen(q, k, v, [1, 0, s_k], 0.3)
+    for h in range(n_h):
+        assert torch.equal(o[0, 0, h], v[0, 0, 0].double())
+        scale32 = float(torch.tensor(0.3, dtype=torch.float32))  # the scale as the device receives it
+        ref = scale32 * (q[0, 0, h].double() * k[0, 0, 0].double()).sum().item()
+        assert abs(lse[0, h, 0].item() - ref) < 1e-12
+    assert torch.all(o[1] == 0) and torch.all(lse[1] == -math.inf)
+    o_full, lse_full = oracle.attention(q[2:], k[2:], v[2:], 0.3)
+    assert torch.equal(o[2], o_full[0]) and torch.equal(lse[2], lse_full[0])
+
+
+def test_varlen_causal_rows_before_the_first_key_are_empty():
+    """T queries at the end of a row of L < T keys: the first T - L queries sit
+    at negative positions and see nothing; query i >= T - L sees keys
+    0..i-(T-L), i.e. it is the prefill row of a cache of L keys."""
+    b, T, n_h, s_k, hd = 1, 6, 2, 10, 8
+    q, k, v = qkv(b, T, n_h, 2, s_k, hd, seed=510)
+    L = 4
+    o, lse = oracle.attention_varlen(q, k, v, [L], 0.5, causal=True)
+    assert torch.all(o[0, :T - L] == 0) and torch.all(lse[0, :, :T - L] == -math.inf)
+    for i in range(T - L, T):
+        pos = L - T + i
+        o_i, lse_i = oracle.attention(q[:, i:i + 1], k[:, :pos + 1], v[:, :pos + 1], 0.5, causal=True)
+        assert torch.allclose(o[0, i], o_i[0, 0], atol=1e-14, rtol=0)
+        assert torch.allclose(lse[0, :, i], lse_i[0, :, 0], atol=1e-14, rtol=0)
+
+
+@pytest.mark.parametrize("split_a,split_b", [(3, 5), (16, 1), (100, 100)])
+def test_merge_over_segments_equals_attention_over_their_union(split_a, split_b):
+    """Two unmasked key segments from separate caches, each split into its own
+    partitions and merged in one pass, give attention over the concatenated
+    keys (the merge identity on disjoint key sets)."""
+    b, T, n_h, hd = 2, 3, 4, 16
+    qa, ka, va = qkv(b, T, n_h, 2, 7, hd, seed=520)
+    _, kb, vb = qkv(b, T, n_h, 2, 30, hd, seed=530)
+    op_a, lp_a = oracle.split(qa, ka, va, 0.4, split_a)
+    op_b, lp_b = oracle.split(qa, kb, vb, 0.4, split_b)
+    o, lse = oracle.merge(torch.cat([op_a, op_b], dim=3), torch.cat([lp_a, lp_b], dim=3))
+    o_u, lse_u = oracle.attention(qa, torch.cat([ka, kb], dim=1), torch.cat([va, vb], dim=1), 0.4)
+    assert (o.permute(0, 2, 1, 3) - o_u).abs().max().item() < 1e-13
+    assert (lse - lse_u).abs().max().item() < 1e-13
