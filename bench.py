@@ -14,6 +14,8 @@ Also reported on the same line:
                 each launch on the launch stream, against 8 TB/s.
   cpu_baseline  the fp64 CPU oracle computing the same workload (split +
                 merge) on the host cores, as KV-read GB/s.
+  ragged_decode the same decode shapes with per-row key counts uniform on
+                1..8192 (split + merge), as GB/s of the K/V actually read.
   prefill       the largest causal MHA prefill point, the sliding-window
                 MQA prefill and a long causal GQA prefill (T = s_k = 4096):
                 fused-kernel TFLOP/s (algorithmic flops) against the dense
@@ -151,6 +153,40 @@ def run_decode(args, torch, fa, I):
     return res
 
 
+def run_ragged_decode(args, torch, fa, I):
+    """Ragged split-KV decode: per-row key counts uniform on 1..8192."""
+    w = I.RAGGED_DECODE
+    q, k, v = I.make_qkv(w, device="cuda")
+    lens = I.ragged_lengths(w.batch, w.s_k)
+    seqlens = lens.to("cuda")
+    o_part = torch.empty((w.batch, w.n_h, w.T, w.n_split, w.hd), dtype=torch.float32, device="cuda")
+    lse_part = torch.empty((w.batch, w.n_h, w.T, w.n_split), dtype=torch.float32, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.n_h, w.T), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.fmha_decode_splitkv_segment(q, k, v, o_part, lse_part, split_len=w.split_len, part_offset=0,
+                                       seqlens_k=seqlens, scale=w.scale, stream=stream)
+        fa.fmha_lse_merge(o_part, lse_part, o, lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / args.steps
+    kv_bytes = 4 * int(lens.sum()) * w.n_kv_h * w.hd
+    log(f"ragged decode {w.name}: {us:.1f} us/step, {kv_bytes / (us * 1e-6) / 1e9:.0f} GB/s of K/V")
+    return {"workload": w.name, "us_per_step": round(us, 2), "kv_gbs": round(kv_bytes / (us * 1e-6) / 1e9, 1),
+            "kv_bytes": kv_bytes, "mean_len": round(float(lens.float().mean()), 1),
+            "step": "fmha_decode_splitkv_segment (per-row lengths) + fmha_lse_merge"}
+
+
 def graph_time_us(torch, calls, reps):
     """Capture `calls` (one launch each) into one graph; return mean us per call."""
     stream = torch.cuda.Stream()
@@ -275,6 +311,7 @@ def main():
     res = run_decode(args, torch, fa, I)
     if args.calibrate_copy:
         calibrate_copy()
+    ragged = run_ragged_decode(args, torch, fa, I)
     prefill = None if args.no_prefill else run_prefill(torch, fa, I)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(res, args.cpu_seconds)
     w = res["w"]
@@ -305,6 +342,7 @@ def main():
                      "alg_bytes_per_launch": res["split_bytes"], "launch_us": round(split_us, 2)},
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "ragged_decode": ragged,
     }
     print(json.dumps(line), flush=True)
 

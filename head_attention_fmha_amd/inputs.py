@@ -132,3 +132,15 @@ def gqa_causal_prefill_long(T: int, hd: int, batch: int = 2, n_h: int = 32, n_kv
 
 
 LONG_PREFILL = gqa_causal_prefill_long(4096, 128)
+
+# A ragged decode batch: the GQA split-KV workload's shapes with per-row key
+# counts drawn uniformly from 1..s_k (the cache holds s_k per row).
+RAGGED_DECODE = Workload("gqa_ragged_decode_b32_h64_kv8_skmax8192_hd128", 32, 64, 8, 1, 8192, 128,
+                         v_dist="uniform", split_len=128)
+
+
+def ragged_lengths(batch: int, s_max: int, seed: int = 0) -> torch.Tensor:
+    """int32 [batch] key counts, uniform on 1..s_max (CPU generator)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return torch.randint(1, s_max + 1, (batch,), generator=g, dtype=torch.int32)

@@ -489,3 +489,24 @@ def test_multi_segment_sink_plus_window(hd, varlen):
     fa.fmha_lse_merge(o_part, lse_part, o, lse)
     torch.cuda.synchronize()
     check_attention(o, lse, o_ref.permute(0, 2, 1, 3), lse_ref, what="sink + window segments")
+
+
+def test_ragged_decode_full_size_sampled_rows():
+    """The timed ragged decode workload at full size (device-drawn inputs);
+    the oracle recomputes four batch rows, each over its own key count."""
+    w = I.RAGGED_DECODE
+    q, k, v = I.make_qkv(w, device="cuda")
+    lens = I.ragged_lengths(w.batch, w.s_k)
+    o_part = nan_f32(w.batch, w.n_h, w.T, w.n_split, w.hd)
+    lse_part = nan_f32(w.batch, w.n_h, w.T, w.n_split)
+    fa.fmha_decode_splitkv_segment(q, k, v, o_part, lse_part, split_len=w.split_len, part_offset=0,
+                                   seqlens_k=lens.to(DEV), scale=w.scale)
+    o = nan_bf16(w.batch, w.T, w.n_h, w.hd)
+    lse = nan_f32(w.batch, w.n_h, w.T)
+    fa.fmha_lse_merge(o_part, lse_part, o, lse)
+    torch.cuda.synchronize()
+    order = torch.argsort(lens)
+    for r in (int(order[0]), int(order[1]), int(order[-1]), 17):
+        L = int(lens[r])
+        o_ref, lse_ref = oracle.attention(q[r:r + 1].cpu(), k[r:r + 1, :L].cpu(), v[r:r + 1, :L].cpu(), w.scale)
+        check_attention(o[r:r + 1], lse[r:r + 1], o_ref, lse_ref, what=f"{w.name} row {r} ({L} keys)")
