@@ -13,6 +13,8 @@ Entry points carry the C names:
   fmha_lse_merge(o_part, lse_part, o, lse=None)
   fmha_forward_varlen(q, k, v, seqlens_k, o, lse=None, *, scale=None, window=0, causal=False)
   fmha_decode_splitkv_segment(q, k, v, o_part, lse_part, *, split_len, part_offset, seqlens_k=None, ...)
+  fmha_forward_mx(q, k, v, o_codes, o_scales, lse=None, *, fmt, ...)   (MX_FP8_E4M3 / MX_FP4_E2M1 output)
+  fmha_lse_merge_mx(o_part, lse_part, o_codes, o_scales, lse=None, *, fmt)
   fmha_status_string(status)
   fmha_attention_plan(batch, n_h, n_kv_h, T, s_k, hd, *, window=0, causal=False, split_len=0, mqa_stride0=False)
 Layouts: q, o [batch, T, n_h, hd]; k, v [batch, s_k, n_kv_h, hd] (a head
@@ -29,7 +31,8 @@ from typing import Optional
 import torch
 
 __all__ = ["FmhaError", "fmha_forward", "fmha_forward_varlen", "fmha_decode_splitkv", "fmha_decode_splitkv_segment",
-           "fmha_lse_merge", "fmha_status_string",
+           "fmha_lse_merge", "fmha_forward_mx", "fmha_lse_merge_mx", "MX_FP8_E4M3", "MX_FP4_E2M1", "mx_shapes",
+           "fmha_status_string",
            "fmha_attention_plan", "n_split_for", "library_path", "load_library", "FmhaStrides", "FmhaPlan"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +78,10 @@ def load_library():
     lib.fmha_decode_splitkv_segment.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, S, S, S, F, I, I, I, I, I,
                                                 P]
     lib.fmha_decode_splitkv_segment.restype = I
+    lib.fmha_forward_mx.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, S, S, S, F, I, I, I, P]
+    lib.fmha_forward_mx.restype = I
+    lib.fmha_lse_merge_mx.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
+    lib.fmha_lse_merge_mx.restype = I
     lib.fmha_lse_merge.argtypes = [P, P, P, P, I, I, I, I, I, S, P]
     lib.fmha_lse_merge.restype = I
     lib.fmha_attention_plan.argtypes = [I, I, I, I, I, I, S, S, I, I, I, ctypes.POINTER(FmhaPlan)]
@@ -246,3 +253,49 @@ def fmha_attention_plan(batch, n_h, n_kv_h, T, s_k, hd, *, window=0, causal=Fals
     _check(load_library().fmha_attention_plan(batch, n_h, n_kv_h, T, s_k, hd, kv_st, kv_st, int(window),
                                               int(bool(causal)), int(split_len), ctypes.byref(plan)))
     return {name: getattr(plan, name) for name, _ in FmhaPlan._fields_}
+
+
+MX_FP8_E4M3 = 1
+MX_FP4_E2M1 = 2
+
+
+def mx_shapes(b, T, n_h, hd, fmt):
+    """(codes shape, scales shape) of an MX output; both uint8, dense."""
+    if fmt not in (MX_FP8_E4M3, MX_FP4_E2M1):
+        raise ValueError("fmt must be MX_FP8_E4M3 or MX_FP4_E2M1")
+    return (b, T, n_h, hd if fmt == MX_FP8_E4M3 else hd // 2), (b, T, n_h, hd // 32)
+
+
+def fmha_forward_mx(q, k, v, o_codes, o_scales, lse=None, *, fmt, scale=None, window=0, causal=False,
+                    stream=None) -> None:
+    """fmha_forward with the output in an MX format (codes + E8M0 block
+    scales); see include/fmha.h."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev4(t, n)
+    b, T, n_h, hd = q.shape
+    _, s_k, n_kv_h, _ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != b or k.shape[3] != hd:
+        raise ValueError("shape mismatch between q, k, v")
+    cs, ss = mx_shapes(b, T, n_h, hd, fmt)
+    _dense(o_codes, cs, "o_codes", torch.uint8)
+    _dense(o_scales, ss, "o_scales", torch.uint8)
+    _dense(lse, (b, n_h, T), "lse")
+    _check(load_library().fmha_forward_mx(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o_codes), _ptr(o_scales), _ptr(lse), b, n_h, n_kv_h, T, s_k, hd,
+        _st(q), _st(k), _st(v), _scale(scale, hd), int(window), int(bool(causal)), int(fmt), _stream(stream)))
+
+
+def fmha_lse_merge_mx(o_part, lse_part, o_codes, o_scales, lse=None, *, fmt, stream=None) -> None:
+    """fmha_lse_merge with the output in an MX format; see include/fmha.h."""
+    if o_part.dim() != 5:
+        raise ValueError("o_part must be [batch, n_h, T, n_split, hd]")
+    b, n_h, T, ns, hd = o_part.shape
+    _dense(o_part, (b, n_h, T, ns, hd), "o_part")
+    _dense(lse_part, (b, n_h, T, ns), "lse_part")
+    cs, ss = mx_shapes(b, T, n_h, hd, fmt)
+    _dense(o_codes, cs, "o_codes", torch.uint8)
+    _dense(o_scales, ss, "o_scales", torch.uint8)
+    _dense(lse, (b, n_h, T), "lse")
+    _check(load_library().fmha_lse_merge_mx(
+        _ptr(o_part), _ptr(lse_part), _ptr(o_codes), _ptr(o_scales), _ptr(lse), b, n_h, T, hd, ns, int(fmt),
+        _stream(stream)))

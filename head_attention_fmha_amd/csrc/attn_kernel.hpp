@@ -51,6 +51,7 @@
 #pragma once
 
 #include "device_common.hpp"
+#include "mx_quant.hpp"
 #include "params.hpp"
 
 namespace fmha {
@@ -484,6 +485,22 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
             for (int nb = 0; nb < NB; ++nb)
                 __builtin_nontemporal_store(acc[mt][nb] * inv, reinterpret_cast<f32x4 *>(op + 16 * nb));
             if (hp == 0 && lg == 0) p.lse_part[r] = lse_val;
+        } else if (p.out_format != kOutBf16) {
+            // MX codes: 32-column blocks = pairs of 16-column blocks over the row's 4 lanes
+            const int64_t orow = ((int64_t)b * p.T + t) * p.n_h + h;
+            uint8_t *crow = p.o_codes + orow * (p.out_format == kOutMxFp8E4M3 ? HD : HD / 2);
+            uint8_t *srow = p.o_scales + orow * (HD / 32);
+#pragma unroll
+            for (int nb = 0; nb < NB; nb += 2) {
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[j] = acc[mt][nb][j] * inv;
+                    v[4 + j] = acc[mt][nb + 1][j] * inv;
+                }
+                mx_store_block_4lanes(v, p.out_format, crow, srow, col0 + 16 * nb, lg);
+            }
+            if (hp == 0 && lg == 0 && p.lse != nullptr) p.lse[((int64_t)b * p.n_h + h) * p.T + t] = lse_val;
         } else {
             uint16_t *op = p.o + (int64_t)b * p.o_sb + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + col0 + 4 * lg;
 #pragma unroll

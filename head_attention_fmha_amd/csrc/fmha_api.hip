@@ -198,6 +198,32 @@ int launch_attention(FwdParams p, int hd, void *stream) {
     return hipGetLastError() == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
 }
 
+int launch_merge(MergeParams p, int batch, int n_h, int T, int hd, int n_split, void *stream) {
+    const int64_t rows = (int64_t)batch * n_h * T;
+    p.n_h = n_h;
+    p.T = T;
+    p.n_split = n_split;
+    int rpw;
+    switch (hd) {
+        case 64: rpw = fmha::MergeShape<64>::RPW; break;
+        case 128: rpw = fmha::MergeShape<128>::RPW; break;
+        case 256: rpw = fmha::MergeShape<256>::RPW; break;
+        default: rpw = fmha::MergeShape<512>::RPW; break;
+    }
+    const int64_t blocks = (rows + rpw - 1) / rpw;
+    if (rows > 0x7fffffff || blocks > 0x7fffffff) return FMHA_ERR_UNSUPPORTED;
+    p.rows = (int)rows;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)blocks), block(256);
+    switch (hd) {
+        case 64: hipLaunchKernelGGL(fmha::merge_kernel<64>, grid, block, 0, s, p); break;
+        case 128: hipLaunchKernelGGL(fmha::merge_kernel<128>, grid, block, 0, s, p); break;
+        case 256: hipLaunchKernelGGL(fmha::merge_kernel<256>, grid, block, 0, s, p); break;
+        default: hipLaunchKernelGGL(fmha::merge_kernel<512>, grid, block, 0, s, p); break;
+    }
+    return hipGetLastError() == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -233,6 +259,25 @@ int fmha_forward_varlen(const void *q, const void *k, const void *v, const int *
     p.lse = lse;
     p.o_sb = o_st.batch; p.o_st = o_st.token; p.o_sh = o_st.head;
     p.split_len = s_k_max;
+    p.n_split = 1;
+    p.n_split_total = 1;
+    return launch_attention<false>(p, hd, stream);
+}
+
+int fmha_forward_mx(const void *q, const void *k, const void *v, void *o_codes, void *o_scales, float *lse,
+                    int batch, int n_h, int n_kv_h, int T, int s_k, int hd, fmha_strides q_st, fmha_strides k_st,
+                    fmha_strides v_st, float scale, int window, int causal, int format, void *stream) {
+    if (!o_scales) return FMHA_ERR_INVALID_ARG;
+    if (format != FMHA_MX_FP8_E4M3 && format != FMHA_MX_FP4_E2M1) return FMHA_ERR_INVALID_ARG;
+    int rc = validate_attention(q, k, v, o_codes, lse, false, batch, n_h, n_kv_h, T, s_k, hd, q_st, k_st, v_st,
+                                nullptr, window, causal);
+    if (rc != FMHA_OK) return rc;
+    FwdParams p = make_params(q, k, v, batch, n_h, n_kv_h, T, s_k, q_st, k_st, v_st, scale, window, causal);
+    p.lse = lse;
+    p.out_format = format;
+    p.o_codes = static_cast<uint8_t *>(o_codes);
+    p.o_scales = static_cast<uint8_t *>(o_scales);
+    p.split_len = s_k;
     p.n_split = 1;
     p.n_split_total = 1;
     return launch_attention<false>(p, hd, stream);
@@ -278,35 +323,32 @@ int fmha_lse_merge(const float *o_part, const float *lse_part, void *o, float *l
     if (!aligned16(o_part) || !aligned16(lse_part) || !aligned16(o) || (lse && !aligned16(lse)))
         return FMHA_ERR_ALIGNMENT;
     if (!strides_ok(o_st)) return FMHA_ERR_ALIGNMENT;
-    const int64_t rows = (int64_t)batch * n_h * T;
     MergeParams p{};
     p.o_part = o_part;
     p.lse_part = lse_part;
     p.o = static_cast<uint16_t *>(o);
     p.lse = lse;
     p.o_sb = o_st.batch; p.o_st = o_st.token; p.o_sh = o_st.head;
-    p.n_h = n_h;
-    p.T = T;
-    p.n_split = n_split;
-    int rpw;
-    switch (hd) {
-        case 64: rpw = fmha::MergeShape<64>::RPW; break;
-        case 128: rpw = fmha::MergeShape<128>::RPW; break;
-        case 256: rpw = fmha::MergeShape<256>::RPW; break;
-        default: rpw = fmha::MergeShape<512>::RPW; break;
-    }
-    const int64_t blocks = (rows + rpw - 1) / rpw;
-    if (rows > 0x7fffffff || blocks > 0x7fffffff) return FMHA_ERR_UNSUPPORTED;
-    p.rows = (int)rows;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const dim3 grid((unsigned)blocks), block(256);
-    switch (hd) {
-        case 64: hipLaunchKernelGGL(fmha::merge_kernel<64>, grid, block, 0, s, p); break;
-        case 128: hipLaunchKernelGGL(fmha::merge_kernel<128>, grid, block, 0, s, p); break;
-        case 256: hipLaunchKernelGGL(fmha::merge_kernel<256>, grid, block, 0, s, p); break;
-        default: hipLaunchKernelGGL(fmha::merge_kernel<512>, grid, block, 0, s, p); break;
-    }
-    return hipGetLastError() == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+    p.out_format = fmha::kOutBf16;
+    return launch_merge(p, batch, n_h, T, hd, n_split, stream);
+}
+
+int fmha_lse_merge_mx(const float *o_part, const float *lse_part, void *o_codes, void *o_scales, float *lse,
+                      int batch, int n_h, int T, int hd, int n_split, int format, void *stream) {
+    if (!o_part || !lse_part || !o_codes || !o_scales) return FMHA_ERR_INVALID_ARG;
+    if (format != FMHA_MX_FP8_E4M3 && format != FMHA_MX_FP4_E2M1) return FMHA_ERR_INVALID_ARG;
+    if (batch <= 0 || n_h <= 0 || T <= 0 || hd <= 0 || n_split <= 0) return FMHA_ERR_INVALID_ARG;
+    if (!hd_supported(hd)) return FMHA_ERR_UNSUPPORTED;
+    if (!aligned16(o_part) || !aligned16(lse_part) || !aligned16(o_codes) || (lse && !aligned16(lse)))
+        return FMHA_ERR_ALIGNMENT;
+    MergeParams p{};
+    p.o_part = o_part;
+    p.lse_part = lse_part;
+    p.lse = lse;
+    p.out_format = format;
+    p.o_codes = static_cast<uint8_t *>(o_codes);
+    p.o_scales = static_cast<uint8_t *>(o_scales);
+    return launch_merge(p, batch, n_h, T, hd, n_split, stream);
 }
 
 int fmha_attention_plan(int batch, int n_h, int n_kv_h, int T, int s_k, int hd, fmha_strides k_st,

@@ -13,6 +13,7 @@
 #pragma once
 
 #include "device_common.hpp"
+#include "mx_quant.hpp"
 
 namespace fmha {
 
@@ -23,6 +24,9 @@ struct MergeParams {
     float *lse;             // [b][n_h][T], may be null
     int64_t o_sb, o_st, o_sh;
     int n_h, T, rows, n_split;
+    int out_format;         // OutFormat: bf16 o, or MX codes + scales
+    uint8_t *o_codes;       // MX: dense [b][T][n_h][hd] (E4M3) or [..][hd / 2] (E2M1)
+    uint8_t *o_scales;      // MX: dense [b][T][n_h][hd / 32]
 };
 
 // One row per workgroup: 256 / (HD/4) partition groups (16, 8, 4, 2 for hd
@@ -122,10 +126,19 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     const int h = bh % p.n_h;
     const int b = bh / p.n_h;
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    uint2 packed;
-    packed.x = (uint32_t)bf16_bits(acc[0] * inv) | ((uint32_t)bf16_bits(acc[1] * inv) << 16);
-    packed.y = (uint32_t)bf16_bits(acc[2] * inv) | ((uint32_t)bf16_bits(acc[3] * inv) << 16);
-    *reinterpret_cast<uint2 *>(p.o + (int64_t)b * p.o_sb + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + col) = packed;
+    if (p.out_format != kOutBf16) {
+        // a 32-column block is held by 8 adjacent lanes (TPR is a multiple of 8)
+        const int64_t orow = ((int64_t)b * p.T + t) * p.n_h + h;
+        const float v[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+        mx_store_block_8lanes(v, p.out_format, p.o_codes + orow * (p.out_format == kOutMxFp8E4M3 ? HD : HD / 2),
+                              p.o_scales + orow * (HD / 32), col & ~31, lane_c & 7);
+    } else {
+        uint2 packed;
+        packed.x = (uint32_t)bf16_bits(acc[0] * inv) | ((uint32_t)bf16_bits(acc[1] * inv) << 16);
+        packed.y = (uint32_t)bf16_bits(acc[2] * inv) | ((uint32_t)bf16_bits(acc[3] * inv) << 16);
+        *reinterpret_cast<uint2 *>(p.o + (int64_t)b * p.o_sb + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + col) =
+            packed;
+    }
     if (col == 0 && p.lse != nullptr) p.lse[row] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
 }
 

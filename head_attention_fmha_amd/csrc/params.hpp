@@ -27,6 +27,9 @@ struct FwdParams {
     int n_units;      // gridDim.x
     int xcd_remap;    // 1: n_units % 8 == 0, give each XCD a contiguous unit range
     float scale_log2; // scale * log2(e)
+    int out_format;   // forward mode: OutFormat (bf16 o, or MX codes + scales)
+    uint8_t *o_codes;  // MX: [b][T][n_h][hd] E4M3 or [..][hd / 2] E2M1 pairs, dense
+    uint8_t *o_scales; // MX: [b][T][n_h][hd / 32] E8M0, dense
 };
 
 }  // namespace fmha

@@ -201,6 +201,40 @@ int fmha_lse_merge(const float *o_part, const float *lse_part, void *o, float *l
                    fmha_strides o_st, void *stream);
 
 /*
+ * Output in an OCP microscaling (MX) format instead of bf16: the output
+ * quantisation step the pages attach to the attention epilogue (the FP4 pack
+ * slot of the one-way epilogue on CURRENT_ISSUE.md; the NVFP4 quantiser and
+ * its round-to-nearest-even thresholds in the commit log at 593bc25a), in
+ * the MX formats of this hardware.  Each block of 32 consecutive head-dim
+ * columns of an output row shares one E8M0 scale 2^X with
+ * X = floor(log2 max|o|) - emax (emax = 8 for E4M3, 2 for E2M1), clamped to
+ * [-127, 127] (-127 for an all-zero block); every element o / 2^X is rounded
+ * to nearest, ties to even, saturating at 448 (E4M3) or 6 (E2M1).
+ *   FMHA_MX_FP8_E4M3: one byte per element, sign | exponent (bias 7) |
+ *                     3 mantissa bits (exponent field 0: subnormals)
+ *   FMHA_MX_FP4_E2M1: sign | exponent (bias 1) | 1 mantissa bit, two per
+ *                     byte, the lower column in the low nibble
+ * Layouts (dense, caller-owned device memory):
+ *   o_codes  [batch][T][n_h][hd]      (E4M3) or [batch][T][n_h][hd / 2] (E2M1),
+ *            16-byte aligned
+ *   o_scales [batch][T][n_h][hd / 32] E8M0 codes (X + 127)
+ */
+enum { FMHA_MX_FP8_E4M3 = 1, FMHA_MX_FP4_E2M1 = 2 };
+
+/* fmha_forward with MX output; lse as in fmha_forward.  Errors: as
+ * fmha_forward; FMHA_ERR_INVALID_ARG for a null o_codes / o_scales or an
+ * unknown format. */
+int fmha_forward_mx(const void *q, const void *k, const void *v, void *o_codes, void *o_scales, float *lse,
+                    int batch, int n_h, int n_kv_h, int T, int s_k, int hd,
+                    fmha_strides q_st, fmha_strides k_st, fmha_strides v_st,
+                    float scale, int window, int causal, int format, void *stream);
+
+/* fmha_lse_merge with MX output.  Errors: as fmha_lse_merge;
+ * FMHA_ERR_INVALID_ARG for a null o_codes / o_scales or an unknown format. */
+int fmha_lse_merge_mx(const float *o_part, const float *lse_part, void *o_codes, void *o_scales, float *lse,
+                      int batch, int n_h, int T, int hd, int n_split, int format, void *stream);
+
+/*
  * How fmha_forward (split_len = 0) or fmha_decode_splitkv (split_len > 0)
  * would run a call of these sizes: a host-only query that launches nothing
  * and needs no device, for diagnostics and tests that must reach every

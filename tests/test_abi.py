@@ -31,7 +31,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fmha_attention_plan", "fmha_decode_splitkv", "fmha_decode_splitkv_segment",
-                                    "fmha_forward", "fmha_forward_varlen", "fmha_lse_merge", "fmha_status_string"]
+                                    "fmha_forward", "fmha_forward_mx", "fmha_forward_varlen", "fmha_lse_merge",
+                                    "fmha_lse_merge_mx", "fmha_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -201,3 +202,23 @@ def test_variant_shapes_reach_every_kernel(lib, hd):
         plan = fa.fmha_attention_plan(*dims, hd, window=window, causal=causal, split_len=split_len)
         seen.add(VS.branch(plan))
     assert seen == VS.EXPECTED[hd]
+
+
+def fwd_mx(lib, codes=OP, scales=ctypes.c_void_p(0x70000), fmt=1, hd=128, T=4, s_k=64):
+    st_q = dense(T, 8, hd)
+    st_k = dense(s_k, 2, hd)
+    return lib.fmha_forward_mx(QP, KP, VP, codes, scales, LP, 2, 8, 2, T, s_k, hd, st_q, st_k, st_k, 0.1, 0, 1,
+                               fmt, None)
+
+
+def merge_mx(lib, codes=OP, scales=ctypes.c_void_p(0x70000), fmt=2, hd=128, n_split=4):
+    return lib.fmha_lse_merge_mx(QP, KP, codes, scales, None, 2, 8, 1, hd, n_split, fmt, None)
+
+
+@pytest.mark.parametrize("call", [fwd_mx, merge_mx])
+@pytest.mark.parametrize("kw,code", [
+    (dict(codes=None), INVALID), (dict(scales=None), INVALID), (dict(fmt=0), INVALID), (dict(fmt=3), INVALID),
+    (dict(hd=96), UNSUPPORTED), (dict(codes=ctypes.c_void_p(0x50008)), ALIGN),
+])
+def test_mx_entry_points_reject(lib, call, kw, code):
+    assert call(lib, **kw) == code

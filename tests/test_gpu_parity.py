@@ -510,3 +510,114 @@ def test_ragged_decode_full_size_sampled_rows():
         L = int(lens[r])
         o_ref, lse_ref = oracle.attention(q[r:r + 1].cpu(), k[r:r + 1, :L].cpu(), v[r:r + 1, :L].cpu(), w.scale)
         check_attention(o[r:r + 1], lse[r:r + 1], o_ref, lse_ref, what=f"{w.name} row {r} ({L} keys)")
+
+
+# ---------------------------------------------------------------------------
+# MX output (FP8 E4M3 / FP4 E2M1 codes with E8M0 block scales)
+# ---------------------------------------------------------------------------
+
+from oracle import mx as MX  # noqa: E402
+
+MX_FORMATS = [(fa.MX_FP8_E4M3, MX.FP8_E4M3), (fa.MX_FP4_E2M1, MX.FP4_E2M1)]
+
+
+def mx_buffers(b, T, n_h, hd, fmt):
+    cs, ss = fa.mx_shapes(b, T, n_h, hd, fmt)
+    return (torch.full(cs, 0xAB, dtype=torch.uint8, device=DEV), torch.full(ss, 0xAB, dtype=torch.uint8, device=DEV))
+
+
+@pytest.mark.parametrize("fmt,ofmt", MX_FORMATS, ids=["fp8", "fp4"])
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+@pytest.mark.parametrize("name,dims,split_len,causal,window", [s for s in VS.SHAPES if s[2] == 0],
+                         ids=[s[0] for s in VS.SHAPES if s[2] == 0])
+def test_mx_forward_codes_are_the_quantised_fp32_output(name, dims, split_len, causal, window, hd, fmt, ofmt):
+    """The MX epilogue's codes equal the oracle quantiser applied to the very
+    fp32 values the kernel divides out -- read back through a one-partition
+    split call, which runs the same kernel variant and stores those values.
+    Quantising an fp32 value is exact in fp64, so the match is bit-exact; the
+    fp32 values themselves are checked against the oracle's attention."""
+    b, n_h, n_kv_h, T, s_k = dims
+    seed = 600 + hd + len(name)
+    q = I.randn_bf16((b, T, n_h, hd), seed).to(DEV)
+    k = I.randn_bf16((b, s_k, n_kv_h, hd), seed + 1).to(DEV)
+    v = I.randn_bf16((b, s_k, n_kv_h, hd), seed + 2).to(DEV)
+    scale = 1.0 / math.sqrt(hd)
+    plan_f = fa.fmha_attention_plan(b, n_h, n_kv_h, T, s_k, hd, window=window, causal=causal)
+    plan_s = fa.fmha_attention_plan(b, n_h, n_kv_h, T, s_k, hd, window=window, causal=causal, split_len=s_k)
+    assert plan_f == plan_s
+    o_part = nan_f32(b, n_h, T, 1, hd)
+    lse_part = nan_f32(b, n_h, T, 1)
+    fa.fmha_decode_splitkv(q, k, v, o_part, lse_part, split_len=s_k, scale=scale, window=window, causal=causal)
+    codes, scales = mx_buffers(b, T, n_h, hd, fmt)
+    lse = nan_f32(b, n_h, T)
+    fa.fmha_forward_mx(q, k, v, codes, scales, lse, fmt=fmt, scale=scale, window=window, causal=causal)
+    torch.cuda.synchronize()
+    o32 = o_part[:, :, :, 0].permute(0, 2, 1, 3).cpu().double()          # [b, T, n_h, hd]
+    want_c, want_s = MX.quantize(o32, ofmt)
+    assert torch.equal(scales.cpu(), want_s), "block scales differ"
+    assert torch.equal(codes.cpu(), want_c), "element codes differ"
+    assert torch.equal(lse.cpu(), lse_part[..., 0].cpu())
+    o_ref, lse_ref = oracle.attention(q.cpu(), k.cpu(), v.cpu(), scale, causal=causal, window=window)
+    check_attention(o32, lse, o_ref, lse_ref, what=f"{name} fp32 output")
+
+
+@pytest.mark.parametrize("fmt,ofmt", MX_FORMATS, ids=["fp8", "fp4"])
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+def test_mx_merge_codes(hd, fmt, ofmt):
+    """The merge's MX epilogue on partials whose merge is exact (one live
+    partition of weight 1, the others empty): the codes are the oracle
+    quantiser applied to that partition's values."""
+    b, n_h, T, ns = 3, 5, 2, 4
+    o_part = I.rand_f32((b, n_h, T, ns, hd), seed=hd, lo=-3.0, hi=3.0)
+    o_part *= torch.exp(I.rand_f32((b, n_h, T, 1, 1), seed=hd + 1, lo=-8.0, hi=8.0))   # spread the block scales
+    lse_part = torch.full((b, n_h, T, ns), -math.inf)
+    lse_part[..., 2] = I.rand_f32((b, n_h, T), seed=hd + 2, lo=-5.0, hi=5.0)
+    o_part[..., 0, :] = float("nan")                                  # empty partitions carry no weight
+    codes, scales = mx_buffers(b, T, n_h, hd, fmt)
+    lse = nan_f32(b, n_h, T)
+    fa.fmha_lse_merge_mx(o_part.to(DEV), lse_part.to(DEV), codes, scales, lse, fmt=fmt)
+    torch.cuda.synchronize()
+    want_c, want_s = MX.quantize(o_part[..., 2, :].permute(0, 2, 1, 3).double(), ofmt)
+    assert torch.equal(scales.cpu(), want_s)
+    assert torch.equal(codes.cpu(), want_c)
+    assert (lse.cpu() - lse_part[..., 2]).abs().max().item() <= 1e-5
+
+
+@pytest.mark.parametrize("fmt,ofmt", MX_FORMATS, ids=["fp8", "fp4"])
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 50)])
+def test_mx_constant_v_rows_give_their_own_codes(hd, fmt, ofmt, causal, window):
+    """V rows all equal to one vector c that the format holds exactly (block
+    maxima 1.5 * 2^k, away from any scale boundary): attention returns c,
+    and the MX output is exactly the oracle's codes of c, through the
+    forward and the split + merge paths."""
+    b, T, n_h, s_k = 2, 5, 4, 300
+    g = torch.Generator().manual_seed(hd + fmt)
+    emax = 8 if ofmt == MX.FP8_E4M3 else 2
+    nblk = hd // 32
+    max_code = 0x7C if ofmt == MX.FP8_E4M3 else 5          # magnitudes up to 1.5 * 2^emax
+    el = torch.randint(0, max_code + 1, (b, nblk, 32), generator=g)
+    el[..., 7] = max_code                                   # the block maximum: 1.5 * 2^emax
+    sign = torch.randint(0, 2, (b, nblk, 32), generator=g)
+    vals = torch.where(el == 0, torch.zeros((), dtype=torch.float64), MX.element_values(el, ofmt) * (1 - 2 * sign))
+    xs = torch.randint(-4, 5, (b, nblk, 1), generator=g)
+    c = torch.ldexp(vals, xs.double()).reshape(b, hd)       # exactly representable in bf16 as well
+    v = c.to(torch.bfloat16).reshape(b, 1, 1, hd).expand(b, s_k, 1, hd).contiguous()
+    assert torch.equal(v[:, 0, 0].double(), c)
+    q = I.randn_bf16((b, T, n_h, hd), 5, sigma=2.0)
+    k = I.randn_bf16((b, s_k, 1, hd), 6, sigma=2.0)
+    want_c, want_s = MX.quantize(c.reshape(b, 1, 1, hd).expand(b, T, n_h, hd), ofmt)
+    codes, scales = mx_buffers(b, T, n_h, hd, fmt)
+    fa.fmha_forward_mx(q.to(DEV), k.to(DEV), v.to(DEV), codes, scales, fmt=fmt, scale=1.0 / math.sqrt(hd),
+                       window=window, causal=causal)
+    ns = fa.n_split_for(s_k, 64)
+    o_part = nan_f32(b, n_h, T, ns, hd)
+    lse_part = nan_f32(b, n_h, T, ns)
+    fa.fmha_decode_splitkv(q.to(DEV), k.to(DEV), v.to(DEV), o_part, lse_part, split_len=64,
+                           scale=1.0 / math.sqrt(hd), window=window, causal=causal)
+    codes_m, scales_m = mx_buffers(b, T, n_h, hd, fmt)
+    fa.fmha_lse_merge_mx(o_part, lse_part, codes_m, scales_m, fmt=fmt)
+    torch.cuda.synchronize()
+    for cd, sc, path in ((codes, scales, "forward"), (codes_m, scales_m, "split + merge")):
+        assert torch.equal(sc.cpu(), want_s), path
+        assert torch.equal(cd.cpu(), want_c), path
