@@ -16,6 +16,8 @@ Also reported on the same line:
                 merge) on the host cores, as KV-read GB/s.
   ragged_decode the same decode shapes with per-row key counts uniform on
                 1..8192 (split + merge), as GB/s of the K/V actually read.
+  mx_output     the largest causal prefill point with MX-coded output
+                (FP8 E4M3 and FP4 E2M1 with E8M0 block scales).
   prefill       the largest causal MHA prefill point, the sliding-window
                 MQA prefill and a long causal GQA prefill (T = s_k = 4096):
                 fused-kernel TFLOP/s (algorithmic flops) against the dense
@@ -247,6 +249,35 @@ def run_prefill(torch, fa, I):
     return out
 
 
+def run_mx_output(torch, fa, I):
+    """The largest causal MHA prefill point with the output written as MX
+    codes (FP8 E4M3, FP4 E2M1) instead of bf16, each timed like the prefill
+    lines (graph replays over rotated replicas)."""
+    w = I.mha_causal_prefill(128, 512, 512)
+    flops, _ = prefill_work(w)
+    foot = 2 * (w.batch * w.T * w.n_h * w.hd * 2) + 2 * (w.batch * w.s_k * w.n_kv_h * w.hd * 2)
+    reps = max(1, min(64, math.ceil(512 * 2**20 / foot)))
+    q, k, v = I.make_qkv(w, device="cuda")
+    ins = [(q, k, v) if r == 0 else (q.clone(), k.clone(), v.clone()) for r in range(reps)]
+    out = []
+    for fmt, name in ((fa.MX_FP8_E4M3, "mxfp8_e4m3"), (fa.MX_FP4_E2M1, "mxfp4_e2m1")):
+        cs, ss = fa.mx_shapes(w.batch, w.T, w.n_h, w.hd, fmt)
+        bufs = [(x, torch.empty(cs, dtype=torch.uint8, device="cuda"),
+                 torch.empty(ss, dtype=torch.uint8, device="cuda")) for x in ins]
+
+        def mk(bf, fmt=fmt):
+            return lambda: fa.fmha_forward_mx(bf[0][0], bf[0][1], bf[0][2], bf[1], bf[2], fmt=fmt, scale=w.scale,
+                                              causal=True, stream=torch.cuda.current_stream())
+        us = graph_time_us(torch, [mk(bf) for bf in bufs], reps=max(3, 200 // reps))
+        out.append({"workload": w.name, "format": name, "us_per_call": round(us, 2),
+                    "tflops": round(flops / (us * 1e-6) / 1e12, 1)})
+        log(f"mx output {name} {w.name}: {us:.2f} us")
+        del bufs
+    del ins, q, k, v
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_cpu_baseline(res, seconds):
     import oracle
     w = res["w"]
@@ -313,6 +344,7 @@ def main():
         calibrate_copy()
     ragged = run_ragged_decode(args, torch, fa, I)
     prefill = None if args.no_prefill else run_prefill(torch, fa, I)
+    mx_out = None if args.no_prefill else run_mx_output(torch, fa, I)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(res, args.cpu_seconds)
     w = res["w"]
     split_us = res["split_ms"] * 1e3
@@ -343,6 +375,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": prefill,
         "ragged_decode": ragged,
+        "mx_output": mx_out,
     }
     print(json.dumps(line), flush=True)
 
