@@ -124,22 +124,27 @@ def run_decode(args, torch, fa, I):
         merge()
     torch.cuda.synchronize()
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    evs = [(E(), E(), E()) for _ in range(args.steps)]
+    # the timed steps: nothing but the two launches between the two events
     t0, t1 = E(), E()
-    torch.cuda.synchronize()
     t0.record(stream)
+    for _ in range(args.steps):
+        split()
+        merge()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    # per-kernel durations from events around each launch, in a second pass
+    # (the events themselves add a few microseconds per step)
+    evs = [(E(), E(), E()) for _ in range(args.steps)]
     for a, b, c in evs:
         a.record(stream)
         split()
         b.record(stream)
         merge()
         c.record(stream)
-    t1.record(stream)
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
     split_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / args.steps
     merge_ms = sum(b.elapsed_time(c) for _, b, c in evs) / args.steps
-    ms_per_step = total_ms / args.steps
     kv_bytes, split_bytes, merge_bytes = decode_bytes(w)
     log(f"decode: {ms_per_step * 1e3:.1f} us/step (split {split_ms * 1e3:.1f} us, merge {merge_ms * 1e3:.1f} us)")
     res = {
