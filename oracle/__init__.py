@@ -23,7 +23,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fmha_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# FMHA_ORACLE_LIB names another build of fmha_oracle.c to load instead (the
+# mutation tests use it to check that the pins catch planted mistakes)
+_LIB_PATH = os.environ.get("FMHA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _I64x3 = ctypes.c_int64 * 3

@@ -434,3 +434,15 @@ def test_merge_over_segments_equals_attention_over_their_union(split_a, split_b)
     o_u, lse_u = oracle.attention(qa, torch.cat([ka, kb], dim=1), torch.cat([va, vb], dim=1), 0.4)
     assert (o.permute(0, 2, 1, 3) - o_u).abs().max().item() < 1e-13
     assert (lse - lse_u).abs().max().item() < 1e-13
+
+
+def test_merge_ignores_whatever_an_empty_partition_holds():
+    """A partition with lse = -inf has no visible key: it carries zero weight
+    even when its O slot holds garbage (NaN or huge values)."""
+    o_part = torch.tensor([[[1.0, 2.0], [float("nan"), 1e300], [3.0, -1.0]]], dtype=torch.float64)
+    lse_part = torch.tensor([[0.5, -math.inf, -0.25]], dtype=torch.float64)
+    o, lse = oracle.merge(o_part, lse_part)
+    o2, lse2 = oracle.merge(o_part[:, [0, 2]], lse_part[:, [0, 2]])
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    w0, w2 = math.exp(0.5), math.exp(-0.25)
+    assert abs(o[0, 0].item() - (w0 * 1.0 + w2 * 3.0) / (w0 + w2)) < 1e-15
