@@ -90,6 +90,14 @@ constexpr int kComputeUnits = 256;
 // (64 or 128 columns per wave).
 int head_parts(int hd) { return hd <= 128 ? 1 : hd / 128; }
 
+// Positions a 16-row tile can span: rows are numbered t * group + head and
+// tiles start at multiples of 16.
+int tile_positions(int group) {
+    if (16 % group == 0) return 16 / group;
+    if (group % 16 == 0) return 1;
+    return 15 / group + 2;
+}
+
 // Row-parallel kernel: keys per LDS chunk.  Used up to hd 256: at 512 the
 // full-width Q and output tiles crowd one wave's registers and the per-wave
 // kernel is faster.
@@ -102,9 +110,10 @@ fmha_plan plan_attention(const FwdParams &p, int hd) {
     fmha_plan pl{};
     // the widest key range any 16-row tile can see
     int span = p.split_len < p.s_k ? p.split_len : p.s_k;
-    // causal + window: a tile's rows span at most 16 positions, so at most
-    // window + 15 keys are visible to any of them
-    if (p.causal && p.window > 0 && p.window + 15 < span) span = p.window + 15;
+    // causal + window: a tile's rows span at most tile_positions() positions,
+    // so at most window + positions - 1 keys are visible to any of them
+    const int ppt = tile_positions(p.group);
+    if (p.causal && p.window > 0 && (int64_t)p.window + ppt - 1 < span) span = p.window + ppt - 1;
     // too few 16-row units to give every compute unit two workgroups, at head
     // dims whose four waves hold only one or two key groups, and keys enough
     // for several slices per wave even with eight: eight waves per workgroup,

@@ -166,7 +166,8 @@ def test_merge_rejects(lib, kw, code):
     ((4, 32, 32, 32, 512, 128), dict(causal=True), (4, 1, 0, 0, 256)),
     # single-head decode
     ((1, 1, 1, 1, 128, 64), {}, (4, 1, 1, 1, 1)),
-    # sliding window MQA prefill: span window + 15 = 143 keys > 2 x 32
+    # sliding window MQA prefill: a 16-row tile is one position (16 heads) and
+    # sees 128 keys, more than one pass of the eight waves' two key groups
     ((2, 16, 1, 128, 4096, 512), dict(causal=True, window=128), (8, 1, 0, 0, 256)),
 ])
 def test_plan_of_each_workload(lib, args, kw, want):

@@ -15,6 +15,8 @@ SHAPES = [
     ("row-parallel-gqa", (4, 64, 32, 100, 300), 0, True, 0),
     ("row-parallel-window", (4, 64, 64, 100, 300), 0, True, 70),
     ("row-parallel-two-tiles", (4, 128, 128, 100, 200), 0, True, 0),
+    ("mqa-short-cache", (2, 32, 1, 1, 100), 0, False, 0),
+    ("window-group7-straddling-tiles", (1, 7, 1, 40, 300), 0, True, 30),
 ]
 
 HEAD_DIMS = (64, 128, 256, 512)
