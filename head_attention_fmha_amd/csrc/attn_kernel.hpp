@@ -154,7 +154,32 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
         r_lo[mt] = p.window > 0 ? max(klo, pos - p.window + 1) : klo;
         if (!row_ok[mt]) r_hi[mt] = r_lo[mt];  // no visible key: the row stays at -inf
     }
+    // keys visible to EVERY valid row of tile mt (wave-uniform): slices inside
+    // need no mask (rows past the end hold Q = 0 and are never stored)
+    int full_lo[MT], full_hi[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int first = row0 + 16 * mt;
+        const int last = min(first + 15, row_last);
+        if (first > row_last) {
+            full_lo[mt] = khi;
+            full_hi[mt] = klo;
+        } else {
+            full_hi[mt] = p.causal ? min(khi, s_k - p.T + first / p.group + 1) : khi;
+            full_lo[mt] = p.window > 0 ? max(klo, s_k - p.T + last / p.group - p.window + 1) : klo;
+        }
+    }
 
+    // LAZY (two-tile workgroups, where the softmax's vector work matters more
+    // than one slice's latency): the running maximum is kept on raw scores,
+    // c = |scale| log2 e is folded into the exponent's fma (a negative scale
+    // flips the sign of Q instead, exact in bf16), the reference maximum
+    // moves only when exceeded by more than 2^8, and the bf16 weight sums
+    // come from an MFMA.  Single-tile workgroups are latency-bound and keep
+    // the eager form, which has the shorter dependency chain per slice.
+    constexpr bool LAZY = !ONE && MT == 2;
+    const float c_scale = fabsf(p.scale_log2);
+    const unsigned q_flip = (LAZY && p.scale_log2 < 0.f) ? 0x80008000u : 0u;
     const int col0 = hp * HDP;  // first head-dim column of this wave
     bf16x8 qf[MT][KSTEPS];      // Q^T B operand: Q[row lr][col0 + 32*s + 8*lg + 0..7]
 #pragma unroll
@@ -162,20 +187,30 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
         const uint16_t *qp = p.q + (int64_t)b * p.q_sb + (int64_t)t_of[mt] * p.q_st + (int64_t)h_of[mt] * p.q_sh +
                              col0 + 8 * lg;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-            qf[mt][s] = row_ok[mt] ? *reinterpret_cast<const bf16x8 *>(qp + 32 * s) : bf16x8{};
+        for (int s = 0; s < KSTEPS; ++s) {
+            u32x4 raw = row_ok[mt] ? *reinterpret_cast<const u32x4 *>(qp + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+            raw ^= q_flip;
+            qf[mt][s] = __builtin_bit_cast(bf16x8, raw);
+        }
     }
 
     f32x4 acc[MT][NB];
+    f32x4 accq[MT];  // LAZY: the bf16 weight sum of row lr, in every element (-> O)
     float m[MT], l[MT], lq[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mt][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accq[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         m[mt] = -INFINITY;  // running max (base 2), equal in the 4 lanes of a row
         l[mt] = 0.f;        // this lane's share of the fp32 sum of weights (-> lse)
-        lq[mt] = 0.f;       // the same over the bf16-rounded weights (-> O)
+        lq[mt] = 0.f;       // eager form: the same over the bf16-rounded weights (-> O)
     }
+    // A operand of ones: one MFMA per slice sums the bf16 weights the PV
+    // product consumes, already complete in every lane of the row
+    bf16x8 ones;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ones[j] = (__bf16)1.0f;
 
     const uint16_t *kbase = p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh + col0;
     const uint16_t *vbase = p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh + col0;
@@ -281,6 +316,58 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
         return alpha;
     };
 
+    // ---- LAZY: online softmax of tile mt over a slice.  The
+    // maximum is taken on raw scores (masked keys excluded only in slices that
+    // cut through some row's range); the reference point m moves -- rescaling
+    // the accumulators -- only when some row of the wave exceeds it by more
+    // than 2^8, so weights stay below 256 and most slices rescale nothing.
+    auto softmax_lazy = [&](int mt, int k0, const f32x4 &s0, const f32x4 &s1, bf16x8 &pt) __attribute__((always_inline)) {
+        const bool full = k0 >= full_lo[mt] && k0 + 32 <= full_hi[mt];  // wave-uniform
+        float sv[8];
+        bool vis[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sv[j] = s0[j];
+            sv[4 + j] = s1[j];
+        }
+        float mr = -INFINITY;
+        if (full) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mr = fmaxf(mr, sv[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int key = k0 + 4 * lg + (j & 3) + (j >> 2) * 16;
+                vis[j] = key >= r_lo[mt] && key < r_hi[mt];
+                mr = fmaxf(mr, vis[j] ? sv[j] : -INFINITY);
+            }
+        }
+        mr = fmaxf(mr, xor_shuffle(mr, 16));
+        mr = fmaxf(mr, xor_shuffle(mr, 32));
+        const float mx = mr * c_scale;  // NaN (ignored by fmaxf) for a fully masked row when c = 0
+        if (__any(mx > m[mt] + kRescaleLog2)) {
+            const float m_new = fmaxf(m[mt], mx);
+            const float alpha = fast_exp2(m[mt] - ((m_new == -INFINITY) ? 0.f : m_new));
+            l[mt] *= alpha;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[mt][nb] = acc[mt][nb] * alpha;
+            accq[mt] = accq[mt] * alpha;
+            m[mt] = m_new;
+        }
+        const float neg_m = (m[mt] == -INFINITY) ? 0.f : -m[mt];
+        float psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float xj = fmaf(sv[j], c_scale, neg_m);
+            if (!full) xj = vis[j] ? xj : -INFINITY;
+            const float pj = fast_exp2(xj);
+            pt[j] = to_bf16(pj);
+            psum += pj;
+        }
+        l[mt] += psum;
+        accq[mt] = mfma_16x16x32(ones, pt, accq[mt]);
+    };
+
     // ---- O^T = alpha O^T + V^T . P^T for every tile, from the wave's LDS slice.
     // Item j of lane (lr, lg) is key 4*lg + j (j < 4) or 16 + 4*lg + (j - 4),
     // column 16*nb + lr.  Each half comes from one transposing read
@@ -310,6 +397,8 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
             for (int mt = 0; mt < MT; ++mt) {
                 if constexpr (ONE) {
                     acc[mt][nb] = mfma_16x16x32(vt, pt[mt], f32x4{0.f, 0.f, 0.f, 0.f});
+                } else if constexpr (LAZY) {  // rescaled (if at all) in softmax_lazy
+                    acc[mt][nb] = mfma_16x16x32(vt, pt[mt], acc[mt][nb]);
                 } else {
                     acc[mt][nb] = acc[mt][nb] * alpha[mt];
                     acc[mt][nb] = mfma_16x16x32(vt, pt[mt], acc[mt][nb]);
@@ -369,7 +458,14 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
             bf16x8 pt[MT];
             float alpha[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) alpha[mt] = softmax(mt, k0, s0[mt], s1[mt], pt[mt]);
+            for (int mt = 0; mt < MT; ++mt) {
+                if constexpr (LAZY) {
+                    softmax_lazy(mt, k0, s0[mt], s1[mt], pt[mt]);
+                    alpha[mt] = 1.f;
+                } else {
+                    alpha[mt] = softmax(mt, k0, s0[mt], s1[mt], pt[mt]);
+                }
+            }
             // the previous slice's V^T reads are done before its LDS slice is reused
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 #pragma unroll
@@ -419,8 +515,12 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
     for (int mt = 0; mt < MT; ++mt) {
         l[mt] += xor_shuffle(l[mt], 16);
         l[mt] += xor_shuffle(l[mt], 32);
-        lq[mt] += xor_shuffle(lq[mt], 16);
-        lq[mt] += xor_shuffle(lq[mt], 32);
+        if constexpr (LAZY) {
+            lq[mt] = accq[mt][0];
+        } else {
+            lq[mt] += xor_shuffle(lq[mt], 16);
+            lq[mt] += xor_shuffle(lq[mt], 32);
+        }
     }
 
     // ---- merge the NK key groups of each head part and tile (fixed order) ----------

@@ -22,6 +22,10 @@ typedef unsigned u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned))));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Lazy online softmax: the running maximum moves only when a score exceeds
+// it by more than this (base-2 units), so weights stay below 2^8, far inside
+// bf16 and fp32 range.
+constexpr float kRescaleLog2 = 8.f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ f32x4 mfma_16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {

@@ -28,10 +28,6 @@
 
 namespace fmha {
 
-// The running maximum moves only when a score exceeds it by more than this
-// (base-2 units): weights stay below 2^8, far inside bf16 and fp32 range.
-constexpr float kRescaleLog2 = 8.f;
-
 template <int HD, int RT, int KC>
 struct RowsShape {
     static constexpr int KSTEPS = HD / 32;         // QK MFMA steps
