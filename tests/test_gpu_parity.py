@@ -621,3 +621,69 @@ def test_mx_constant_v_rows_give_their_own_codes(hd, fmt, ofmt, causal, window):
     for cd, sc, path in ((codes, scales, "forward"), (codes_m, scales_m, "split + merge")):
         assert torch.equal(sc.cpu(), want_s), path
         assert torch.equal(cd.cpu(), want_c), path
+
+
+# ---------------------------------------------------------------------------
+# Layout and shape corners of the newer entry points
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("hd", [64, 512])
+def test_more_queries_than_keys_without_mask(hd):
+    """T > s_k is legal without a mask (every query sees every key)."""
+    b, T, n_h, s_k = 2, 40, 4, 7
+    q, k, v = (I.randn_bf16(s, 950 + i) for i, s in enumerate([(b, T, n_h, hd), (b, s_k, 2, hd), (b, s_k, 2, hd)]))
+    o_ref, lse_ref = oracle.attention(q, k, v, 0.1)
+    o, lse = gpu_forward(q, k, v, 0.1)
+    check_attention(o, lse, o_ref, lse_ref, what="T > s_k")
+
+
+@pytest.mark.parametrize("hd", [128, 256])
+def test_varlen_with_strided_layouts(hd):
+    """Ragged batch with BHSD-ordered Q memory, a padded K cache (extra head
+    and columns), V with a larger token stride, and a strided output."""
+    lens = [150, 3, 77]
+    b, T, n_h, n_kv_h, s_max = 3, 9, 8, 2, 150
+    q = I.randn_bf16((b, T, n_h, hd), 960)
+    k = I.randn_bf16((b, s_max, n_kv_h, hd), 961)
+    v = I.randn_bf16((b, s_max, n_kv_h, hd), 962)
+    o_ref, lse_ref = oracle.attention_varlen(q, k, v, lens, 0.07, causal=True)
+    q_bhsd = q.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3)
+    kpad = torch.zeros((b, s_max, n_kv_h + 1, hd + 64), dtype=torch.bfloat16, device=DEV)
+    kpad[:, :, :n_kv_h, :hd] = k.to(DEV)
+    vpad = torch.zeros((b, s_max + 5, n_kv_h, hd), dtype=torch.bfloat16, device=DEV)
+    vpad[:, :s_max] = v.to(DEV)
+    obuf = nan_bf16(b, n_h, T, hd + 16)
+    o_view = obuf[..., :hd].permute(0, 2, 1, 3)
+    lse = nan_f32(b, n_h, T)
+    fa.fmha_forward_varlen(q_bhsd, kpad[:, :, :n_kv_h, :hd], vpad[:, :s_max], torch.tensor(lens, dtype=torch.int32,
+                           device=DEV), o_view, lse, scale=0.07, causal=True)
+    torch.cuda.synchronize()
+    check_attention(o_view, lse, o_ref, lse_ref, what="varlen strided")
+    assert torch.isnan(obuf[..., hd:].float()).all(), "writes outside the output view"
+
+
+@pytest.mark.parametrize("fmt,ofmt", MX_FORMATS, ids=["fp8", "fp4"])
+def test_mx_forward_with_strided_inputs_and_mqa_stride_zero(fmt, ofmt):
+    """MX output from strided Q and from K/V given once with head stride 0:
+    the codes equal those of the same call on dense inputs with one KV head."""
+    b, T, n_h, s_k, hd = 2, 6, 8, 200, 128
+    q = I.randn_bf16((b, T, n_h, hd), 970).to(DEV)
+    k1 = I.randn_bf16((b, s_k, 1, hd), 971).to(DEV)
+    v1 = I.randn_bf16((b, s_k, 1, hd), 972).to(DEV)
+    c1, s1 = mx_buffers(b, T, n_h, hd, fmt)
+    fa.fmha_forward_mx(q, k1, v1, c1, s1, fmt=fmt, causal=True)
+    q_bhsd = q.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    c2, s2 = mx_buffers(b, T, n_h, hd, fmt)
+    fa.fmha_forward_mx(q_bhsd, k1.expand(b, s_k, n_h, hd), v1.expand(b, s_k, n_h, hd), c2, s2, fmt=fmt, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(s1, s2)
+    o_ref, _ = oracle.attention(q.cpu(), k1.cpu(), v1.cpu(), 1.0 / math.sqrt(hd), causal=True)
+    deq = MX.dequantize(c1.cpu(), s1.cpu(), ofmt)
+    # every element within half a step of its block's top binade, or its
+    # saturation gap (the MX rule lets block maxima above vmax * 2^X clip),
+    # plus the bf16-weight error of the fp32 path
+    emax, mbits, vmax = (8, 3, 448.0) if ofmt == MX.FP8_E4M3 else (2, 1, 6.0)
+    x = MX.block_exponents(o_ref, ofmt).repeat_interleave(32, dim=-1).double()
+    half_step = torch.ldexp(torch.full_like(x, 0.5), x + emax - mbits)
+    clip = o_ref.abs() - torch.ldexp(torch.full_like(x, vmax), x)
+    assert torch.all((deq - o_ref).abs() <= torch.maximum(half_step, clip) + 1e-2)
