@@ -310,6 +310,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the ragged decode line (profiler runs of the headline kernel)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only-prefill", action="store_true",
                     help="time only the prefill workloads (for profiler runs); prints no JSON line")
@@ -347,7 +349,7 @@ def main():
     res = run_decode(args, torch, fa, I)
     if args.calibrate_copy:
         calibrate_copy()
-    ragged = run_ragged_decode(args, torch, fa, I)
+    ragged = None if args.no_ragged else run_ragged_decode(args, torch, fa, I)
     prefill = None if args.no_prefill else run_prefill(torch, fa, I)
     mx_out = None if args.no_prefill else run_mx_output(torch, fa, I)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(res, args.cpu_seconds)
