@@ -18,8 +18,8 @@
 //     ds_read_b64_tr_b16, P^T straight from the QK result registers -- the
 //     same transposed-product scheme as attn_kernel.hpp (keys in the MFMA M
 //     dimension, all softmax state of row lr in lanes lr + 16*lg).
-// A tile whose rows see none of a chunk's keys (the causal upper triangle)
-// skips that chunk's products.
+// A wave skips the chunks that none of its rows sees (the causal upper
+// triangle).
 #pragma once
 
 #include "device_common.hpp"
@@ -203,8 +203,10 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
     const int tr_col = 4 * (lr & 3);
 
     // ---- the products of one staged chunk for every tile of this wave.  Each
-    // K operand and each V^T operand read from LDS feeds the MFMAs of all
-    // tiles that see the chunk.
+    // K operand and each V^T operand read from LDS feeds the MFMAs of all the
+    // wave's tiles.  Once any tile sees the chunk, every tile's products are
+    // issued, free of branches (which would split the MFMA/LDS schedule into
+    // small blocks); a tile that sees none of its keys gets weights 0.
     auto compute_chunk = [&](int k0, const unsigned char *sK) __attribute__((always_inline)) {
         const unsigned char *sV = sK + PART_BYTES;
         bool live[RT];  // wave-uniform: does any row of the tile see a key of the chunk?
@@ -228,8 +230,7 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
                 const int slot = (4 * s + lg + rot_of(r)) % CHUNKS;
                 const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(krow + slot * 16);
 #pragma unroll
-                for (int mt = 0; mt < RT; ++mt)
-                    if (live[mt]) sc[mt][kb] = mfma_16x16x32(kf, qf[mt][s], sc[mt][kb]);
+                for (int mt = 0; mt < RT; ++mt) sc[mt][kb] = mfma_16x16x32(kf, qf[mt][s], sc[mt][kb]);
             }
         }
         // ---- online softmax over the chunk's keys, per tile.  The maximum is
@@ -241,7 +242,11 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
         bf16x8 pt[RT][KS];
 #pragma unroll
         for (int mt = 0; mt < RT; ++mt) {
-            if (!live[mt]) continue;
+            if (!live[mt]) {  // weights 0: the tile's products below add nothing
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) pt[mt][ks] = bf16x8{};
+                continue;
+            }
             const bool full = k0 >= full_lo[mt] && k0 + KC <= full_hi[mt];  // wave-uniform
             bool vis[KB][4];
             float mr = -INFINITY;
@@ -304,8 +309,7 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
                 }
                 const bf16x8 vt = __builtin_shufflevector(q2[0], q2[1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-                for (int mt = 0; mt < RT; ++mt)
-                    if (live[mt]) acc[mt][nb] = mfma_16x16x32(vt, pt[mt][ks], acc[mt][nb]);
+                for (int mt = 0; mt < RT; ++mt) acc[mt][nb] = mfma_16x16x32(vt, pt[mt][ks], acc[mt][nb]);
             }
         }
     };
