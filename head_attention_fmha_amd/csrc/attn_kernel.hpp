@@ -114,13 +114,15 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
     // partitions (consecutive key ranges of one KV head; their partial outputs
     // are adjacent in memory), then KV heads and batches.  With several row
     // blocks the units are regrouped so that one XCD (one L2) runs consecutive
-    // ones: blocks are dealt to the 8 XCDs round-robin ------------------------
+    // ones: blocks are dealt to the 8 XCDs round-robin.  Row blocks run last
+    // first: under a causal mask the last rows see the most keys, and starting
+    // the longest units first keeps them out of the tail of the launch -------
     int bid = blockIdx.x;
     if (p.xcd_remap) {
         const int per = p.n_units >> 3;
         bid = (bid & 7) * per + (bid >> 3);
     }
-    const int rb = bid % p.n_row_blocks;
+    const int rb = p.n_row_blocks - 1 - bid % p.n_row_blocks;
     bid /= p.n_row_blocks;
     const int part = bid % p.n_split;
     bid /= p.n_split;

@@ -62,13 +62,14 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
     const int lr = lane & 15;
     const int lg = lane >> 4;
 
-    // ---- work unit (row blocks fastest; regrouped per XCD when they share K/V)
+    // ---- work unit (row blocks fastest, last block first; regrouped per XCD
+    // when they share K/V) -- the same order as attn_kernel.hpp
     int bid = blockIdx.x;
     if (p.xcd_remap) {
         const int per = p.n_units >> 3;
         bid = (bid & 7) * per + (bid >> 3);
     }
-    const int rb = bid % p.n_row_blocks;
+    const int rb = p.n_row_blocks - 1 - bid % p.n_row_blocks;
     bid /= p.n_row_blocks;
     const int part = bid % p.n_split;
     bid /= p.n_split;
