@@ -265,7 +265,9 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
                         buf[((mt * NW + wave) * 8 + 4 + j) * 64 + lane] = s1[mt][j];
                     }
             }
-            __syncthreads();
+            // LDS-only barrier: a full __syncthreads() would also wait for the
+            // next slice's loads already in flight
+            lds_barrier();
             if (active) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
@@ -298,8 +300,7 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
         float mx = x[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-        mx = fmaxf(mx, xor_shuffle(mx, 16));
-        mx = fmaxf(mx, xor_shuffle(mx, 32));
+        mx = row4_max(mx);
         const float m_new = ONE ? mx : fmaxf(m[mt], mx);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = ONE ? 0.f : fast_exp2(m[mt] - m_use);
@@ -344,8 +345,7 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
                 mr = fmaxf(mr, vis[j] ? sv[j] : -INFINITY);
             }
         }
-        mr = fmaxf(mr, xor_shuffle(mr, 16));
-        mr = fmaxf(mr, xor_shuffle(mr, 32));
+        mr = row4_max(mr);
         const float mx = mr * c_scale;  // NaN (ignored by fmaxf) for a fully masked row when c = 0
         if (__any(mx > m[mt] + kRescaleLog2)) {
             const float m_new = fmaxf(m[mt], mx);
@@ -451,12 +451,19 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
                 vr[it] = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)key * p.v_st + v_slot * 8);
             }
         };
-        auto step = [&](int n, const bf16x8 (&kf)[2][KSTEPS], const u32x4 (&vr)[VLOADS]) __attribute__((always_inline)) {
+        // after_qk / after_v: run once this slice's K registers / V registers
+        // are consumed (the caller refills them there)
+        auto step = [&](int n, const bf16x8 (&kf)[2][KSTEPS], const u32x4 (&vr)[VLOADS], auto after_qk,
+                        auto after_v) __attribute__((always_inline)) {
             const int k0 = klo + n * chunk_keys + 32 * kg;
             const bool active = k0 < khi;
             f32x4 s0[MT], s1[MT];
             scores(active, n, kf, s0, s1);
-            if (!active) return;
+            after_qk();
+            if (!active) {
+                after_v();
+                return;
+            }
             bf16x8 pt[MT];
             float alpha[MT];
 #pragma unroll
@@ -476,9 +483,11 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
                 const int slot = (v_slot + rot_of(r)) % CHUNKS;
                 *reinterpret_cast<u32x4 *>(sVw + r * ROW_BYTES + slot * 16) = vr[it];
             }
+            after_v();
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
             pv(alpha, pt);
         };
+        auto nothing = [] {};
         if constexpr (MT == 1 && NW == 4) {
             // two slices per iteration, both loaded up front: the second
             // slice's loads are in flight while the first is computed.  The
@@ -494,20 +503,26 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
                 load_k(klo + (n + 1) * chunk_keys + 32 * kg, kfB);
                 load_v(klo + (n + 1) * chunk_keys + 32 * kg, vrB);
                 __builtin_amdgcn_sched_barrier(0);  // keep all 2 x (K + V) loads ahead of the math
-                step(n, kfA, vrA);
-                if (n + 1 < nslices) step(n + 1, kfB, vrB);
+                step(n, kfA, vrA, nothing, nothing);
+                if (n + 1 < nslices) step(n + 1, kfB, vrB, nothing, nothing);
             }
         } else {
-            // two tiles already double the math per loaded slice, and eight
-            // waves already overlap one another's loads; one slice per
-            // iteration keeps the registers within two waves per SIMD
+            // two tiles already double the math per loaded slice; one slice per
+            // iteration keeps the registers within two waves per SIMD.  The
+            // next slice's K is requested as soon as this slice's QK has
+            // consumed the K registers, so its latency overlaps this slice's
+            // softmax and PV product; V is requested at the top of its own
+            // slice and waited for only before its copy to LDS, after the
+            // softmax.  A load past the range clamps its keys to khi - 1
+            // (valid memory; the last prefetch is never used)
+            bf16x8 kf[2][KSTEPS];
+            if (nslices > 0) load_k(klo + 32 * kg, kf);  // khi > klo >= 0: clamped keys are valid
             for (int n = 0; n < nslices; ++n) {
-                bf16x8 kf[2][KSTEPS];
+                const int k_cur = klo + n * chunk_keys + 32 * kg;
                 u32x4 vr[VLOADS];
-                load_k(klo + n * chunk_keys + 32 * kg, kf);
-                load_v(klo + n * chunk_keys + 32 * kg, vr);
-                __builtin_amdgcn_sched_barrier(0);
-                step(n, kf, vr);
+                load_v(k_cur, vr);
+                step(
+                    n, kf, vr, [&]() __attribute__((always_inline)) { load_k(k_cur + chunk_keys, kf); }, nothing);
             }
         }
     }
@@ -515,13 +530,11 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
     // full row sums over the four lanes of a row
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        l[mt] += xor_shuffle(l[mt], 16);
-        l[mt] += xor_shuffle(l[mt], 32);
+        l[mt] = row4_sum(l[mt]);
         if constexpr (LAZY) {
             lq[mt] = accq[mt][0];
         } else {
-            lq[mt] += xor_shuffle(lq[mt], 16);
-            lq[mt] += xor_shuffle(lq[mt], 32);
+            lq[mt] = row4_sum(lq[mt]);
         }
     }
 

@@ -12,6 +12,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <stdint.h>
 
 namespace fmha {
@@ -39,6 +40,31 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float xor_shuffle(float x, int mask) {
     const int lane = __lane_id();
     return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
+}
+
+// Max / sum over the four lanes lr + 16*lg (lg = 0..3) that hold one row of
+// an MFMA result, on the VALU.  v_permlane16_swap exchanges the odd 16-lane
+// rows of one register with the even rows of another, v_permlane32_swap the
+// upper 32 lanes of one with the lower 32 of another; handed the same value
+// twice, each leaves lane l holding its own value and that of lane l ^ 16
+// (resp. l ^ 32) in its two results.  Both operations are commutative, so
+// the four lanes end with identical bits.
+__device__ __forceinline__ float row4_max(float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const unsigned v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float row4_sum(float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const unsigned v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt

@@ -85,8 +85,7 @@ __device__ __forceinline__ void mx_store_block_4lanes(const float (&v)[8], int f
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    amax = fmaxf(amax, xor_shuffle(amax, 16));
-    amax = fmaxf(amax, xor_shuffle(amax, 32));
+    amax = row4_max(amax);
     const int x = mx_block_exp(amax, mx_emax(fmt));
     mx_store4(v, x, fmt, codes_row, col + 4 * lg);
     mx_store4(v + 4, x, fmt, codes_row, col + 16 + 4 * lg);

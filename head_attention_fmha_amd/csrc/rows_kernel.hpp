@@ -266,8 +266,7 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
                         mr = fmaxf(mr, vis[kb][j] ? sc[mt][kb][j] : -INFINITY);
                     }
             }
-            mr = fmaxf(mr, xor_shuffle(mr, 16));
-            mr = fmaxf(mr, xor_shuffle(mr, 32));
+            mr = row4_max(mr);
             const float mx = mr * c_scale;  // NaN (ignored by fmaxf) for a fully masked row when c = 0
             if (__any(mx > m[mt] + kRescaleLog2)) {
                 const float m_new = fmaxf(m[mt], mx);
@@ -347,8 +346,7 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
     // ---- epilogue: full row sums, one division, lse = (m + log2 l) ln 2 ------
 #pragma unroll
     for (int mt = 0; mt < RT; ++mt) {
-        l[mt] += xor_shuffle(l[mt], 16);
-        l[mt] += xor_shuffle(l[mt], 32);
+        l[mt] = row4_sum(l[mt]);
         if (!row_ok[mt]) continue;
         const int t = t_of[mt], h = h_of[mt];
         const float lq = accq[mt][0];
