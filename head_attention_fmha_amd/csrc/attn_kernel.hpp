@@ -227,7 +227,7 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             const int key = min(k0 + 16 * blk + lr, khi - 1);
-            const uint16_t *kp = kbase + (int64_t)key * p.k_st + 8 * lg;
+            const uint16_t *kp = kbase + key_offset(key, p.k_st) + 8 * lg;
 #pragma unroll
             for (int s = 0; s < KSTEPS; ++s) kf[blk][s] = *reinterpret_cast<const bf16x8 *>(kp + 32 * s);
         }
@@ -245,7 +245,10 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
             s0[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
             s1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        if (active) {
+        // multi-slice work always holds loaded K (keys clamp into the range),
+        // so its products need no branch; an inactive key group's scores are
+        // never used
+        if (!ONE || active) {
 #pragma unroll
             for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
@@ -423,7 +426,7 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
                     const int r = it * KEYS_PER_LOAD + v_row_in_load;
                     const int chunk = (v_slot - rot_of(r) + CHUNKS) % CHUNKS;
                     const int key = min(k0 + r, khi - 1);
-                    load_lds_16<STREAM>(vbase + (int64_t)key * p.v_st + chunk * 8, sVw + it * 64 * 16);
+                    load_lds_16<STREAM>(vbase + key_offset(key, p.v_st) + chunk * 8, sVw + it * 64 * 16);
                 }
                 load_k(k0, kf);
                 __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
@@ -448,7 +451,7 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
 #pragma unroll
             for (int it = 0; it < VLOADS; ++it) {
                 const int key = min(k0 + it * KEYS_PER_LOAD + v_row_in_load, khi - 1);
-                vr[it] = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)key * p.v_st + v_slot * 8);
+                vr[it] = *reinterpret_cast<const u32x4 *>(vbase + key_offset(key, p.v_st) + v_slot * 8);
             }
         };
         // after_qk / after_v: run once this slice's K registers / V registers

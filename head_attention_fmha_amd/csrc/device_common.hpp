@@ -67,6 +67,12 @@ __device__ __forceinline__ float row4_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Element offset of key row `key` (>= 0) for a K/V token stride below 2^32
+// (the host rejects larger ones): a single 32 x 32 -> 64-bit multiply.
+__device__ __forceinline__ int64_t key_offset(int key, int64_t stride) {
+    return (int64_t)((uint64_t)(uint32_t)key * (uint64_t)(uint32_t)stride);
+}
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8; a field at its maximum does not wait).
 constexpr int waitcnt_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }

@@ -27,6 +27,11 @@ bool strides_ok(const fmha_strides &st) {
     return stride_ok(st.batch) && stride_ok(st.token) && stride_ok(st.head);
 }
 
+// K/V rows are addressed with 32 x 32-bit products: token strides below 2^32.
+bool kv_token_strides_ok(const fmha_strides &k_st, const fmha_strides &v_st) {
+    return k_st.token < (1ll << 32) && v_st.token < (1ll << 32);
+}
+
 bool hd_supported(int hd) { return hd == 64 || hd == 128 || hd == 256 || hd == 512; }
 
 // Size limits: keep every row, key and partition index inside int.
@@ -58,6 +63,7 @@ int validate_attention(const void *q, const void *k, const void *v, const void *
         return FMHA_ERR_ALIGNMENT;
     if (!strides_ok(q_st) || !strides_ok(k_st) || !strides_ok(v_st) || (o_st && !strides_ok(*o_st)))
         return FMHA_ERR_ALIGNMENT;
+    if (!kv_token_strides_ok(k_st, v_st)) return FMHA_ERR_UNSUPPORTED;
     return FMHA_OK;
 }
 

@@ -192,8 +192,8 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
 #pragma unroll
             for (int it = 0; it < LOADS; ++it) {
                 const int key = min(k0 + ld_row[it], khi - 1);
-                load_lds_16(kbase + (int64_t)key * p.k_st + ld_col[it] * 8, sK + (wave * LOADS + it) * 1024);
-                load_lds_16(vbase + (int64_t)key * p.v_st + ld_col[it] * 8, sV + (wave * LOADS + it) * 1024);
+                load_lds_16(kbase + key_offset(key, p.k_st) + ld_col[it] * 8, sK + (wave * LOADS + it) * 1024);
+                load_lds_16(vbase + key_offset(key, p.v_st) + ld_col[it] * 8, sV + (wave * LOADS + it) * 1024);
             }
         }
     };

@@ -55,7 +55,8 @@
  *     K/V head stride): the kernels move 16-byte vectors.
  *   - Supported sizes: hd in {64, 128, 256, 512}; 1 <= T <= 2^20;
  *     1 <= s_k <= 2^30; n_h a multiple of n_kv_h with (n_h / n_kv_h) * T
- *     <= 2^30.  With causal or window set, T must not exceed s_k.  Decode
+ *     <= 2^30; K and V token strides below 2^32 elements (key rows are
+ *     addressed with 32-bit products; FMHA_ERR_UNSUPPORTED otherwise).  With causal or window set, T must not exceed s_k.  Decode
  *     (T = 1), short prefill and long prefill (T up to s_k, the prefill the
  *     "Next steps" of CURRENT_ISSUE.md call for) share the entry points.
  */

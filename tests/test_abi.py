@@ -90,6 +90,9 @@ def merge(lib, o_part=QP, lse_part=KP, o=OP, b=2, n_h=8, T=1, hd=128, n_split=4,
     (dict(q_st=FmhaStrides(4 * 8 * 128, 8 * 128 + 4, 128)), ALIGN),
     (dict(k_st=FmhaStrides(64 * 256, 256, 130)), ALIGN),
     (dict(o_st=FmhaStrides(-8, 1024, 128)), ALIGN),
+    # K/V token strides of 2^32 elements or more: rows are addressed with 32-bit products
+    (dict(k_st=FmhaStrides(1 << 40, 1 << 32, 128)), UNSUPPORTED),
+    (dict(v_st=FmhaStrides(1 << 40, (1 << 32) + 8, 128)), UNSUPPORTED),
 ])
 def test_forward_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
