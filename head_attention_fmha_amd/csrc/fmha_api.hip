@@ -104,9 +104,10 @@ int tile_positions(int group) {
     return 15 / group + 2;
 }
 
-// Row-parallel kernel: keys per LDS chunk.  Used up to hd 256: at 512 the
-// full-width Q and output tiles crowd one wave's registers and the per-wave
-// kernel is faster.
+// Row-parallel kernel: keys per LDS chunk for one tile per wave (two tiles
+// per wave take 32: two chunks of scores are live in its pipeline).  Used up
+// to hd 256: at 512 the full-width Q and output tiles crowd one wave's
+// registers and the per-wave kernel is faster.
 constexpr int rows_chunk_keys(int hd) { return hd <= 128 ? 64 : 32; }
 
 // The kernel variant and grid for one call.  A workgroup serves MT 16-row
@@ -177,7 +178,7 @@ void launch_hd(const FwdParams &p, const fmha_plan &pl, hipStream_t s) {
     if (pl.row_parallel) {
         if constexpr (HD <= 256) {
             if (HD <= 128 && pl.tiles_per_group == 8)
-                hipLaunchKernelGGL((fmha::rows_kernel<HD, HD <= 128 ? 2 : 1, rows_chunk_keys(HD), SPLIT>),
+                hipLaunchKernelGGL((fmha::rows_kernel<HD, HD <= 128 ? 2 : 1, 32, SPLIT>),
                                    dim3(p.n_units), dim3(256), 0, s, p);
             else
                 hipLaunchKernelGGL((fmha::rows_kernel<HD, 1, rows_chunk_keys(HD), SPLIT>), dim3(p.n_units), dim3(256),

@@ -9,8 +9,11 @@
 // once per 16*MT rows).  This is the tiled prefill loop of the pages' fused
 // kernel -- Q tile resident, K/V tiles staged on chip, online softmax state
 // in registers -- laid out for CDNA4:
-//   * a chunk travels HBM -> LDS by global_load_lds_dwordx4 (no registers),
-//     double-buffered: chunk n+1 is in flight while chunk n is computed;
+//   * a chunk travels HBM -> LDS by global_load_lds_dwordx4 (no registers)
+//     into one of two K and two V slots; K runs one chunk ahead of V, so the
+//     QK product of chunk n+1 is issued together with the softmax of chunk n
+//     (independent MFMA and vector work in one basic block, which the
+//     hardware overlaps), then chunk n's PV product;
 //   * LDS key row r holds its 16-byte column chunk c at slot
 //     (c + 2*(r mod 8)) mod CHUNKS, for both K and V;
 //   * S^T = K . Q^T with the K A-operand read from LDS (16 bytes per lane),
@@ -18,8 +21,8 @@
 //     ds_read_b64_tr_b16, P^T straight from the QK result registers -- the
 //     same transposed-product scheme as attn_kernel.hpp (keys in the MFMA M
 //     dimension, all softmax state of row lr in lanes lr + 16*lg).
-// A wave skips the chunks that none of its rows sees (the causal upper
-// triangle).
+// A wave computes every chunk of the workgroup's range; keys its rows do not
+// see (the causal diagonal, at most one chunk per wave) get weight 0.
 #pragma once
 
 #include "device_common.hpp"
@@ -36,26 +39,26 @@ struct RowsShape {
     static constexpr int ROW_BYTES = HD * 2;
     static constexpr int KB = KC / 16;             // 16-key blocks per chunk
     static constexpr int KS = KC / 32;             // 32-key PV slices per chunk
-    static constexpr int PART_BYTES = KC * ROW_BYTES;  // K (or V) part of a stage
-    static constexpr int STAGE_BYTES = 2 * PART_BYTES;
-    static constexpr int LOADS = PART_BYTES / (256 * 16);  // 16-byte loads per lane per part
+    static constexpr int PART_BYTES = KC * ROW_BYTES;  // one K (or V) slot
+    static constexpr int LOADS = PART_BYTES / (256 * 16);  // 16-byte loads per lane per slot
     static constexpr int ROWS = 64 * RT;           // rows per workgroup
     static_assert(KC % 32 == 0 && PART_BYTES % (256 * 16) == 0, "whole wave-wide loads");
-    static_assert(2 * STAGE_BYTES <= 160 * 1024, "two stages fit the LDS");
+    static_assert(4 * PART_BYTES <= 64 * 1024, "four slots leave room for two workgroups per CU");
 };
 
 template <int HD, int RT, int KC, bool SPLIT>
-__global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 * 1024 ? 2 : 1)) void rows_kernel(
-    const FwdParams p) {
+__global__ __launch_bounds__(256, 2) void rows_kernel(const FwdParams p) {
     using S = RowsShape<HD, RT, KC>;
     constexpr int KSTEPS = S::KSTEPS, NB = S::NB, CHUNKS = S::CHUNKS, ROW_BYTES = S::ROW_BYTES;
-    constexpr int KB = S::KB, KS = S::KS, PART_BYTES = S::PART_BYTES, STAGE_BYTES = S::STAGE_BYTES;
+    constexpr int KB = S::KB, KS = S::KS, PART_BYTES = S::PART_BYTES;
     constexpr int LOADS = S::LOADS;
-    // two stages as two LDS objects, used alternately by a loop unrolled by
-    // two: the compiler can then tell the prefetch into one stage from the
-    // reads of the other and need not wait for the prefetch before them
-    __shared__ __attribute__((aligned(16))) unsigned char stage0[STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char stage1[STAGE_BYTES];
+    // two K and two V slots as four LDS objects, used in turn by a loop
+    // unrolled by two: the compiler can then tell each prefetch from the
+    // reads of the other slot and need not wait for the prefetch before them
+    __shared__ __attribute__((aligned(16))) unsigned char sK0[PART_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char sK1[PART_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char sV0[PART_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char sV1[PART_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
 
     // ---- this wave's tiles: rows, masks, and the key range of each tile ----
     bool row_ok[RT];
-    int t_of[RT], h_of[RT], r_lo[RT], r_hi[RT], tile_lo[RT], tile_hi[RT], full_lo[RT], full_hi[RT];
+    int t_of[RT], h_of[RT], r_lo[RT], r_hi[RT], full_lo[RT], full_hi[RT];
 #pragma unroll
     for (int mt = 0; mt < RT; ++mt) {
         const int first = row0 + 16 * (wave * RT + mt);
@@ -102,29 +105,28 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
         r_hi[mt] = p.causal ? min(khi, pos + 1) : khi;
         r_lo[mt] = p.window > 0 ? max(klo, pos - p.window + 1) : klo;
         if (!row_ok[mt]) r_hi[mt] = r_lo[mt];
-        // wave-uniform bounds of the keys any row of the tile can see
+        // wave-uniform bounds of the keys visible to EVERY row of the tile:
+        // chunks inside need no mask (an empty tile has none)
         if (first > row_last) {
-            tile_lo[mt] = khi;
-            tile_hi[mt] = klo;  // empty tile
             full_lo[mt] = khi;
             full_hi[mt] = klo;
         } else {
             const int pos_first = s_k - p.T + first / p.group;
             const int pos_last = s_k - p.T + last / p.group;
-            tile_hi[mt] = p.causal ? min(khi, pos_last + 1) : khi;
-            tile_lo[mt] = p.window > 0 ? max(klo, pos_first - p.window + 1) : klo;
-            // keys visible to EVERY row of the tile: chunks inside need no mask
             // (rows past the end of the block hold Q = 0 and are never stored)
             full_hi[mt] = p.causal ? min(khi, pos_first + 1) : khi;
             full_lo[mt] = p.window > 0 ? max(klo, pos_last - p.window + 1) : klo;
         }
     }
 
-    // Scores enter the softmax as s * c with c = |scale| log2 e >= 0: a
+    // Scores enter the softmax as s * c with c = |scale| log2 e > 0: a
     // negative scale flips the sign of Q instead (exact in bf16), so the
     // running maximum can be kept on raw scores and the scaling folded into
-    // the exponent's fma.
-    const float c_scale = fabsf(p.scale_log2);
+    // the exponent's fma.  A zero scale is taken as the smallest normal
+    // float, so that a masked score (-inf) still scales to -inf: scaled
+    // scores then stay below 2^-26 in magnitude for |s| < 2^100 and every
+    // weight rounds to exactly 1, as with the scale 0 itself.
+    const float c_scale = fmaxf(fabsf(p.scale_log2), FLT_MIN);
     const unsigned q_flip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
     bf16x8 qf[RT][KSTEPS];  // Q^T B operand: Q[row lr][32*s + 8*lg + 0..7]
 #pragma unroll
@@ -160,12 +162,12 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
     const uint16_t *vbase = p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh;
     auto rot_of = [](int r) __attribute__((always_inline)) { return (2 * (r & 7)) % CHUNKS; };
 
-    // ---- one chunk HBM -> LDS stage: wave w fills bytes [w*LOADS*1 KiB, ...)
-    // of each part; the lane writing LDS byte x of a part fetches the global
-    // chunk that belongs at x under the rotation.  The lane's row and chunk
-    // are fixed, so its byte offset from the chunk's first key is computed
-    // once; a chunk then costs one scalar base per tensor.  The last chunk
-    // of a range clamps keys past khi to key khi-1 instead.
+    // ---- one chunk HBM -> an LDS slot: wave w fills bytes [w*LOADS*1 KiB, ...)
+    // of the slot; the lane writing LDS byte x fetches the global chunk that
+    // belongs at x under the rotation.  The lane's row and chunk are fixed,
+    // so its byte offset from the chunk's first key is computed once; a
+    // chunk then costs one scalar base per tensor.  The last chunk of a range
+    // clamps keys past khi to key khi-1 instead.
     int ld_row[LOADS], ld_col[LOADS];
     unsigned ld_koff[LOADS], ld_voff[LOADS];
     const bool offsets32 = (int64_t)(KC - 1) * (p.k_st > p.v_st ? p.k_st : p.v_st) * 2 + ROW_BYTES < (1ll << 31);
@@ -177,23 +179,17 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
         ld_koff[it] = (unsigned)(((int64_t)ld_row[it] * p.k_st + ld_col[it] * 8) * 2);
         ld_voff[it] = (unsigned)(((int64_t)ld_row[it] * p.v_st + ld_col[it] * 8) * 2);
     }
-    auto issue_chunk = [&](int k0, unsigned char *stage) __attribute__((always_inline)) {
-        unsigned char *sK = stage;
-        unsigned char *sV = stage + PART_BYTES;
+    auto issue = [&](const uint16_t *base, int64_t st, const unsigned (&off)[LOADS], int k0, unsigned char *slot)
+                     __attribute__((always_inline)) {
         if (offsets32 && k0 + KC <= khi) {  // wave-uniform
-            const char *kc = reinterpret_cast<const char *>(kbase + (int64_t)k0 * p.k_st);
-            const char *vc = reinterpret_cast<const char *>(vbase + (int64_t)k0 * p.v_st);
+            const char *c = reinterpret_cast<const char *>(base + key_offset(k0, st));
 #pragma unroll
-            for (int it = 0; it < LOADS; ++it) {
-                load_lds_16(kc + ld_koff[it], sK + (wave * LOADS + it) * 1024);
-                load_lds_16(vc + ld_voff[it], sV + (wave * LOADS + it) * 1024);
-            }
+            for (int it = 0; it < LOADS; ++it) load_lds_16(c + off[it], slot + (wave * LOADS + it) * 1024);
         } else {
 #pragma unroll
             for (int it = 0; it < LOADS; ++it) {
                 const int key = min(k0 + ld_row[it], khi - 1);
-                load_lds_16(kbase + key_offset(key, p.k_st) + ld_col[it] * 8, sK + (wave * LOADS + it) * 1024);
-                load_lds_16(vbase + key_offset(key, p.v_st) + ld_col[it] * 8, sV + (wave * LOADS + it) * 1024);
+                load_lds_16(base + key_offset(key, st) + ld_col[it] * 8, slot + (wave * LOADS + it) * 1024);
             }
         }
     };
@@ -203,23 +199,9 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
     const int tr_row0 = 4 * lg + (lr >> 2);
     const int tr_col = 4 * (lr & 3);
 
-    // ---- the products of one staged chunk for every tile of this wave.  Each
-    // K operand and each V^T operand read from LDS feeds the MFMAs of all the
-    // wave's tiles.  Once any tile sees the chunk, every tile's products are
-    // issued, free of branches (which would split the MFMA/LDS schedule into
-    // small blocks); a tile that sees none of its keys gets weights 0.
-    auto compute_chunk = [&](int k0, const unsigned char *sK) __attribute__((always_inline)) {
-        const unsigned char *sV = sK + PART_BYTES;
-        bool live[RT];  // wave-uniform: does any row of the tile see a key of the chunk?
-        bool any_live = false;
-#pragma unroll
-        for (int mt = 0; mt < RT; ++mt) {
-            live[mt] = k0 < tile_hi[mt] && k0 + KC > tile_lo[mt];
-            any_live = any_live || live[mt];
-        }
-        if (!any_live) return;
-        // ---- S^T for the chunk: KB blocks of 16 keys
-        f32x4 sc[RT][KB];
+    // ---- S^T of one staged chunk for every tile of this wave: KB blocks of 16
+    // keys; each K operand read from LDS feeds the MFMAs of all the tiles
+    auto qk = [&](const unsigned char *sK, f32x4 (&sc)[RT][KB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int r = 16 * kb + lr;
@@ -234,40 +216,38 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
                 for (int mt = 0; mt < RT; ++mt) sc[mt][kb] = mfma_16x16x32(kf, qf[mt][s], sc[mt][kb]);
             }
         }
-        // ---- online softmax over the chunk's keys, per tile.  The maximum is
-        // taken on raw scores (masked keys excluded only in chunks that cut
-        // through some row's range); the reference point m moves -- rescaling
-        // the accumulators -- only when some row of the wave exceeds it by
-        // more than 2^8, so weights stay below 256 and most chunks rescale
-        // nothing
-        bf16x8 pt[RT][KS];
+    };
+
+    // ---- online softmax, first half: mask, maximum, rescale.  A chunk that
+    // cuts through some row's visible range sets the scores of masked keys
+    // to -inf (weight 0); chunks inside every tile's fully visible range skip
+    // that.  The maximum is taken on raw scores; the reference point m moves
+    // -- rescaling the accumulators -- only when some row of the wave
+    // exceeds it by more than 2^8, so weights stay below 256 and most chunks
+    // rescale nothing.
+    auto prep = [&](int k0, f32x4 (&sc)[RT][KB]) __attribute__((always_inline)) {
+        bool all_full = true;  // wave-uniform
 #pragma unroll
-        for (int mt = 0; mt < RT; ++mt) {
-            if (!live[mt]) {  // weights 0: the tile's products below add nothing
+        for (int mt = 0; mt < RT; ++mt) all_full = all_full && k0 >= full_lo[mt] && k0 + KC <= full_hi[mt];
+        if (!all_full) {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) pt[mt][ks] = bf16x8{};
-                continue;
-            }
-            const bool full = k0 >= full_lo[mt] && k0 + KC <= full_hi[mt];  // wave-uniform
-            bool vis[KB][4];
-            float mr = -INFINITY;
-            if (full) {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) mr = fmaxf(mr, sc[mt][kb][j]);
-            } else {
+            for (int mt = 0; mt < RT; ++mt)
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int key = k0 + 16 * kb + 4 * lg + j;
-                        vis[kb][j] = key >= r_lo[mt] && key < r_hi[mt];
-                        mr = fmaxf(mr, vis[kb][j] ? sc[mt][kb][j] : -INFINITY);
+                        if (key < r_lo[mt] || key >= r_hi[mt]) sc[mt][kb][j] = -INFINITY;
                     }
-            }
-            mr = row4_max(mr);
-            const float mx = mr * c_scale;  // NaN (ignored by fmaxf) for a fully masked row when c = 0
+        }
+#pragma unroll
+        for (int mt = 0; mt < RT; ++mt) {
+            float mr = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) mr = fmaxf(mr, sc[mt][kb][j]);
+            const float mx = row4_max(mr) * c_scale;
             if (__any(mx > m[mt] + kRescaleLog2)) {
                 const float m_new = fmaxf(m[mt], mx);
                 const float alpha = fast_exp2(m[mt] - ((m_new == -INFINITY) ? 0.f : m_new));
@@ -277,15 +257,22 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
                 accq[mt] = accq[mt] * alpha;
                 m[mt] = m_new;
             }
+        }
+    };
+
+    // ---- second half: weights 2^(s c - m) (2^-inf = 0), their bf16 forms for
+    // the PV product, the fp32 sum for lse and the bf16 sum (one MFMA against
+    // the ones operand per 32 keys) for the normalisation
+    auto weights = [&](const f32x4 (&sc)[RT][KB], bf16x8 (&pt)[RT][KS]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < RT; ++mt) {
             const float neg_m = (m[mt] == -INFINITY) ? 0.f : -m[mt];
             float psum = 0.f;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    float xj = fmaf(sc[mt][kb][j], c_scale, neg_m);
-                    if (!full) xj = vis[kb][j] ? xj : -INFINITY;
-                    const float pj = fast_exp2(xj);
+                    const float pj = fast_exp2(fmaf(sc[mt][kb][j], c_scale, neg_m));
                     pt[mt][kb >> 1][(kb & 1) * 4 + j] = to_bf16(pj);
                     psum += pj;
                 }
@@ -293,7 +280,10 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) accq[mt] = mfma_16x16x32(ones, pt[mt][ks], accq[mt]);
         }
-        // ---- O^T += V^T . P^T
+    };
+
+    // ---- O^T += V^T . P^T; each V^T operand read from LDS feeds every tile
+    auto pv = [&](const unsigned char *sV, const bf16x8 (&pt)[RT][KS]) __attribute__((always_inline)) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
@@ -314,33 +304,49 @@ __global__ __launch_bounds__(256, (2 * RowsShape<HD, RT, KC>::STAGE_BYTES <= 64 
         }
     };
 
-    // chunk n+1 is fetched into the other stage while chunk n is computed
-    auto step = [&](int n, int nchunks, unsigned char *cur, unsigned char *next) __attribute__((always_inline)) {
+    // ---- the pipeline.  Step n starts with chunk n+1's K and chunk n's V on
+    // chip and chunk n's scores in registers; it requests chunk n+2's K and
+    // chunk n+1's V into the slots step n-1 finished with, then computes
+    // chunk n+1's scores alongside chunk n's weights, then chunk n's PV
+    // product.  One barrier per step: every wave's loads of the previous step
+    // have landed and every wave is done reading the slots about to be
+    // refilled.  After the last chunk the QK product reads a stale K slot;
+    // those scores are never used.
+    const int nchunks = khi > klo ? (khi - klo + KC - 1) / KC : 0;  // wave-uniform
+    f32x4 sc[RT][KB];
+    if (nchunks > 0) {
+        issue(kbase, p.k_st, ld_koff, klo, sK0);
+        issue(vbase, p.v_st, ld_voff, klo, sV0);
+        if (nchunks > 1) issue(kbase, p.k_st, ld_koff, klo + KC, sK1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        lds_barrier();
+        qk(sK0, sc);
+    }
+    auto step = [&](int n, const unsigned char *sKnext, const unsigned char *sVcur, unsigned char *sKfill,
+                    unsigned char *sVfill) __attribute__((always_inline)) {
         const int k0 = klo + n * KC;
-        if (n + 1 < nchunks) {
-            issue_chunk(k0 + KC, next);
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS));  // this wave's part of chunk n has landed
-        } else {
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        }
-        lds_barrier();  // ... and every wave's part
-        compute_chunk(k0, cur);
-        lds_barrier();  // every wave is done with this stage before it is refilled
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        lds_barrier();
+        if (n + 2 < nchunks) issue(kbase, p.k_st, ld_koff, k0 + 2 * KC, sKfill);
+        if (n + 1 < nchunks) issue(vbase, p.v_st, ld_voff, k0 + KC, sVfill);
+        prep(k0, sc);
+        f32x4 sn[RT][KB];
+        qk(sKnext, sn);
+        bf16x8 pt[RT][KS];
+        weights(sc, pt);
+        pv(sVcur, pt);
+#pragma unroll
+        for (int mt = 0; mt < RT; ++mt)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) sc[mt][kb] = sn[mt][kb];
     };
-
-    // Two chunks per iteration.  Chunk n+2 (fetched during chunk n+1) is
-    // waited for before the back-edge, after chunk n+1's products: no
-    // LDS-direct load crosses the back-edge, which the compiler's wait
-    // placement would otherwise answer with a wait for all loads before the
-    // first LDS read of the iteration -- the prefetch included.
-    const int nchunks = khi > klo ? (khi - klo + KC - 1) / KC : 0;
-    if (nchunks > 0) issue_chunk(klo, stage0);
+    // two steps per iteration (the slots alternate); no LDS-direct load
+    // crosses the back-edge, which the compiler's wait placement would answer
+    // with a wait for all loads before the iteration's first LDS read
     for (int n = 0; n < nchunks; n += 2) {
-        step(n, nchunks, stage0, stage1);
-        if (n + 1 < nchunks) {
-            step(n + 1, nchunks, stage1, stage0);
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        }
+        step(n, sK1, sV0, sK0, sV1);
+        if (n + 1 < nchunks) step(n + 1, sK0, sV1, sK1, sV0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
 
     // ---- epilogue: full row sums, one division, lse = (m + log2 l) ln 2 ------
