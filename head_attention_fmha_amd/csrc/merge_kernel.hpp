@@ -71,7 +71,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
                 const int i = i0 + u * PG;
                 const bool in = i < p.n_split;
                 lv[u] = in ? lp[i] * kLog2e : -INFINITY;
-                ov[u] = in ? *reinterpret_cast<const f32x4 *>(op + (int64_t)i * HD) : f32x4{0.f, 0.f, 0.f, 0.f};
+                // each partial is read once, in whole cache lines: non-temporal
+                ov[u] = in ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(op + (int64_t)i * HD))
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
             }
             float mb = M;
 #pragma unroll
