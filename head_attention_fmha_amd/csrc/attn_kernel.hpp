@@ -348,9 +348,11 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
                 mr = fmaxf(mr, vis[j] ? sv[j] : -INFINITY);
             }
         }
-        mr = row4_max(mr);
-        const float mx = mr * c_scale;  // NaN (ignored by fmaxf) for a fully masked row when c = 0
-        if (__any(mx > m[mt] + kRescaleLog2)) {
+        // a row's maximum exceeds the reference point by more than 2^8 iff one
+        // of its four lanes' maxima does: the row maximum itself (a reduction
+        // across the four lanes) is needed only when the reference moves
+        if (__any(mr * c_scale > m[mt] + kRescaleLog2)) {
+            const float mx = row4_max(mr) * c_scale;  // NaN (ignored by fmaxf) for a fully masked row when c = 0
             const float m_new = fmaxf(m[mt], mx);
             const float alpha = fast_exp2(m[mt] - ((m_new == -INFINITY) ? 0.f : m_new));
             l[mt] *= alpha;

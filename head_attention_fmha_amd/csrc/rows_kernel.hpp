@@ -143,13 +143,14 @@ __global__ __launch_bounds__(256, 2) void rows_kernel(const FwdParams p) {
 
     f32x4 acc[RT][NB];
     f32x4 accq[RT];  // every element: the running sum of row lr's bf16 weights (-> O)
-    float m[RT], l[RT];
+    float m[RT], neg_m[RT], l[RT];
 #pragma unroll
     for (int mt = 0; mt < RT; ++mt) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mt][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
         accq[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         m[mt] = -INFINITY;  // running max (base 2), equal in the 4 lanes of a row
+        neg_m[mt] = 0.f;    // -m, or 0 while m = -inf (every weight is then 0)
         l[mt] = 0.f;        // this lane's share of the fp32 sum of weights (-> lse)
     }
     // A operand of ones: one MFMA per 32-key slice sums the bf16 weights the PV
@@ -247,15 +248,18 @@ __global__ __launch_bounds__(256, 2) void rows_kernel(const FwdParams p) {
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) mr = fmaxf(mr, sc[mt][kb][j]);
-            const float mx = row4_max(mr) * c_scale;
-            if (__any(mx > m[mt] + kRescaleLog2)) {
-                const float m_new = fmaxf(m[mt], mx);
+            // a row's maximum exceeds the reference point by more than 2^8 iff
+            // one of its four lanes' maxima does: the row maximum itself (a
+            // reduction across the four lanes) is needed only when it moves
+            if (__any(mr * c_scale > m[mt] + kRescaleLog2)) {
+                const float m_new = fmaxf(m[mt], row4_max(mr) * c_scale);
                 const float alpha = fast_exp2(m[mt] - ((m_new == -INFINITY) ? 0.f : m_new));
                 l[mt] *= alpha;
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) acc[mt][nb] = acc[mt][nb] * alpha;
                 accq[mt] = accq[mt] * alpha;
                 m[mt] = m_new;
+                neg_m[mt] = (m_new == -INFINITY) ? 0.f : -m_new;
             }
         }
     };
@@ -266,13 +270,12 @@ __global__ __launch_bounds__(256, 2) void rows_kernel(const FwdParams p) {
     auto weights = [&](const f32x4 (&sc)[RT][KB], bf16x8 (&pt)[RT][KS]) __attribute__((always_inline)) {
 #pragma unroll
         for (int mt = 0; mt < RT; ++mt) {
-            const float neg_m = (m[mt] == -INFINITY) ? 0.f : -m[mt];
             float psum = 0.f;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float pj = fast_exp2(fmaf(sc[mt][kb][j], c_scale, neg_m));
+                    const float pj = fast_exp2(fmaf(sc[mt][kb][j], c_scale, neg_m[mt]));
                     pt[mt][kb >> 1][(kb & 1) * 4 + j] = to_bf16(pj);
                     psum += pj;
                 }
