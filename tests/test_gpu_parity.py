@@ -303,6 +303,56 @@ def test_every_kernel_variant(name, dims, split_len, causal, window, hd):
     check_attention(o, lse, o_ref, lse_ref, what=name)
 
 
+@pytest.mark.parametrize("hd", list(VS.HEAD_DIMS))
+@pytest.mark.parametrize("name,dims,split_len,causal,window", VS.SHAPES, ids=[v[0] for v in VS.SHAPES])
+def test_every_kernel_variant_negative_scale(name, dims, split_len, causal, window, hd):
+    """A negative scale (the kernels that keep the running maximum on raw
+    scores flip the sign of Q instead) on every variant, against the oracle."""
+    b, n_h, n_kv_h, T, s_k = dims
+    seed = 1400 + 7 * hd + len(name)
+    q = I.randn_bf16((b, T, n_h, hd), seed)
+    k = I.randn_bf16((b, s_k, n_kv_h, hd), seed + 1)
+    v = I.randn_bf16((b, s_k, n_kv_h, hd), seed + 2)
+    scale = -0.8 / math.sqrt(hd)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=causal, window=window)
+    if split_len:
+        o, lse, _, _ = gpu_split(q, k, v, scale, split_len, causal, window)
+    else:
+        o, lse = gpu_forward(q, k, v, scale, causal, window)
+    check_attention(o, lse, o_ref, lse_ref, what=f"{name} scale {scale:.4f}")
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("dims,tiles", [((4, 64, 64, 64, 150), 4), ((4, 128, 128, 128, 150), 8)],
+                         ids=["one-tile-waves", "two-tile-waves"])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 130)])
+def test_zero_scale_row_parallel(dims, tiles, causal, window, hd):
+    """scale = 0 through the row-parallel kernel (which scales by the smallest
+    normal float instead so that masked scores stay -inf): every visible key
+    gets weight 1, so lse = ln(visible keys) and O = their mean V, closed form."""
+    b, n_h, n_kv_h, T, s_k = dims
+    plan = fa.fmha_attention_plan(b, n_h, n_kv_h, T, s_k, hd, window=window, causal=causal)
+    want_tiles = tiles if hd <= 128 else 4  # two-tile waves only up to hd 128
+    assert plan["row_parallel"] == 1 and plan["tiles_per_group"] == want_tiles, plan
+    seed = 1700 + hd + T
+    q = I.randn_bf16((b, T, n_h, hd), seed)
+    k = I.randn_bf16((b, s_k, n_kv_h, hd), seed + 1)
+    v = I.randn_bf16((b, s_k, n_kv_h, hd), seed + 2)
+    o, lse = gpu_forward(q, k, v, 0.0, causal, window)
+    pos = torch.arange(T) + (s_k - T)
+    hi = (pos + 1) if causal else torch.full((T,), s_k)
+    lo = (pos - window + 1).clamp(min=0) if window else torch.zeros(T, dtype=torch.long)
+    cnt = (hi - lo).double()
+    cs = torch.cat([torch.zeros(b, 1, n_kv_h, hd, dtype=torch.float64), v.double().cumsum(1)], dim=1)
+    mean = (cs[:, hi] - cs[:, lo]) / cnt.view(1, T, 1, 1)          # [b, T, n_kv_h, hd]
+    group = n_h // n_kv_h
+    mean = mean.repeat_interleave(group, dim=2)                    # [b, T, n_h, hd]
+    err = (o.cpu().double() - mean).abs().max().item()
+    lerr = (lse.cpu().double() - cnt.log().view(1, 1, T)).abs().max().item()
+    sys.stderr.write(f"[gpu-case] zero scale: max|O - mean| {err:.2e}, lse err {lerr:.2e}\n")
+    assert err < 1e-2 and lerr < 1e-5
+
+
 # ---------------------------------------------------------------------------
 # Long prefill: T in the thousands, up to T = s_k
 # ---------------------------------------------------------------------------
