@@ -105,9 +105,9 @@ int tile_positions(int group) {
 }
 
 // Row-parallel kernel: keys per LDS chunk for one tile per wave (two tiles
-// per wave take 32: two chunks of scores are live in its pipeline).  Used up
-// to hd 256: at 512 the full-width Q and output tiles crowd one wave's
-// registers and the per-wave kernel is faster.
+// per wave take 32: two chunks of scores are live in its pipeline).  At hd
+// 512 one wave's full-width Q and output tiles fill a SIMD's registers (one
+// wave per SIMD), and the chunk pipeline still beats the per-wave kernel.
 constexpr int rows_chunk_keys(int hd) { return hd <= 128 ? 64 : 32; }
 
 // The kernel variant and grid for one call.  A workgroup serves MT 16-row
@@ -146,14 +146,14 @@ fmha_plan plan_attention(const FwdParams &p, int hd) {
     // workgroup (short prefill); two -- every K operand read from LDS then
     // feeds two MFMAs -- once the grid has two workgroups per compute unit
     // even so (long prefill)
-    if (!pl.one_slice && p.rows >= 64 && hd <= 256) {
+    if (!pl.one_slice && p.rows >= 64) {
         const int64_t per_kv = (int64_t)p.n_split * p.n_kv_h * p.batch;
         const int64_t groups1 = (int64_t)((p.rows + 63) / 64) * per_kv;
         const int64_t groups2 = (int64_t)((p.rows + 127) / 128) * per_kv;
         if (groups1 >= kComputeUnits) {
             pl.row_parallel = 1;
             pl.waves_per_group = 4;
-            // (two tiles of 256 columns would spill: hd 256 keeps one)
+            // (two tiles of 256 or 512 columns would spill: one tile per wave)
             pl.tiles_per_group = (hd <= 128 && groups2 >= 2 * kComputeUnits) ? 8 : 4;
         }
     }
@@ -176,14 +176,12 @@ void launch_kernel(const FwdParams &p, hipStream_t stream) {
 template <int HD, bool SPLIT>
 void launch_hd(const FwdParams &p, const fmha_plan &pl, hipStream_t s) {
     if (pl.row_parallel) {
-        if constexpr (HD <= 256) {
-            if (HD <= 128 && pl.tiles_per_group == 8)
-                hipLaunchKernelGGL((fmha::rows_kernel<HD, HD <= 128 ? 2 : 1, 32, SPLIT>),
-                                   dim3(p.n_units), dim3(256), 0, s, p);
-            else
-                hipLaunchKernelGGL((fmha::rows_kernel<HD, 1, rows_chunk_keys(HD), SPLIT>), dim3(p.n_units), dim3(256),
-                                   0, s, p);
-        }
+        if (HD <= 128 && pl.tiles_per_group == 8)
+            hipLaunchKernelGGL((fmha::rows_kernel<HD, HD <= 128 ? 2 : 1, 32, SPLIT>), dim3(p.n_units), dim3(256), 0, s,
+                               p);
+        else
+            hipLaunchKernelGGL((fmha::rows_kernel<HD, 1, rows_chunk_keys(HD), SPLIT>), dim3(p.n_units), dim3(256), 0,
+                               s, p);
     } else if (pl.waves_per_group == 8) {
         // chosen only for several slices per wave (never one-slice), hd >= 256
         if constexpr (HD >= 256) launch_kernel<HD, 8, 1, SPLIT, false, false>(p, s);

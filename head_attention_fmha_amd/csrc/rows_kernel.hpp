@@ -43,11 +43,13 @@ struct RowsShape {
     static constexpr int LOADS = PART_BYTES / (256 * 16);  // 16-byte loads per lane per slot
     static constexpr int ROWS = 64 * RT;           // rows per workgroup
     static_assert(KC % 32 == 0 && PART_BYTES % (256 * 16) == 0, "whole wave-wide loads");
-    static_assert(4 * PART_BYTES <= 64 * 1024, "four slots leave room for two workgroups per CU");
+    // four slots: 32 or 64 KiB up to hd 256 (two workgroups per CU), 128 KiB
+    // at hd 512 (one; its full-width Q and O tiles fill a SIMD's registers)
+    static_assert(4 * PART_BYTES <= 160 * 1024, "four slots fit the LDS");
 };
 
 template <int HD, int RT, int KC, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void rows_kernel(const FwdParams p) {
+__global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdParams p) {
     using S = RowsShape<HD, RT, KC>;
     constexpr int KSTEPS = S::KSTEPS, NB = S::NB, CHUNKS = S::CHUNKS, ROW_BYTES = S::ROW_BYTES;
     constexpr int KB = S::KB, KS = S::KS, PART_BYTES = S::PART_BYTES;

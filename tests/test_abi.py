@@ -162,8 +162,10 @@ def test_merge_rejects(lib, kw, code):
     ((8, 128, 1, 1, 512, 512), {}, (8, 1, 0, 0, 64)),
     # the same through a head stride of 0 with n_kv_h = n_h: planned as MQA
     ((8, 128, 128, 1, 512, 512), dict(mqa_stride0=True), (8, 1, 0, 0, 64)),
-    # causal prefill T = 128, s_k = 512: two tiles per workgroup
-    ((4, 32, 32, 128, 512, 512), dict(causal=True), (4, 2, 0, 0, 512)),
+    # causal prefill T = 128, s_k = 512, hd 512: the row-parallel kernel, 64 rows
+    # per workgroup (two per KV head); at hd 128 the same with 256 units
+    ((4, 32, 32, 128, 512, 512), dict(causal=True), (4, 4, 0, 0, 256)),
+    ((4, 32, 32, 128, 512, 128), dict(causal=True), (4, 4, 0, 0, 256)),
     # causal prefill T = 32: 256 units, eight waves at hd 256 and 512 only
     ((4, 32, 32, 32, 512, 256), dict(causal=True), (8, 1, 0, 0, 256)),
     ((4, 32, 32, 32, 512, 128), dict(causal=True), (4, 1, 0, 0, 256)),

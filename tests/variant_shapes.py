@@ -41,5 +41,6 @@ EXPECTED = {
           "multi-two-tiles"},
     256: {"row-parallel", "eight-waves", "one-slice-streamed", "one-slice-shared", "multi-one-tile",
           "multi-two-tiles"},
-    512: {"eight-waves", "one-slice-streamed", "one-slice-shared", "multi-one-tile", "multi-two-tiles"},
+    512: {"row-parallel", "eight-waves", "one-slice-streamed", "one-slice-shared", "multi-one-tile",
+          "multi-two-tiles"},
 }
