@@ -62,8 +62,35 @@ __device__ __forceinline__ unsigned mx_e2m1(float v) {
     return sign | code;
 }
 
+typedef short mx_short2 __attribute__((ext_vector_type(2)));
+
 // Codes of four consecutive columns, scaled by 2^-x: FP8 -> 4 bytes, FP4 -> 2.
+// While 2^x is a normal float, gfx950's scaled conversions do it in hardware
+// (v_cvt_scalef32_pk_fp8_f32 / _fp4_f32: element v / 2^x, rounded to nearest
+// even; FP4 saturates at 6).  The FP8 conversion gives NaN instead of
+// saturating, so its inputs are first clamped to +-448 * 2^x, the largest
+// finite code (448 itself, or a value that rounds to it, is unchanged).  The
+// code and packing (lower column in the low byte or nibble) were checked
+// against the fp64 quantiser on the device.  2^-127 (all-zero blocks, or
+// outputs below 2^-118) takes the arithmetic path.
 __device__ __forceinline__ void mx_store4(const float *v, int x, int fmt, uint8_t *codes_row, int col) {
+    if (x > -127) {
+        const float s = __uint_as_float((unsigned)(x + 127) << 23);  // 2^x
+        if (fmt == kOutMxFp8E4M3) {
+            const float lim = 448.f * s;
+            float c[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c[j] = __builtin_amdgcn_fmed3f(v[j], -lim, lim);
+            mx_short2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(mx_short2{0, 0}, c[0], c[1], s, false);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c[2], c[3], s, true);
+            *reinterpret_cast<unsigned *>(codes_row + col) = __builtin_bit_cast(unsigned, w);
+        } else {
+            unsigned w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], s, 0);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], s, 1);
+            *reinterpret_cast<uint16_t *>(codes_row + col / 2) = (uint16_t)w;
+        }
+        return;
+    }
     if (fmt == kOutMxFp8E4M3) {
         const unsigned w = mx_e4m3(ldexpf(v[0], -x)) | (mx_e4m3(ldexpf(v[1], -x)) << 8) |
                            (mx_e4m3(ldexpf(v[2], -x)) << 16) | (mx_e4m3(ldexpf(v[3], -x)) << 24);
