@@ -18,6 +18,9 @@ Also reported on the same line:
                 1..8192 (split + merge), as GB/s of the K/V actually read.
   mx_output     the largest causal prefill point with MX-coded output
                 (FP8 E4M3 and FP4 E2M1 with E8M0 block scales).
+  attainable    what this GPU sustains: a 2 GiB streaming read (plain and
+                non-temporal loads) and a bf16 MFMA loop; `roofline` and the
+                prefill lines also give their fraction of these.
   prefill       the largest causal MHA prefill point, the sliding-window
                 MQA prefill and a long causal GQA prefill (T = s_k = 4096):
                 fused-kernel TFLOP/s (algorithmic flops) against the dense
@@ -283,6 +286,41 @@ def run_mx_output(torch, fa, I):
     return out
 
 
+def run_attainable(torch):
+    """What this GPU sustains, for roofline fractions beside the published
+    peaks: a streaming read of 2 GiB (8x the Infinity Cache) with plain and
+    with non-temporal loads, and a loop of independent bf16 MFMAs."""
+    from head_attention_fmha_amd import peaks
+    st = torch.cuda.current_stream()
+
+    def timed_ms(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    buf = torch.ones(2 * 2**30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1024 * 4, dtype=torch.float32, device="cuda")
+    nbytes = buf.numel()
+    plain = nbytes / (timed_ms(lambda: peaks.stream_read(buf, False, sink, st), 10) * 1e-3) / 1e9
+    nt = nbytes / (timed_ms(lambda: peaks.stream_read(buf, True, sink, st), 10) * 1e-3) / 1e9
+    del buf
+    flops = 1024 * 4 * 4096 * 4 * 32768.0
+    ms = timed_ms(lambda: peaks.mfma_bf16(1024, 4096, sink, st), 5)
+    mfma = flops / (ms * 1e-3) / 1e12
+    log(f"attainable: streaming read {plain:.0f} GB/s plain, {nt:.0f} GB/s non-temporal; bf16 MFMA {mfma:.0f} TFLOP/s")
+    return {"hbm_read_gbs": round(plain, 1), "hbm_read_nt_gbs": round(nt, 1), "mfma_bf16_tflops": round(mfma, 1),
+            "hbm_frac_of_published": round(max(plain, nt) / HBM_PEAK_GBS, 4),
+            "mfma_frac_of_published": round(mfma / MFMA_BF16_PEAK_TFS, 4),
+            "how": "2 GiB streaming read (16-byte loads, whole chip), plain and non-temporal; 1024 x 4 waves x "
+                   "4096 rounds of 4 independent v_mfma_f32_32x32x16_bf16"}
+
+
 def run_cpu_baseline(res, seconds):
     import oracle
     w = res["w"]
@@ -353,6 +391,11 @@ def main():
     prefill = None if args.no_prefill else run_prefill(torch, fa, I)
     mx_out = None if args.no_prefill else run_mx_output(torch, fa, I)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(res, args.cpu_seconds)
+    att = run_attainable(torch)
+    best_bw = max(att["hbm_read_gbs"], att["hbm_read_nt_gbs"])
+    for p in prefill or []:
+        t_att = max(p["alg_mib"] * 2**20 / (best_bw * 1e9), p["alg_gflop"] * 1e9 / (att["mfma_bf16_tflops"] * 1e12))
+        p["frac_of_attainable_roofline"] = round(t_att * 1e6 / p["us_per_call"], 4)
     w = res["w"]
     split_us = res["split_ms"] * 1e3
     split_tag = "attn_kernel_hd128_split_gqa_decode"
@@ -378,7 +421,9 @@ def main():
                                "head part; 1 tile; split; one slice; streamed)", "bound": "hbm",
                      "achieved": round(res["split_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(res["split_gbs"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(split_tag),
-                     "alg_bytes_per_launch": res["split_bytes"], "launch_us": round(split_us, 2)},
+                     "alg_bytes_per_launch": res["split_bytes"], "launch_us": round(split_us, 2),
+                     "frac_of_attainable": round(res["split_gbs"] / best_bw, 4)},
+        "attainable": att,
         "cpu_baseline": cpu,
         "prefill": prefill,
         "ragged_decode": ragged,

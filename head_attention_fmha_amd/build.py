@@ -15,6 +15,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libfmha.so")
 SOURCES = [os.path.join(CSRC, "fmha_api.hip")]
+# attainable-peak probes used by the benchmark (not the attention path)
+PEAKS_LIB_PATH = os.path.join(PKG, "libfmha_peaks.so")
+PEAKS_SOURCES = [os.path.join(PKG, "peaks", "peaks.hip")]
 ARCH = "gfx950"
 
 
@@ -25,14 +28,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build_library(verbose: bool = False) -> str:
-    tmp = LIB_PATH + ".tmp"
+def _compile(sources, out_path, include_dirs, verbose):
+    tmp = out_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed fp32 VALU ops stay disabled: the compiler must not emit them
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wall", "-Wno-unused-function",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *SOURCES, "-o", tmp]
+           *[a for d in include_dirs for a in ("-I", d)],
+           *sources, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(ln for ln in res.stderr.splitlines() if noise not in ln)
@@ -40,7 +43,14 @@ def build_library(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out_path)
+    return out_path
+
+
+def build_library(verbose: bool = False) -> str:
+    """The attention library, then the attainable-peak probes."""
+    _compile(SOURCES, LIB_PATH, [os.path.join(ROOT, "include"), CSRC], verbose)
+    _compile(PEAKS_SOURCES, PEAKS_LIB_PATH, [os.path.join(ROOT, "include")], verbose)
     return LIB_PATH
 
 

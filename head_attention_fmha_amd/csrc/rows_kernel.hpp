@@ -206,18 +206,25 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
     // keys; each K operand read from LDS feeds the MFMAs of all the tiles
     auto qk = [&](const unsigned char *sK, f32x4 (&sc)[RT][KB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int r = 16 * kb + lr;
-            const unsigned char *krow = sK + r * ROW_BYTES;
+        for (int mt = 0; mt < RT; ++mt)
 #pragma unroll
-            for (int mt = 0; mt < RT; ++mt) sc[mt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < KB; ++kb) sc[mt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // head-dim steps outermost: the RT * KB accumulators are independent
+        // chains, and consecutive MFMAs go to different ones (a chain's next
+        // MFMA waits for the previous one's result)
 #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
+        for (int s = 0; s < KSTEPS; ++s) {
+            bf16x8 kf[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int r = 16 * kb + lr;
                 const int slot = (4 * s + lg + rot_of(r)) % CHUNKS;
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(krow + slot * 16);
-#pragma unroll
-                for (int mt = 0; mt < RT; ++mt) sc[mt][kb] = mfma_16x16x32(kf, qf[mt][s], sc[mt][kb]);
+                kf[kb] = *reinterpret_cast<const bf16x8 *>(sK + r * ROW_BYTES + slot * 16);
             }
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int mt = 0; mt < RT; ++mt) sc[mt][kb] = mfma_16x16x32(kf[kb], qf[mt][s], sc[mt][kb]);
         }
     };
 

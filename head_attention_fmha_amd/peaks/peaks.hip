@@ -1,0 +1,80 @@
+// peaks.hip -- attainable-peak probes for the benchmark's roofline fractions:
+// a chip-wide streaming read (plain or non-temporal loads) and a loop of
+// independent bf16 MFMAs.  Measurement only; the attention path never calls
+// them.  Declared in fmha_peaks.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fmha_peaks.h"
+
+namespace {
+
+typedef unsigned u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned))));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+constexpr int kUnroll = 8;  // 16-byte loads in flight per lane and step
+
+// Grid-stride: in each step a workgroup covers 256 * kUnroll consecutive
+// 16-byte words, lane t reading words t, t + 256, ... (coalesced).
+template <bool NT>
+__global__ __launch_bounds__(256) void stream_read(const u32x4 *p, int64_t n, unsigned *sink) {
+    int64_t i = (int64_t)blockIdx.x * 256 * kUnroll + threadIdx.x;
+    const int64_t step = (int64_t)gridDim.x * 256 * kUnroll;
+    unsigned acc = 0;
+    for (; i + 256 * (kUnroll - 1) < n; i += step) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = NT ? __builtin_nontemporal_load(p + i + 256 * u) : p[i + 256 * u];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the loads; practically never taken
+}
+
+// Four independent 32x32x16 accumulation chains per wave (a chain's next
+// MFMA waits for the previous result; four chains and four waves per SIMD
+// keep the matrix unit busy -- the 16x16x32 form needs about sixteen).
+__global__ __launch_bounds__(256) void mfma_loop(int iters, float *sink) {
+    bf16x8 a, b;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        a[j] = (__bf16)((float)((threadIdx.x + j) & 7) * 0x1p-12f);
+        b[j] = (__bf16)((float)((threadIdx.x * 3 + j) & 7) * 0x1p-12f);
+    }
+    f32x16 c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) c[k][j] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[k], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s += c[k][0] + c[k][15];
+    if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
+}
+
+}  // namespace
+
+extern "C" int fmha_peak_stream_read(const void *buf, int64_t bytes, int nontemporal, unsigned *sink,
+                                     void *stream) {
+    if (!buf || !sink || bytes <= 0 || bytes % (256 * 16 * kUnroll) != 0) return 1;
+    if ((reinterpret_cast<uintptr_t>(buf) & 15u) != 0) return 3;
+    const int64_t n = bytes / 16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid(8192), block(256);
+    if (nontemporal)
+        hipLaunchKernelGGL(stream_read<true>, grid, block, 0, s, static_cast<const u32x4 *>(buf), n, sink);
+    else
+        hipLaunchKernelGGL(stream_read<false>, grid, block, 0, s, static_cast<const u32x4 *>(buf), n, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+extern "C" int fmha_peak_mfma_bf16(int workgroups, int iters, float *sink, void *stream) {
+    if (!sink || workgroups <= 0 || iters <= 0) return 1;
+    hipLaunchKernelGGL(mfma_loop, dim3(workgroups), dim3(256), 0, static_cast<hipStream_t>(stream), iters, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
