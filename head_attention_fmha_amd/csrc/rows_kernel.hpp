@@ -204,14 +204,21 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
 
     // ---- S^T of one staged chunk for every tile of this wave: KB blocks of 16
     // keys; each K operand read from LDS feeds the MFMAs of all the tiles
+    // With fewer than four (tile, key-block) accumulators (one tile per wave
+    // at 32-key chunks), each is split into NP partial sums over alternate
+    // head-dim steps, added at the end in a fixed order.
+    constexpr int NP = (RT * KB >= 4 || HD >= 512) ? 1 : 4 / (RT * KB);
     auto qk = [&](const unsigned char *sK, f32x4 (&sc)[RT][KB]) __attribute__((always_inline)) {
+        f32x4 part[NP][RT][KB];
 #pragma unroll
-        for (int mt = 0; mt < RT; ++mt)
+        for (int q = 0; q < NP; ++q)
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) sc[mt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // head-dim steps outermost: the RT * KB accumulators are independent
-        // chains, and consecutive MFMAs go to different ones (a chain's next
-        // MFMA waits for the previous one's result)
+            for (int mt = 0; mt < RT; ++mt)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) part[q][mt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // head-dim steps outermost: the accumulators are independent chains,
+        // and consecutive MFMAs go to different ones (a chain's next MFMA
+        // waits for the previous one's result)
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
             bf16x8 kf[KB];
@@ -224,8 +231,17 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int mt = 0; mt < RT; ++mt) sc[mt][kb] = mfma_16x16x32(kf[kb], qf[mt][s], sc[mt][kb]);
+                for (int mt = 0; mt < RT; ++mt)
+                    part[s % NP][mt][kb] = mfma_16x16x32(kf[kb], qf[mt][s], part[s % NP][mt][kb]);
         }
+#pragma unroll
+        for (int mt = 0; mt < RT; ++mt)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                sc[mt][kb] = part[0][mt][kb];
+#pragma unroll
+                for (int q = 1; q < NP; ++q) sc[mt][kb] = sc[mt][kb] + part[q][mt][kb];
+            }
     };
 
     // ---- online softmax, first half: mask, maximum, rescale.  A chunk that
