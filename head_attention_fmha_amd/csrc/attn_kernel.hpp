@@ -23,7 +23,8 @@
 //   S^T (keys x rows) = K . Q^T      lane holds S^T[4*lg + j][lr]
 //   O^T (hd x rows)  += V^T . P^T    lane holds O^T[4*lg + j][lr]
 // so all softmax state of row lr lives in lanes lr, lr+16, lr+32, lr+48:
-// the running max needs two butterfly steps, the rescale factor is a
+// the running max and sum reduce over those four lanes in two lane-swap
+// steps (v_permlane16_swap, v_permlane32_swap), the rescale factor is a
 // per-lane scalar, and the probabilities leave the QK result registers in
 // exactly the B-operand layout of the PV product (the 32-key reduction
 // index is permuted identically in both PV operands).

@@ -5,8 +5,8 @@
 // (batch, KV head, partition): wave w owns 16-row tiles w*RT .. w*RT + RT - 1
 // of the block, over the FULL head dimension and EVERY key of the range.
 // K/V are streamed through LDS in chunks of KC keys shared by all four
-// waves, so each K/V byte leaves L2 once per 64*RT rows (the per-wave kernel of attn_kernel.hpp fetches it
-// once per 16*MT rows).  This is the tiled prefill loop of the pages' fused
+// waves, so each K/V byte leaves L2 once per 64*RT rows (the per-wave
+// kernel of attn_kernel.hpp fetches it once per 16*MT rows).  This is the tiled prefill loop of the pages' fused
 // kernel -- Q tile resident, K/V tiles staged on chip, online softmax state
 // in registers -- laid out for CDNA4:
 //   * a chunk travels HBM -> LDS by global_load_lds_dwordx4 (no registers)
@@ -203,10 +203,11 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
     const int tr_col = 4 * (lr & 3);
 
     // ---- S^T of one staged chunk for every tile of this wave: KB blocks of 16
-    // keys; each K operand read from LDS feeds the MFMAs of all the tiles
+    // keys; each K operand read from LDS feeds the MFMAs of all the tiles.
     // With fewer than four (tile, key-block) accumulators (one tile per wave
-    // at 32-key chunks), each is split into NP partial sums over alternate
-    // head-dim steps, added at the end in a fixed order.
+    // at 32-key chunks, hd 256), each is split into NP partial sums over
+    // alternate head-dim steps, added at the end in a fixed order (at hd 512
+    // the extra accumulators would not fit the registers).
     constexpr int NP = (RT * KB >= 4 || HD >= 512) ? 1 : 4 / (RT * KB);
     auto qk = [&](const unsigned char *sK, f32x4 (&sc)[RT][KB]) __attribute__((always_inline)) {
         f32x4 part[NP][RT][KB];
