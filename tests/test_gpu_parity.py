@@ -353,6 +353,76 @@ def test_zero_scale_row_parallel(dims, tiles, causal, window, hd):
     assert err < 1e-2 and lerr < 1e-5
 
 
+def _random_cases(n, seed):
+    """A fixed list of random shapes (drawn once from `seed`): head dim, GQA
+    group, KV heads, queries, cache length, mask, value spread and entry
+    point, sized so the oracle finishes each in well under a second."""
+    import random
+    rnd = random.Random(seed)
+    cases = []
+    for i in range(n):
+        hd = rnd.choice([64, 128, 256, 512])
+        group = rnd.choice([1, 2, 3, 4, 5, 8, 16])
+        n_kv_h = rnd.choice([1, 2, 4])
+        T = rnd.choice([1, 2, 7, 16, 33, 64, 100, 130])
+        s_k = rnd.randint(T, 700)
+        causal = rnd.random() < 0.6
+        window = rnd.choice([0, 0, 1, 17, 64, 200]) if causal or rnd.random() < 0.3 else 0
+        if window and not causal and T > s_k:
+            window = 0
+        sigma = rnd.choice([0.5, 1.0, 2.0])
+        split_len = rnd.choice([0, 0, 0, 32, 128, 300])
+        b = rnd.choice([1, 2, 3])
+        cases.append((f"r{i}", b, group * n_kv_h, n_kv_h, T, s_k, hd, causal, window, sigma, split_len))
+    return cases
+
+
+def _random_wide_cases(n, seed):
+    """Random shapes with enough (batch, KV head, row block) units for the
+    two-tile and row-parallel kernels, kept under ~4e9 multiply-adds."""
+    import random
+    rnd = random.Random(seed)
+    cases = []
+    while len(cases) < n:
+        hd = rnd.choice([64, 128, 256, 512])
+        b = rnd.choice([2, 4])
+        n_kv_h = rnd.choice([8, 16, 32])
+        group = rnd.choice([1, 2, 4])
+        T = rnd.choice([40, 64, 100, 128, 200])
+        s_k = rnd.randint(T, 500)
+        if b * group * n_kv_h * T * s_k * hd > 4e9:
+            continue
+        causal = rnd.random() < 0.7
+        window = rnd.choice([0, 0, 33, 150]) if causal else 0
+        split_len = rnd.choice([0, 0, 0, 96])
+        cases.append((f"w{len(cases)}", b, group * n_kv_h, n_kv_h, T, s_k, hd, causal, window, 1.0, split_len))
+    return cases
+
+
+RANDOM_CASES = _random_cases(40, 2027) + _random_wide_cases(24, 7)
+
+
+@pytest.mark.parametrize("name,b,n_h,n_kv_h,T,s_k,hd,causal,window,sigma,split_len", RANDOM_CASES,
+                         ids=[c[0] for c in RANDOM_CASES])
+def test_random_shapes_against_oracle(name, b, n_h, n_kv_h, T, s_k, hd, causal, window, sigma, split_len):
+    """Random shapes over head dims, groups, masks, value spreads and both
+    entry points (forward, or split + merge) against the oracle."""
+    plan = fa.fmha_attention_plan(b, n_h, n_kv_h, T, s_k, hd, window=window, causal=causal, split_len=split_len)
+    sys.stderr.write(f"[gpu-case] {name}: b{b} h{n_h}/{n_kv_h} T{T} s_k{s_k} hd{hd} causal {causal} "
+                     f"window {window} sigma {sigma} split {split_len} -> {VS.branch(plan)}\n")
+    seed = (3000 if name[0] == "r" else 4000) + int(name[1:])
+    q = I.randn_bf16((b, T, n_h, hd), seed, sigma)
+    k = I.randn_bf16((b, s_k, n_kv_h, hd), seed + 1, sigma)
+    v = I.randn_bf16((b, s_k, n_kv_h, hd), seed + 2)
+    scale = 1.0 / math.sqrt(hd)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=causal, window=window)
+    if split_len:
+        o, lse, _, _ = gpu_split(q, k, v, scale, split_len, causal, window)
+    else:
+        o, lse = gpu_forward(q, k, v, scale, causal, window)
+    check_attention(o, lse, o_ref, lse_ref, what=name)
+
+
 # ---------------------------------------------------------------------------
 # Long prefill: T in the thousands, up to T = s_k
 # ---------------------------------------------------------------------------
