@@ -244,11 +244,14 @@ def fmha_lse_merge(o_part, lse_part, o, lse=None, *, stream=None) -> None:
 
 
 def fmha_attention_plan(batch, n_h, n_kv_h, T, s_k, hd, *, window=0, causal=False, split_len=0,
-                        mqa_stride0=False) -> dict:
+                        mqa_stride0=False, kv_token_stride=None) -> dict:
     """How a call of these sizes would run (host-only; see include/fmha.h).
     split_len = 0 asks about fmha_forward, > 0 about fmha_decode_splitkv;
-    mqa_stride0 describes K/V given with head stride 0."""
-    kv_st = FmhaStrides(0, 0, 0 if mqa_stride0 else hd)
+    mqa_stride0 describes K/V given with head stride 0; kv_token_stride is
+    the K/V token stride in elements (default: dense, n_kv_h * hd)."""
+    head = 0 if mqa_stride0 else hd
+    token = n_kv_h * hd if kv_token_stride is None else int(kv_token_stride)
+    kv_st = FmhaStrides(0, token, head)
     plan = FmhaPlan()
     _check(load_library().fmha_attention_plan(batch, n_h, n_kv_h, T, s_k, hd, kv_st, kv_st, int(window),
                                               int(bool(causal)), int(split_len), ctypes.byref(plan)))

@@ -89,6 +89,23 @@ __device__ __forceinline__ void load_lds_16(const void *gptr, void *lds_base) {
     __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 16, 0, NT ? 2 : 0);
 }
 
+// 16 bytes per lane into LDS by a buffer load (buffer_load_dwordx4 ... lds):
+// lane L copies the 16 bytes at base + voffset(L) to lds_base + 16L, with
+// base wave-uniform (a buffer resource in scalar registers) and voffset the
+// lane's byte offset from it (below 2^31).  Like load_lds_16 it completes
+// asynchronously and is tracked by vmcnt.  Unlike the global form, which the
+// compiler counts as a possible LDS access of a flat instruction -- after
+// which it can only wait for all LDS reads at once (lgkmcnt(0)) -- the
+// buffer form leaves the compiler's waits for LDS reads exact, so reads
+// issued ahead of their use stay in flight.  Raw buffer, 32-bit data format,
+// range check off (records = 2^32 - 1).
+__device__ __forceinline__ void load_lds_buf(const void *base, unsigned voffset, void *lds_base) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, -1, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds_base, 16,
+                                             voffset, 0, 0, 0);
+}
+
 // Workgroup barrier for LDS staged by global_load_lds.  The caller has
 // already waited (vmcnt) for its own LDS-direct loads that others will read;
 // this waits for the wave's LDS reads and writes, then meets the other

@@ -110,6 +110,14 @@ int tile_positions(int group) {
 // wave per SIMD), and the chunk pipeline still beats the per-wave kernel.
 constexpr int rows_chunk_keys(int hd) { return hd <= 128 ? 64 : 32; }
 
+// The row-parallel kernel stages K/V by buffer loads of 1 KiB, each from a
+// scalar base at its first key row with 32-bit lane offsets: the rows of one
+// load (1024 / (2 hd) of them) must lie within 2^31 bytes.
+bool rows_loads_fit(const FwdParams &p, int hd) {
+    const int64_t st = p.k_st > p.v_st ? p.k_st : p.v_st;
+    return (int64_t)(1024 / (2 * hd) - 1) * st * 2 + 2 * hd < (int64_t(1) << 31);
+}
+
 // The kernel variant and grid for one call.  A workgroup serves MT 16-row
 // tiles of one (batch, KV head, partition); its NW waves split head-dim
 // columns (NH parts) and keys (NK = NW / NH groups of 32-key slices).
@@ -146,7 +154,7 @@ fmha_plan plan_attention(const FwdParams &p, int hd) {
     // workgroup (short prefill); two -- every K operand read from LDS then
     // feeds two MFMAs -- once the grid has two workgroups per compute unit
     // even so (long prefill)
-    if (!pl.one_slice && p.rows >= 64) {
+    if (!pl.one_slice && p.rows >= 64 && rows_loads_fit(p, hd)) {
         const int64_t per_kv = (int64_t)p.n_split * p.n_kv_h * p.batch;
         const int64_t groups1 = (int64_t)((p.rows + 63) / 64) * per_kv;
         const int64_t groups2 = (int64_t)((p.rows + 127) / 128) * per_kv;

@@ -9,13 +9,17 @@
 // kernel of attn_kernel.hpp fetches it once per 16*MT rows).  This is the tiled prefill loop of the pages' fused
 // kernel -- Q tile resident, K/V tiles staged on chip, online softmax state
 // in registers -- laid out for CDNA4:
-//   * a chunk travels HBM -> LDS by global_load_lds_dwordx4 (no registers)
-//     into one of two K and two V slots; K runs one chunk ahead of V, so the
-//     QK product of chunk n+1 is issued together with the softmax of chunk n
-//     (independent MFMA and vector work in one basic block, which the
-//     hardware overlaps), then chunk n's PV product;
+//   * a chunk travels HBM -> LDS by buffer_load_dwordx4 ... lds (no
+//     registers; the buffer form, unlike global_load_lds, leaves the
+//     compiler's waits for LDS reads exact) into one of two K and two V
+//     slots; K runs one chunk ahead of V, so the QK product of chunk n+1 is
+//     issued together with the softmax of chunk n (independent MFMA and
+//     vector work in one basic block, which the hardware overlaps), then
+//     chunk n's PV product;
 //   * LDS key row r holds its 16-byte column chunk c at slot
-//     (c + 2*(r mod 8)) mod CHUNKS, for both K and V;
+//     (c + 2*(r mod 8)) mod CHUNKS, for both K and V (at hd 512 the row is
+//     padded and shifted by 2*(r mod 8) chunks instead: the same banks, and
+//     every read address is a base plus a constant);
 //   * S^T = K . Q^T with the K A-operand read from LDS (16 bytes per lane),
 //     O^T += V^T . P^T with V^T from the transposing LDS read
 //     ds_read_b64_tr_b16, P^T straight from the QK result registers -- the
@@ -39,28 +43,38 @@ struct RowsShape {
     static constexpr int ROW_BYTES = HD * 2;
     static constexpr int KB = KC / 16;             // 16-key blocks per chunk
     static constexpr int KS = KC / 32;             // 32-key PV slices per chunk
-    static constexpr int PART_BYTES = KC * ROW_BYTES;  // one K (or V) slot
+    static constexpr int PART_BYTES = KC * ROW_BYTES;  // K (or V) bytes of one chunk
     static constexpr int LOADS = PART_BYTES / (256 * 16);  // 16-byte loads per lane per slot
     static constexpr int ROWS = 64 * RT;           // rows per workgroup
+    // LDS key rows: up to hd 256 a row is stored in ROW_BYTES with its chunks
+    // rotated in place; at hd 512 (one 1 KiB row per wave-wide load) rows are
+    // padded to PITCH and shifted whole, which keeps the bank spread of the
+    // rotation while every LDS read of a slot is one per-lane base plus a
+    // compile-time offset (no per-step address registers)
+    static constexpr bool SHIFTED = HD >= 512;
+    static constexpr int PITCH = SHIFTED ? ROW_BYTES + 256 : ROW_BYTES;
+    static constexpr int SLOT_BYTES = KC * PITCH;
     static_assert(KC % 32 == 0 && PART_BYTES % (256 * 16) == 0, "whole wave-wide loads");
-    // four slots: 32 or 64 KiB up to hd 256 (two workgroups per CU), 128 KiB
+    static_assert(!SHIFTED || ROW_BYTES == 1024, "a shifted row is one wave-wide load");
+    // four slots: 32 or 64 KiB up to hd 256 (two workgroups per CU), 160 KiB
     // at hd 512 (one; its full-width Q and O tiles fill a SIMD's registers)
-    static_assert(4 * PART_BYTES <= 160 * 1024, "four slots fit the LDS");
+    static_assert(4 * SLOT_BYTES <= 160 * 1024, "four slots fit the LDS");
 };
 
 template <int HD, int RT, int KC, bool SPLIT>
 __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdParams p) {
     using S = RowsShape<HD, RT, KC>;
     constexpr int KSTEPS = S::KSTEPS, NB = S::NB, CHUNKS = S::CHUNKS, ROW_BYTES = S::ROW_BYTES;
-    constexpr int KB = S::KB, KS = S::KS, PART_BYTES = S::PART_BYTES;
-    constexpr int LOADS = S::LOADS;
+    constexpr int KB = S::KB, KS = S::KS, SLOT_BYTES = S::SLOT_BYTES;
+    constexpr int LOADS = S::LOADS, PITCH = S::PITCH;
+    constexpr bool SHIFTED = S::SHIFTED;
     // two K and two V slots as four LDS objects, used in turn by a loop
     // unrolled by two: the compiler can then tell each prefetch from the
     // reads of the other slot and need not wait for the prefetch before them
-    __shared__ __attribute__((aligned(16))) unsigned char sK0[PART_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char sK1[PART_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char sV0[PART_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char sV1[PART_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char sK0[SLOT_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char sK1[SLOT_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char sV0[SLOT_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char sV1[SLOT_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -165,34 +179,47 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
     const uint16_t *vbase = p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh;
     auto rot_of = [](int r) __attribute__((always_inline)) { return (2 * (r & 7)) % CHUNKS; };
 
-    // ---- one chunk HBM -> an LDS slot: wave w fills bytes [w*LOADS*1 KiB, ...)
-    // of the slot; the lane writing LDS byte x fetches the global chunk that
-    // belongs at x under the rotation.  The lane's row and chunk are fixed,
-    // so its byte offset from the chunk's first key is computed once; a
-    // chunk then costs one scalar base per tensor.  The last chunk of a range
-    // clamps keys past khi to key khi-1 instead.
-    int ld_row[LOADS], ld_col[LOADS];
+    // ---- one chunk HBM -> an LDS slot: wave w issues loads w*LOADS ..
+    // w*LOADS + LOADS-1, each 1 KiB of consecutive LDS bytes covering key rows
+    // r0 .. r0 + 1024/ROW_BYTES - 1 of the chunk; the lane writing LDS byte x
+    // fetches the global chunk that belongs at x under the rotation (a shifted
+    // row: load i is row i, lane j its chunk j).  A load is a buffer load from
+    // a scalar base at its first key row; the lane's byte offset from there
+    // is fixed and computed once (the host picks this kernel only when it
+    // stays below 2^31).  The last chunk of a range clamps keys past khi to
+    // key khi-1 instead.
+    int ld_r0[LOADS], ld_row[LOADS], ld_col[LOADS], ld_dst[LOADS];
     unsigned ld_koff[LOADS], ld_voff[LOADS];
-    const bool offsets32 = (int64_t)(KC - 1) * (p.k_st > p.v_st ? p.k_st : p.v_st) * 2 + ROW_BYTES < (1ll << 31);
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
-        const int x = ((wave * LOADS + it) * 64 + lane) * 16;  // LDS byte of this lane
-        ld_row[it] = x / ROW_BYTES;
-        ld_col[it] = ((x % ROW_BYTES) / 16 - rot_of(ld_row[it]) + CHUNKS) % CHUNKS;
-        ld_koff[it] = (unsigned)(((int64_t)ld_row[it] * p.k_st + ld_col[it] * 8) * 2);
-        ld_voff[it] = (unsigned)(((int64_t)ld_row[it] * p.v_st + ld_col[it] * 8) * 2);
+        const int i = wave * LOADS + it;  // wave-uniform
+        ld_r0[it] = i * 1024 / ROW_BYTES;
+        if constexpr (SHIFTED) {
+            ld_row[it] = i;
+            ld_col[it] = lane;
+            ld_dst[it] = i * PITCH + rot_of(i) * 16;
+        } else {
+            const int x = (i * 64 + lane) * 16;  // LDS byte of this lane
+            ld_row[it] = x / ROW_BYTES;
+            ld_col[it] = ((x % ROW_BYTES) / 16 - rot_of(ld_row[it]) + CHUNKS) % CHUNKS;
+            ld_dst[it] = i * 1024;
+        }
+        ld_koff[it] = (unsigned)(((int64_t)(ld_row[it] - ld_r0[it]) * p.k_st + ld_col[it] * 8) * 2);
+        ld_voff[it] = (unsigned)(((int64_t)(ld_row[it] - ld_r0[it]) * p.v_st + ld_col[it] * 8) * 2);
     }
     auto issue = [&](const uint16_t *base, int64_t st, const unsigned (&off)[LOADS], int k0, unsigned char *slot)
                      __attribute__((always_inline)) {
-        if (offsets32 && k0 + KC <= khi) {  // wave-uniform
-            const char *c = reinterpret_cast<const char *>(base + key_offset(k0, st));
+        if (SHIFTED || k0 + KC <= khi) {  // wave-uniform
 #pragma unroll
-            for (int it = 0; it < LOADS; ++it) load_lds_16(c + off[it], slot + (wave * LOADS + it) * 1024);
+            for (int it = 0; it < LOADS; ++it)
+                load_lds_buf(base + key_offset(min(k0 + ld_r0[it], khi - 1), st), off[it], slot + ld_dst[it]);
         } else {
 #pragma unroll
             for (int it = 0; it < LOADS; ++it) {
+                const int first = min(k0 + ld_r0[it], khi - 1);
                 const int key = min(k0 + ld_row[it], khi - 1);
-                load_lds_16(base + key_offset(key, st) + ld_col[it] * 8, slot + (wave * LOADS + it) * 1024);
+                const unsigned o = (unsigned)(((int64_t)(key - first) * st + ld_col[it] * 8) * 2);
+                load_lds_buf(base + key_offset(first, st), o, slot + ld_dst[it]);
             }
         }
     };
@@ -201,6 +228,12 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
     // lg addresses key 4*lg + s/4 (+16) of a 32-key slice, columns 4*(s%4)..+3
     const int tr_row0 = 4 * lg + (lr >> 2);
     const int tr_col = 4 * (lr & 3);
+    // shifted rows: this lane's LDS byte for K chunk 4s + lg of key row
+    // 16 kb + lr is k_lane + 16 kb PITCH + 64 s, for V^T columns 16 nb + tr_col
+    // of key row 32 ks + 16 half + tr_row0 it is v_lane + (32 ks + 16 half)
+    // PITCH + 32 nb (the rotation of a row depends on its index mod 8 only)
+    const int k_lane = lr * PITCH + (lg + rot_of(lr)) * 16;
+    const int v_lane = tr_row0 * PITCH + ((tr_col >> 3) + rot_of(tr_row0)) * 16 + (tr_col & 7) * 2;
 
     // ---- S^T of one staged chunk for every tile of this wave: KB blocks of 16
     // keys; each K operand read from LDS feeds the MFMAs of all the tiles.
@@ -225,9 +258,13 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
             bf16x8 kf[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const int r = 16 * kb + lr;
-                const int slot = (4 * s + lg + rot_of(r)) % CHUNKS;
-                kf[kb] = *reinterpret_cast<const bf16x8 *>(sK + r * ROW_BYTES + slot * 16);
+                if constexpr (SHIFTED) {
+                    kf[kb] = *reinterpret_cast<const bf16x8 *>(sK + k_lane + 16 * kb * PITCH + 64 * s);
+                } else {
+                    const int r = 16 * kb + lr;
+                    const int slot = (4 * s + lg + rot_of(r)) % CHUNKS;
+                    kf[kb] = *reinterpret_cast<const bf16x8 *>(sK + r * ROW_BYTES + slot * 16);
+                }
             }
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -322,7 +359,8 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
                 for (int half = 0; half < 2; ++half) {
                     const int r = 32 * ks + 16 * half + tr_row0;
                     const int c = 16 * nb + tr_col;
-                    const int off = r * ROW_BYTES + (((c >> 3) + rot_of(r)) % CHUNKS) * 16 + (c & 7) * 2;
+                    const int off = SHIFTED ? v_lane + (32 * ks + 16 * half) * PITCH + 32 * nb
+                                            : r * ROW_BYTES + (((c >> 3) + rot_of(r)) % CHUNKS) * 16 + (c & 7) * 2;
                     q2[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                         (__attribute__((address_space(3))) bf16x4 *)(sV + off));
                 }
@@ -331,6 +369,79 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
                 for (int mt = 0; mt < RT; ++mt) acc[mt][nb] = mfma_16x16x32(vt, pt[mt][ks], acc[mt][nb]);
             }
         }
+    };
+
+    // ---- hd 512 (shifted rows): the straight-line part of a step -- chunk
+    // n+1's QK product, chunk n's weights and PV product -- in an explicit
+    // order.  One wave per SIMD has no other wave to cover LDS latency, so
+    // each K operand is read D head-dim steps before its MFMAs and each V^T
+    // operand D column blocks before its MFMA (the first D of them during the
+    // last QK steps), and the weights' vector work is spread over the QK
+    // steps, one element per step, beside the MFMAs.  The scheduling barriers
+    // keep the compiler from regrouping the phases: it would otherwise issue
+    // every read just before its use and wait for it there.
+    auto fused = [&](const unsigned char *sK, f32x4 (&sn)[RT][KB], const f32x4 (&sc)[RT][KB],
+                     const unsigned char *sV) __attribute__((always_inline)) {
+        static_assert(!SHIFTED || (KS == 1 && KSTEPS >= RT * KB * 4 && KSTEPS >= 4 && NB >= 4), "one PV slice per chunk");
+        constexpr int D = 4, R = D + 1;  // read-ahead distance, ring size
+        auto read_k = [&](int st, bf16x8 (&kf)[KB]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                kf[kb] = *reinterpret_cast<const bf16x8 *>(sK + k_lane + 16 * kb * PITCH + 64 * st);
+        };
+        auto read_v = [&](int nb) __attribute__((always_inline)) {
+            bf16x4 q2[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+                q2[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (__attribute__((address_space(3))) bf16x4 *)(sV + v_lane + 16 * half * PITCH + 32 * nb));
+            return __builtin_shufflevector(q2[0], q2[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        bf16x8 kf[R][KB];
+        bf16x8 vt[R];
+#pragma unroll
+        for (int st = 0; st < D; ++st) read_k(st, kf[st]);
+#pragma unroll
+        for (int mt = 0; mt < RT; ++mt)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) sn[mt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 pt[RT];
+        float psum[RT];
+#pragma unroll
+        for (int mt = 0; mt < RT; ++mt) psum[mt] = 0.f;
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int mt = 0; mt < RT; ++mt) sn[mt][kb] = mfma_16x16x32(kf[st % R][kb], qf[mt][st], sn[mt][kb]);
+            if (st + D < KSTEPS)
+                read_k(st + D, kf[(st + D) % R]);
+            else
+                vt[(st + D - KSTEPS) % R] = read_v(st + D - KSTEPS);
+            // weights, one element per step: e = (mt, kb, j)
+            if (st < RT * KB * 4) {
+                const int mt = st / (KB * 4), kb = (st / 4) % KB, j = st % 4;
+                const float pj = fast_exp2(fmaf(sc[mt][kb][j], c_scale, neg_m[mt]));
+                pt[mt][kb * 4 + j] = to_bf16(pj);
+                psum[mt] += pj;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mt = 0; mt < RT; ++mt) {
+            l[mt] += psum[mt];
+            accq[mt] = mfma_16x16x32(ones, pt[mt], accq[mt]);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mt = 0; mt < RT; ++mt) acc[mt][nb] = mfma_16x16x32(vt[nb % R], pt[mt], acc[mt][nb]);
+            if (nb + D < NB) vt[(nb + D) % R] = read_v(nb + D);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // ---- the pipeline.  Step n starts with chunk n+1's K and chunk n's V on
@@ -360,10 +471,14 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
         if (n + 1 < nchunks) issue(vbase, p.v_st, ld_voff, k0 + KC, sVfill);
         prep(k0, sc);
         f32x4 sn[RT][KB];
-        qk(sKnext, sn);
-        bf16x8 pt[RT][KS];
-        weights(sc, pt);
-        pv(sVcur, pt);
+        if constexpr (SHIFTED) {
+            fused(sKnext, sn, sc, sVcur);
+        } else {
+            qk(sKnext, sn);
+            bf16x8 pt[RT][KS];
+            weights(sc, pt);
+            pv(sVcur, pt);
+        }
 #pragma unroll
         for (int mt = 0; mt < RT; ++mt)
 #pragma unroll

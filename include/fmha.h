@@ -251,7 +251,10 @@ int fmha_lse_merge_mx(const float *o_part, const float *lse_part, void *o_codes,
  *   row_parallel     1 when each wave owns whole rows and the waves share
  *                    K/V chunks staged in LDS (many rows per KV head)
  *   workgroups       grid size
- * k_st / v_st matter only through their head strides (both 0 = MQA).
+ * k_st / v_st matter through their head strides (both 0 = MQA) and their
+ * token strides: the row-parallel kernel stages K/V by 1 KiB buffer loads
+ * with 32-bit offsets from the load's first key row, so it is chosen only
+ * when (1024 / (2 hd) - 1) * token stride * 2 + 2 hd < 2^31 bytes.
  * Errors: as fmha_forward for sizes and mask arguments;
  * FMHA_ERR_INVALID_ARG for a null plan or split_len < 0.
  */

@@ -181,6 +181,19 @@ def test_plan_of_each_workload(lib, args, kw, want):
             got["workgroups"]) == want
 
 
+@pytest.mark.parametrize("hd,token_stride,row_parallel", [
+    # the row-parallel kernel's 1 KiB buffer loads address the key rows of one
+    # load (1024 / (2 hd) of them) by 32-bit offsets from the first
+    (128, 128, 1), (128, (1 << 31) // 6 - 128, 1), (128, (1 << 31) // 6, 0),
+    (64, (1 << 31) // 14 - 64, 1), (64, (1 << 31) // 14, 0),
+    # at hd 512 a load is one row: any token stride below 2^32 elements
+    (512, (1 << 32) - 512, 1),
+])
+def test_plan_row_parallel_token_stride_limit(lib, hd, token_stride, row_parallel):
+    got = fa.fmha_attention_plan(4, 32, 32, 128, 512, hd, causal=True, kv_token_stride=token_stride)
+    assert got["row_parallel"] == row_parallel
+
+
 @pytest.mark.parametrize("args,kw,code", [
     ((1, 1, 1, 1, 128, 96), {}, UNSUPPORTED),
     ((1, 1, 1, (1 << 20) + 1, (1 << 20) + 1, 64), {}, UNSUPPORTED),
