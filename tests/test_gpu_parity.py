@@ -230,6 +230,35 @@ def test_strided_layouts():
     assert torch.isnan(obuf[..., hd:].float()).all(), "writes outside the output view"
 
 
+@pytest.mark.parametrize("hd,b,n_h,n_kv_h,T,s_k,tiles", [
+    (64, 4, 32, 32, 128, 200, 4),     # one tile per wave, 64-key chunks, 8 key rows per 1 KiB load
+    (128, 8, 32, 8, 256, 300, 8),     # two tiles per wave, 32-key chunks
+    (256, 4, 32, 32, 128, 200, 4),    # 32-key chunks, 2 key rows per load
+    (512, 4, 32, 32, 128, 200, 4),    # padded, shifted LDS rows, one key row per load
+], ids=["hd64", "hd128_rt2", "hd256", "hd512"])
+def test_row_parallel_strided_kv(hd, b, n_h, n_kv_h, T, s_k, tiles):
+    """The row-parallel kernel's LDS loads address key rows by a scalar base
+    and per-lane offsets of (row - first row of the load) * token stride:
+    padded K and V caches with different token strides, ragged s_k (a
+    clamped last chunk), causal."""
+    scale = 1.0 / math.sqrt(hd)
+    q = I.randn_bf16((b, T, n_h, hd), 1300 + hd)
+    k = I.randn_bf16((b, s_k, n_kv_h, hd), 1301 + hd)
+    v = I.randn_bf16((b, s_k, n_kv_h, hd), 1302 + hd)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=True)
+    kpad = torch.zeros((b, s_k, n_kv_h + 1, hd + 64), dtype=torch.bfloat16, device=DEV)
+    kpad[:, :, :n_kv_h, :hd] = k.to(DEV)
+    vpad = torch.zeros((b, s_k + 3, 2 * n_kv_h, hd), dtype=torch.bfloat16, device=DEV)
+    vpad[:, :s_k, :n_kv_h] = v.to(DEV)
+    k_view, v_view = kpad[:, :, :n_kv_h, :hd], vpad[:, :s_k, :n_kv_h]
+    assert k_view.stride(1) != v_view.stride(1)
+    plan = fa.fmha_attention_plan(b, n_h, n_kv_h, T, s_k, hd, causal=True,
+                                  kv_token_stride=max(k_view.stride(1), v_view.stride(1)))
+    assert plan["row_parallel"] == 1 and plan["tiles_per_group"] == tiles, plan
+    o, lse = gpu_forward(q, k_view, v_view, scale, True, 0)
+    check_attention(o, lse, o_ref, lse_ref, what=f"row-parallel strided hd{hd}")
+
+
 def test_lse_is_optional():
     q, k, v = (I.randn_bf16(s, i) for i, s in enumerate([(1, 4, 4, 64), (1, 64, 4, 64), (1, 64, 4, 64)]))
     o1, _ = gpu_forward(q, k, v, 0.125, True, 0, want_lse=False)
