@@ -455,10 +455,16 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
     const int nchunks = khi > klo ? (khi - klo + KC - 1) / KC : 0;  // wave-uniform
     f32x4 sc[RT][KB];
     if (nchunks > 0) {
+        // chunk 0's scores need only Q and chunk 0's K (the oldest loads):
+        // chunk 0's V and chunk 1's K stay in flight during that product
         issue(kbase, p.k_st, ld_koff, klo, sK0);
         issue(vbase, p.v_st, ld_voff, klo, sV0);
-        if (nchunks > 1) issue(kbase, p.k_st, ld_koff, klo + KC, sK1);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        if (nchunks > 1) {
+            issue(kbase, p.k_st, ld_koff, klo + KC, sK1);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS));
+        } else {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS));
+        }
         lds_barrier();
         qk(sK0, sc);
     }
