@@ -29,7 +29,11 @@ Also reported on the same line:
                 over input replicas rotated through more than the Infinity
                 Cache.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+Separately, `--grid PATH` times every point of the decode and prefill grids
+(cold and hot, with the launch floor of an empty kernel) and writes them to
+PATH.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--grid PATH]
 """
 import argparse
 import glob
@@ -88,8 +92,10 @@ def decode_bytes(w):
     return kv, split_kernel, merge_kernel
 
 
-def prefill_work(w):
-    """Algorithmic (flops, bytes) of one fused call; masked keys are not work."""
+def forward_work(w):
+    """Algorithmic (flops, total bytes, K+V bytes) of one fused call: masked
+    keys are not work, and K/V bytes count the union of the keys any query
+    sees (each read once)."""
     pairs = 0
     union_lo, union_hi = w.s_k, 0
     for i in range(w.T):
@@ -100,8 +106,14 @@ def prefill_work(w):
         union_lo, union_hi = min(union_lo, lo), max(union_hi, hi)
     flops = 4.0 * w.hd * w.batch * w.n_h * pairs
     u = max(0, union_hi - union_lo)
-    byts = (2 * 2 * w.batch * w.T * w.n_h * w.hd + 4 * w.batch * w.n_h * w.T
-            + 4 * w.batch * w.n_kv_h * u * w.hd)
+    kv = 4 * w.batch * w.n_kv_h * u * w.hd
+    byts = 2 * 2 * w.batch * w.T * w.n_h * w.hd + 4 * w.batch * w.n_h * w.T + kv
+    return flops, byts, kv
+
+
+def prefill_work(w):
+    """Algorithmic (flops, bytes) of one fused call."""
+    flops, byts, _ = forward_work(w)
     return flops, byts
 
 
@@ -197,8 +209,12 @@ def run_ragged_decode(args, torch, fa, I):
             "step": "fmha_decode_splitkv_segment (per-row lengths) + fmha_lse_merge"}
 
 
+WARM_MS = 30.0  # GPU time replayed before timing: clocks settle under sustained load
+
+
 def graph_time_us(torch, calls, reps):
-    """Capture `calls` (one launch each) into one graph; return mean us per call."""
+    """Capture `calls` (one launch each) into one graph, replay it for about
+    WARM_MS untimed, then return the mean us per call over `reps` replays."""
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
@@ -210,15 +226,28 @@ def graph_time_us(torch, calls, reps):
         for c in calls:
             c()
     torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    for _ in range(max(1, math.ceil(WARM_MS / max(s.elapsed_time(e), 1e-3)))):
+        g.replay()
+    torch.cuda.synchronize()
     s.record()
     for _ in range(reps):
         g.replay()
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) * 1e3 / (reps * len(calls))
+
+
+def rotated_time_us(torch, calls):
+    """Mean us per call over the given calls (one per input replica), captured
+    at least 32 to a graph -- a graph replay has a fixed cost of its own -- and
+    replayed for about 200 calls in all."""
+    per_graph = calls * max(1, 32 // len(calls))
+    return graph_time_us(torch, per_graph, reps=max(3, 200 // len(per_graph)))
 
 
 def run_prefill(torch, fa, I):
@@ -238,7 +267,7 @@ def run_prefill(torch, fa, I):
             return lambda: fa.fmha_forward(bf[0], bf[1], bf[2], bf[3], bf[4], scale=w.scale,
                                            window=w.window, causal=w.causal,
                                            stream=torch.cuda.current_stream())
-        us = graph_time_us(torch, [mk(bf) for bf in bufs], reps=max(3, 200 // reps))
+        us = rotated_time_us(torch, [mk(bf) for bf in bufs])
         t_roof_us = max(byts / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFS * 1e12)) * 1e6
         tfs = flops / (us * 1e-6) / 1e12
         plan = fa.fmha_attention_plan(w.batch, w.n_h, w.n_kv_h, w.T, w.s_k, w.hd, window=w.window,
@@ -255,6 +284,60 @@ def run_prefill(torch, fa, I):
         del bufs, q, k, v
         torch.cuda.empty_cache()
     return out
+
+
+def run_grid(torch, fa, I, path):
+    """Every point of the single-head decode, the MQA decode grid, the causal
+    MHA prefill grid and the sliding-window MQA prefill, one fmha_forward call
+    each, timed from graph replays: cold (input replicas rotated through at
+    least 512 MiB, twice the Infinity Cache; the single-head decode point is
+    32 KiB and is timed hot only, as latency) and hot (one input set).  The
+    launch floor is an empty kernel timed the same way; a point whose
+    roofline time is below five floors is flagged launch-bound.  Writes the
+    table to `path` as JSON."""
+    from head_attention_fmha_amd import peaks
+    floor_us = graph_time_us(torch, [lambda: peaks.empty(1, torch.cuda.current_stream())] * 64, reps=50)
+    log(f"grid: launch floor (empty kernel) {floor_us:.2f} us")
+    points = []
+    for w in [I.SINGLE_HEAD_DECODE] + I.MQA_DECODE_GRID + I.MHA_PREFILL_GRID + [I.SWA_MQA_PREFILL]:
+        flops, byts, kv = forward_work(w)
+        foot = 2 * (w.batch * w.T * w.n_h * w.hd * 2) + 2 * (w.batch * w.s_k * w.n_kv_h * w.hd * 2)
+        cold = w is not I.SINGLE_HEAD_DECODE
+        reps = max(1, min(64, math.ceil(512 * 2**20 / foot))) if cold else 1
+        q, k, v = I.make_qkv(w, device="cuda")
+        bufs = []
+        for r in range(reps):
+            qr, kr, vr = (q, k, v) if r == 0 else (q.clone(), k.clone(), v.clone())
+            bufs.append((qr, kr, vr, torch.empty_like(qr),
+                         torch.empty((w.batch, w.n_h, w.T), dtype=torch.float32, device="cuda")))
+
+        def mk(bf):
+            return lambda: fa.fmha_forward(bf[0], bf[1], bf[2], bf[3], bf[4], scale=w.scale,
+                                           window=w.window, causal=w.causal,
+                                           stream=torch.cuda.current_stream())
+        hot_us = rotated_time_us(torch, [mk(bufs[0])])
+        us = rotated_time_us(torch, [mk(bf) for bf in bufs]) if cold else hot_us
+        t_roof_us = max(byts / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFS * 1e12)) * 1e6
+        tfs = flops / (us * 1e-6) / 1e12
+        plan = fa.fmha_attention_plan(w.batch, w.n_h, w.n_kv_h, w.T, w.s_k, w.hd, window=w.window, causal=w.causal)
+        pt = {"workload": w.name, "T": w.T, "s_k": w.s_k, "hd": w.hd, "us": round(us, 2), "hot_us": round(hot_us, 2),
+              "cold": cold, "kv_gbs": round(kv / (us * 1e-6) / 1e9, 1),
+              "total_gbs": round(byts / (us * 1e-6) / 1e9, 1), "tflops": round(tfs, 2),
+              "t_roof_us": round(t_roof_us, 3), "frac_of_roofline": round(t_roof_us / us, 4),
+              "frac_of_hbm_peak": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+              "frac_of_mfma_peak": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+              "launch_bound": t_roof_us < 5 * floor_us, "replicas": reps,
+              "workgroups": plan["workgroups"], "row_parallel": plan["row_parallel"]}
+        points.append(pt)
+        log(f"grid {w.name}: {us:.2f} us (hot {hot_us:.2f}), {pt['kv_gbs']:.0f} GB/s K+V, "
+            f"{pt['total_gbs']:.0f} GB/s total, {tfs:.1f} TFLOP/s, {t_roof_us / us:.1%} of roofline"
+            f"{' (launch-bound)' if pt['launch_bound'] else ''}")
+        del bufs, q, k, v
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        json.dump({"launch_floor_us": round(floor_us, 3), "hbm_peak_gbs": HBM_PEAK_GBS,
+                   "mfma_bf16_peak_tflops": MFMA_BF16_PEAK_TFS, "points": points}, f, indent=1)
+    log(f"grid: {len(points)} points written to {path}")
 
 
 def run_mx_output(torch, fa, I):
@@ -276,7 +359,7 @@ def run_mx_output(torch, fa, I):
         def mk(bf, fmt=fmt):
             return lambda: fa.fmha_forward_mx(bf[0][0], bf[0][1], bf[0][2], bf[1], bf[2], fmt=fmt, scale=w.scale,
                                               causal=True, stream=torch.cuda.current_stream())
-        us = graph_time_us(torch, [mk(bf) for bf in bufs], reps=max(3, 200 // reps))
+        us = rotated_time_us(torch, [mk(bf) for bf in bufs])
         out.append({"workload": w.name, "format": name, "us_per_call": round(us, 2),
                     "tflops": round(flops / (us * 1e-6) / 1e12, 1)})
         log(f"mx output {name} {w.name}: {us:.2f} us")
@@ -344,8 +427,8 @@ def run_cpu_baseline(res, seconds):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-ragged", action="store_true",
@@ -353,6 +436,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only-prefill", action="store_true",
                     help="time only the prefill workloads (for profiler runs); prints no JSON line")
+    ap.add_argument("--grid", metavar="PATH",
+                    help="time every point of the decode and prefill grids, write them to PATH as JSON, "
+                         "and print no JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, copy 1 GiB twice (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -379,6 +465,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.grid:
+        run_grid(torch, fa, I, args.grid)
+        return
     if args.only_prefill:
         run_prefill(torch, fa, I)
         if args.calibrate_copy:

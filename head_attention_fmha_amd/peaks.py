@@ -24,6 +24,8 @@ def load():
         lib.fmha_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         lib.fmha_peak_stream_read.restype = ctypes.c_int
         lib.fmha_peak_mfma_bf16.restype = ctypes.c_int
+        lib.fmha_peak_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
+        lib.fmha_peak_empty.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -45,3 +47,8 @@ def mfma_bf16(workgroups: int, iters: int, sink, stream) -> float:
     _check(load().fmha_peak_mfma_bf16(workgroups, iters, ctypes.c_void_p(sink.data_ptr()),
                                       ctypes.c_void_p(stream.cuda_stream)), "fmha_peak_mfma_bf16")
     return float(workgroups) * 4 * iters * 4 * 32768
+
+
+def empty(workgroups: int, stream) -> None:
+    """Enqueue the empty kernel (launch floor)."""
+    _check(load().fmha_peak_empty(int(workgroups), ctypes.c_void_p(stream.cuda_stream)), "fmha_peak_empty")

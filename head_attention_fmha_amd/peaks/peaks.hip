@@ -1,6 +1,7 @@
 // peaks.hip -- attainable-peak probes for the benchmark's roofline fractions:
-// a chip-wide streaming read (plain or non-temporal loads) and a loop of
-// independent bf16 MFMAs.  Measurement only; the attention path never calls
+// a chip-wide streaming read (plain or non-temporal loads), a loop of
+// independent bf16 MFMAs, and an empty kernel (the launch floor).
+// Measurement only; the attention path never calls
 // them.  Declared in fmha_peaks.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -57,6 +58,9 @@ __global__ __launch_bounds__(256) void mfma_loop(int iters, float *sink) {
     if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
 }
 
+// Does nothing: its time per launch is the floor under any kernel's.
+__global__ __launch_bounds__(256) void empty_kernel() {}
+
 }  // namespace
 
 extern "C" int fmha_peak_stream_read(const void *buf, int64_t bytes, int nontemporal, unsigned *sink,
@@ -76,5 +80,11 @@ extern "C" int fmha_peak_stream_read(const void *buf, int64_t bytes, int nontemp
 extern "C" int fmha_peak_mfma_bf16(int workgroups, int iters, float *sink, void *stream) {
     if (!sink || workgroups <= 0 || iters <= 0) return 1;
     hipLaunchKernelGGL(mfma_loop, dim3(workgroups), dim3(256), 0, static_cast<hipStream_t>(stream), iters, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+extern "C" int fmha_peak_empty(int workgroups, void *stream) {
+    if (workgroups <= 0) return 1;
+    hipLaunchKernelGGL(empty_kernel, dim3(workgroups), dim3(256), 0, static_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }

@@ -32,6 +32,11 @@ int fmha_peak_stream_read(const void *buf, int64_t bytes, int nontemporal, unsig
  * Flops = workgroups * 4 * iters * 4 * 32768. */
 int fmha_peak_mfma_bf16(int workgroups, int iters, float *sink, void *stream);
 
+/* `workgroups` workgroups of four waves running an empty kernel: the time
+ * per launch, back to back on one stream, is the launch floor against which
+ * the benchmark flags launch-bound workloads. */
+int fmha_peak_empty(int workgroups, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

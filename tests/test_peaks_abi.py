@@ -21,7 +21,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     text = open(os.path.join(ROOT, "include", "fmha_peaks.h")).read()
     names = re.findall(r"^int (fmha_\w+)\(", text, flags=re.M)
-    assert sorted(names) == ["fmha_peak_mfma_bf16", "fmha_peak_stream_read"]
+    assert sorted(names) == ["fmha_peak_empty", "fmha_peak_mfma_bf16", "fmha_peak_stream_read"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -44,3 +44,10 @@ def test_mfma_rejects(lib):
     assert f(16, 16, None, None) == 1
     assert f(0, 16, sink, None) == 1
     assert f(16, 0, sink, None) == 1
+
+
+def test_empty_rejects(lib):
+    f = lib.fmha_peak_empty
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    assert f(0, None) == 1
+    assert f(-3, None) == 1
