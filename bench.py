@@ -209,6 +209,7 @@ def run_ragged_decode(args, torch, fa, I):
             "step": "fmha_decode_splitkv_segment (per-row lengths) + fmha_lse_merge"}
 
 
+SPLIT_DECODE_LEN = 128  # keys per partition when the grid times MQA decode as split-KV + merge
 WARM_MS = 30.0  # GPU time replayed before timing: clocks settle under sustained load
 
 
@@ -319,6 +320,24 @@ def run_grid(torch, fa, I, path):
         us = rotated_time_us(torch, [mk(bf) for bf in bufs]) if cold else hot_us
         t_roof_us = max(byts / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFS * 1e12)) * 1e6
         tfs = flops / (us * 1e-6) / 1e12
+        # MQA decode also as split-KV into 128-key partitions + LSE merge: its
+        # fused call has only 64 workgroups (8 batch rows x 8 tiles of the 128
+        # stacked query heads), the split spreads the keys over more
+        split_us = None
+        if w.n_kv_h == 1 and w.T == 1 and w.s_k > SPLIT_DECODE_LEN:
+            ns = fa.n_split_for(w.s_k, SPLIT_DECODE_LEN)
+            o_part = torch.empty((w.batch, w.n_h, 1, ns, w.hd), dtype=torch.float32, device="cuda")
+            lse_part = torch.empty((w.batch, w.n_h, 1, ns), dtype=torch.float32, device="cuda")
+
+            def mk_split(bf):
+                def step():
+                    st = torch.cuda.current_stream()
+                    fa.fmha_decode_splitkv(bf[0], bf[1], bf[2], o_part, lse_part, split_len=SPLIT_DECODE_LEN,
+                                           scale=w.scale, stream=st)
+                    fa.fmha_lse_merge(o_part, lse_part, bf[3], bf[4], stream=st)
+                return step
+            split_us = rotated_time_us(torch, [mk_split(bf) for bf in bufs])
+            del o_part, lse_part
         plan = fa.fmha_attention_plan(w.batch, w.n_h, w.n_kv_h, w.T, w.s_k, w.hd, window=w.window, causal=w.causal)
         pt = {"workload": w.name, "T": w.T, "s_k": w.s_k, "hd": w.hd, "us": round(us, 2), "hot_us": round(hot_us, 2),
               "cold": cold, "kv_gbs": round(kv / (us * 1e-6) / 1e9, 1),
@@ -328,10 +347,14 @@ def run_grid(torch, fa, I, path):
               "frac_of_mfma_peak": round(tfs / MFMA_BF16_PEAK_TFS, 4),
               "launch_bound": t_roof_us < 5 * floor_us, "replicas": reps,
               "workgroups": plan["workgroups"], "row_parallel": plan["row_parallel"]}
+        if split_us is not None:
+            pt.update({"split_merge_us": round(split_us, 2), "split_len": SPLIT_DECODE_LEN,
+                       "split_merge_frac_of_roofline": round(t_roof_us / split_us, 4)})
         points.append(pt)
         log(f"grid {w.name}: {us:.2f} us (hot {hot_us:.2f}), {pt['kv_gbs']:.0f} GB/s K+V, "
             f"{pt['total_gbs']:.0f} GB/s total, {tfs:.1f} TFLOP/s, {t_roof_us / us:.1%} of roofline"
-            f"{' (launch-bound)' if pt['launch_bound'] else ''}")
+            f"{' (launch-bound)' if pt['launch_bound'] else ''}"
+            f"{f'; split-KV + merge {split_us:.2f} us' if split_us is not None else ''}")
         del bufs, q, k, v
         torch.cuda.empty_cache()
     with open(path, "w") as f:
