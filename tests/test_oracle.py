@@ -17,6 +17,7 @@ from fractions import Fraction
 
 import pytest
 import torch
+from hypothesis import given, settings, strategies as st
 import torch.nn.functional as F
 from torch.nn.attention.bias import causal_lower_right
 
@@ -370,6 +371,51 @@ def test_brute_force_decimal_tiny(causal, window, seed):
     o_ref, l_ref = _decimal_reference(q, k, v, 0.6, causal, window)
     assert (o - o_ref).abs().max().item() < 1e-13
     assert (lse - l_ref).abs().max().item() < 1e-13
+
+
+@st.composite
+def tiny_problem(draw):
+    """A random tiny attention problem: shapes, mask, scale and value spread."""
+    n_kv_h = draw(st.integers(1, 2))
+    group = draw(st.integers(1, 3))
+    T = draw(st.integers(1, 3))
+    causal = draw(st.booleans())
+    window = draw(st.integers(0, 6))
+    lo = T if (causal or window > 0) else 1
+    s_k = draw(st.integers(lo, 8))
+    return dict(b=draw(st.integers(1, 2)), T=T, n_h=n_kv_h * group, n_kv_h=n_kv_h, s_k=s_k,
+                hd=draw(st.sampled_from([1, 2, 4, 8])), causal=causal, window=window,
+                scale=draw(st.sampled_from([0.25, 0.6, -0.5, 1.5])), sigma=draw(st.sampled_from([0.5, 2.0])),
+                seed=draw(st.integers(0, 10_000)))
+
+
+@settings(max_examples=40, deadline=None, derandomize=True)
+@given(tiny_problem())
+def test_brute_force_decimal_random_tiny_shapes(pb):
+    """Random tiny shapes, every mask combination, GQA groups of 1..3: the
+    oracle against exact dot products with exp/ln at 40 digits.  A row that
+    sees no key is O = 0, lse = -inf in the oracle and has no brute-force
+    value."""
+    q, k, v = qkv(pb["b"], pb["T"], pb["n_h"], pb["n_kv_h"], pb["s_k"], pb["hd"], seed=pb["seed"], sigma=pb["sigma"])
+    o, lse = oracle.attention(q, k, v, pb["scale"], causal=pb["causal"], window=pb["window"])
+    o_ref, l_ref = _decimal_reference(q, k, v, pb["scale"], pb["causal"], pb["window"])
+    assert (o - o_ref).abs().max().item() < 1e-12
+    assert (lse - l_ref).abs().max().item() < 1e-12
+
+
+@settings(max_examples=40, deadline=None, derandomize=True)
+@given(tiny_problem(), st.integers(1, 8))
+def test_split_merge_equals_unsplit_random_tiny_shapes(pb, split_len):
+    """Any partition length: the partitions merged by the D5 formula give the
+    unsplit attention."""
+    q, k, v = qkv(pb["b"], pb["T"], pb["n_h"], pb["n_kv_h"], pb["s_k"], pb["hd"], seed=pb["seed"], sigma=pb["sigma"])
+    o, lse = oracle.attention(q, k, v, pb["scale"], causal=pb["causal"], window=pb["window"])
+    op, lp = oracle.split(q, k, v, pb["scale"], split_len, causal=pb["causal"], window=pb["window"])
+    om, lm = oracle.merge(op, lp)  # rows [b, n_h, T]
+    assert (om.permute(0, 2, 1, 3) - o).abs().max().item() < 1e-13
+    fin = torch.isfinite(lse)
+    assert torch.equal(fin, torch.isfinite(lm))
+    assert (lm[fin] - lse[fin]).abs().max().item() < 1e-13 if fin.any() else True
 
 
 def test_large_scores_do_not_overflow():
