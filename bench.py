@@ -16,6 +16,9 @@ Also reported on the same line:
                 merge) on the host cores, as KV-read GB/s.
   ragged_decode the same decode shapes with per-row key counts uniform on
                 1..8192 (split + merge), as GB/s of the K/V actually read.
+  sharded_decode_one_gpu_share
+                one GPU's share of the decode workload sharded over 8 GPUs
+                by KV head or by sequence, at its real shape (cold).
   mx_output     the largest causal prefill point with MX-coded output
                 (FP8 E4M3 and FP4 E2M1 with E8M0 block scales).
   attainable    what this GPU sustains: a 2 GiB streaming read (plain and
@@ -211,6 +214,66 @@ def run_ragged_decode(args, torch, fa, I):
 
 SPLIT_DECODE_LEN = 128  # keys per partition when the grid times MQA decode as split-KV + merge
 WARM_MS = 30.0  # GPU time replayed before timing: clocks settle under sustained load
+
+
+def run_shards(torch, fa, I):
+    """One GPU's share of the GQA split-KV decode workload sharded over
+    I.SHARDS GPUs, at its real shape.  Each share holds 128 MiB of K/V, which
+    the Infinity Cache would keep, so K/V replicas are rotated through at
+    least 512 MiB (graph-timed, cold).
+      by KV head: b32, 8 query heads over one KV head, 8192 keys; split into
+        64 partitions of 128 + LSE merge (nothing to exchange);
+      by sequence: b32, h64/kv8, 1024 keys; its 8 partitions go to slots
+        0..7 of the 64-slot fp32 partial buffer (the other GPUs fill the
+        rest); after the exchange, the owner of 8 query heads merges their 64
+        slots.  The exchange itself (fp32 partials over xGMI) is not timed."""
+    out = []
+    for w in (I.HEAD_SHARD_DECODE, I.SEQ_SHARD_DECODE):
+        seq = w is I.SEQ_SHARD_DECODE
+        n_total = w.n_split * (I.SHARDS if seq else 1)
+        q, k, v = I.make_qkv(w, device="cuda")
+        kv = 4 * w.batch * w.n_kv_h * w.s_k * w.hd
+        reps = max(1, math.ceil(512 * 2**20 / kv))
+        ins = [(q, k, v) if r == 0 else (q.clone(), k.clone(), v.clone()) for r in range(reps)]
+        o_part = torch.empty((w.batch, w.n_h, 1, n_total, w.hd), dtype=torch.float32, device="cuda")
+        lse_part = torch.empty((w.batch, w.n_h, 1, n_total), dtype=torch.float32, device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty((w.batch, w.n_h, 1), dtype=torch.float32, device="cuda")
+
+        def mk(x):
+            def step():
+                st = torch.cuda.current_stream()
+                if seq:
+                    fa.fmha_decode_splitkv_segment(x[0], x[1], x[2], o_part, lse_part, split_len=w.split_len,
+                                                   part_offset=0, scale=w.scale, stream=st)
+                else:
+                    fa.fmha_decode_splitkv(x[0], x[1], x[2], o_part, lse_part, split_len=w.split_len, scale=w.scale,
+                                           stream=st)
+                    fa.fmha_lse_merge(o_part, lse_part, o, lse, stream=st)
+            return step
+        us = rotated_time_us(torch, [mk(x) for x in ins])
+        line = {"workload": w.name, "us_per_step": round(us, 2), "kv_gbs": round(kv / (us * 1e-6) / 1e9, 1),
+                "frac_of_hbm_peak": round(kv / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "rotated_replicas": reps}
+        if seq:
+            # after the exchange: 8 query heads x 64 slots per batch row
+            heads = w.n_h // I.SHARDS
+            op_own = torch.zeros((w.batch, heads, 1, n_total, w.hd), dtype=torch.float32, device="cuda")
+            lp_own = torch.zeros((w.batch, heads, 1, n_total), dtype=torch.float32, device="cuda")
+            o_own = torch.empty((w.batch, 1, heads, w.hd), dtype=torch.bfloat16, device="cuda")
+            m_us = rotated_time_us(torch, [lambda: fa.fmha_lse_merge(op_own, lp_own, o_own, None,
+                                                                      stream=torch.cuda.current_stream())])
+            sent = w.batch * w.n_h * w.n_split * (w.hd + 1) * 4 * (I.SHARDS - 1) // I.SHARDS
+            line.update({"step": f"fmha_decode_splitkv_segment: {w.n_split} partitions into slots 0..{w.n_split - 1} "
+                                 f"of {n_total}", "merge_after_exchange_us": round(m_us, 2),
+                         "exchange_bytes_per_gpu": sent})
+        else:
+            line["step"] = "fmha_decode_splitkv + fmha_lse_merge"
+        log(f"shard {w.name}: {us:.2f} us/step, {line['kv_gbs']:.0f} GB/s of K/V"
+            + (f", merge after exchange {line['merge_after_exchange_us']:.2f} us" if seq else ""))
+        out.append(line)
+        del ins, q, k, v, o_part, lse_part
+        torch.cuda.empty_cache()
+    return out
 
 
 def graph_time_us(torch, calls, reps):
@@ -456,6 +519,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-ragged", action="store_true",
                     help="skip the ragged decode line (profiler runs of the headline kernel)")
+    ap.add_argument("--no-shards", action="store_true",
+                    help="skip the per-GPU share lines of the sharded decode (profiler runs of the headline kernel)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only-prefill", action="store_true",
                     help="time only the prefill workloads (for profiler runs); prints no JSON line")
@@ -500,6 +565,7 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
     ragged = None if args.no_ragged else run_ragged_decode(args, torch, fa, I)
+    shards = None if args.no_shards else run_shards(torch, fa, I)
     prefill = None if args.no_prefill else run_prefill(torch, fa, I)
     mx_out = None if args.no_prefill else run_mx_output(torch, fa, I)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(res, args.cpu_seconds)
@@ -539,6 +605,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": prefill,
         "ragged_decode": ragged,
+        "sharded_decode_one_gpu_share": shards,
         "mx_output": mx_out,
     }
     print(json.dumps(line), flush=True)

@@ -133,6 +133,16 @@ def gqa_causal_prefill_long(T: int, hd: int, batch: int = 2, n_h: int = 32, n_kv
 
 LONG_PREFILL = gqa_causal_prefill_long(4096, 128)
 
+# One GPU's share of the GQA split-KV decode workload sharded over 8 GPUs:
+# by KV head (one KV head and its 8 query heads per GPU), or by sequence
+# (1024 of the 8192 keys per GPU, its 8 partitions written into its slots of
+# a 64-slot partial buffer that is exchanged and merged once).
+HEAD_SHARD_DECODE = Workload("gqa_splitkv_decode_head_shard_b32_h8_kv1_sk8192_hd128", 32, 8, 1, 1, 8192, 128,
+                             v_dist="uniform", split_len=128)
+SEQ_SHARD_DECODE = Workload("gqa_splitkv_decode_seq_shard_b32_h64_kv8_sk1024_hd128", 32, 64, 8, 1, 1024, 128,
+                            v_dist="uniform", split_len=128)
+SHARDS = 8
+
 # A ragged decode batch: the GQA split-KV workload's shapes with per-row key
 # counts drawn uniformly from 1..s_k (the cache holds s_k per row).
 RAGGED_DECODE = Workload("gqa_ragged_decode_b32_h64_kv8_skmax8192_hd128", 32, 64, 8, 1, 8192, 128,

@@ -110,6 +110,46 @@ def test_gqa_splitkv_decode_full_size():
         assert perr <= 1e-2 and lerr <= 1e-3, (perr, lerr)
 
 
+def test_head_shard_share_full_size():
+    """One GPU's share of the GQA decode workload sharded by KV head (8 query
+    heads over one KV head, 8192 keys), split + merge: sampled batches against
+    the oracle."""
+    w = I.HEAD_SHARD_DECODE
+    q, k, v = I.make_qkv(w, device=DEV)
+    o, lse, _, _ = gpu_split(q, k, v, w.scale, w.split_len)
+    for bi in (0, 17, w.batch - 1):
+        qs, ks, vs = (x[bi:bi + 1].cpu() for x in (q, k, v))
+        o_ref, lse_ref = oracle.attention(qs, ks, vs, w.scale)
+        check_attention(o[bi:bi + 1], lse[bi:bi + 1], o_ref, lse_ref, what=f"{w.name} batch {bi}")
+
+
+def test_sequence_shards_reproduce_the_unsharded_partials():
+    """The GQA decode workload sharded by sequence: each of 8 shares (1024
+    keys, a strided view of the cache) writes its 8 partitions into its slots
+    of one 64-slot buffer.  Partition boundaries coincide with the unsharded
+    split, so the partials and the merged output are bitwise those of the
+    unsharded call; one batch row is also checked against the oracle."""
+    w = I.GQA_SPLITKV_DECODE
+    q, k, v = I.make_qkv(w, device=DEV)
+    o, lse, o_part, lse_part = gpu_split(q, k, v, w.scale, w.split_len)
+    span = w.s_k // I.SHARDS
+    per = span // w.split_len
+    op = nan_f32(w.batch, w.n_h, 1, w.n_split, w.hd)
+    lp = nan_f32(w.batch, w.n_h, 1, w.n_split)
+    for g in range(I.SHARDS):
+        ks, vs = k[:, g * span:(g + 1) * span], v[:, g * span:(g + 1) * span]
+        fa.fmha_decode_splitkv_segment(q, ks, vs, op, lp, split_len=w.split_len, part_offset=g * per, scale=w.scale)
+    om = nan_bf16(w.batch, 1, w.n_h, w.hd)
+    lm = nan_f32(w.batch, w.n_h, 1)
+    fa.fmha_lse_merge(op, lp, om, lm)
+    torch.cuda.synchronize()
+    assert torch.equal(op, o_part) and torch.equal(lp, lse_part)
+    assert torch.equal(om, o) and torch.equal(lm, lse)
+    bi = 11
+    o_ref, lse_ref = oracle.attention(*(x[bi:bi + 1].cpu() for x in (q, k, v)), w.scale)
+    check_attention(om[bi:bi + 1], lm[bi:bi + 1], o_ref, lse_ref, what="sequence-sharded merge")
+
+
 def test_gqa_splitkv_decode_small_full_compare():
     """Same shape class at a size the oracle checks completely."""
     w = I.Workload("gqa_splitkv_small", 3, 64, 8, 1, 1000, 128, v_dist="uniform", split_len=128)
