@@ -150,6 +150,33 @@ def test_sequence_shards_reproduce_the_unsharded_partials():
     check_attention(om[bi:bi + 1], lm[bi:bi + 1], o_ref, lse_ref, what="sequence-sharded merge")
 
 
+def test_decode_over_16m_keys_fused_and_split():
+    """A 2^24-key cache (4 GiB of K/V, MQA group 4, hd 64): the fused kernel
+    walks every key with one workgroup, the split runs 4096 partitions of
+    4096 keys and merges them; both against the oracle over every key."""
+    w = I.Workload("decode_b1_h4_kv1_sk16M_hd64", 1, 4, 1, 1, 1 << 24, 64)
+    q, k, v = I.make_qkv(w, device=DEV)
+    o, lse = gpu_forward(q, k, v, w.scale)
+    o2, lse2, _, _ = gpu_split(q, k, v, w.scale, 4096)
+    o_ref, lse_ref = oracle.attention(q.cpu(), k.cpu(), v.cpu(), w.scale)
+    check_attention(o, lse, o_ref, lse_ref, what="fused over 2^24 keys")
+    check_attention(o2, lse2, o_ref, lse_ref, what="split 4096 x 4096 + merge over 2^24 keys")
+
+
+def test_causal_prefill_at_the_query_limit():
+    """T = s_k = 2^20, the largest T the library accepts (row-parallel kernel,
+    hd 64): sampled rows against the oracle as decodes at their positions."""
+    T = 1 << 20
+    w = I.Workload("causal_prefill_b1_h1_T1M_hd64", 1, 1, 1, T, T, 64, causal=True)
+    assert fa.fmha_attention_plan(1, 1, 1, T, T, 64, causal=True)["row_parallel"] == 1
+    q, k, v = I.make_qkv(w, device=DEV)
+    o, lse = gpu_forward(q, k, v, w.scale, causal=True)
+    for i in (0, 1, 63, 64, 4097, (1 << 19) - 1, 1 << 19, T - 1):
+        o_ref, lse_ref = oracle.attention(q[:, i:i + 1].cpu(), k[:, :i + 1].cpu(), v[:, :i + 1].cpu(), w.scale,
+                                          causal=True)
+        check_attention(o[:, i:i + 1], lse[:, :, i:i + 1], o_ref, lse_ref, what=f"row {i} of T = 2^20")
+
+
 def test_gqa_splitkv_decode_small_full_compare():
     """Same shape class at a size the oracle checks completely."""
     w = I.Workload("gqa_splitkv_small", 3, 64, 8, 1, 1000, 128, v_dist="uniform", split_len=128)
