@@ -1,0 +1,58 @@
+"""The benchmark's algorithmic work counts (host arithmetic, no GPU) against
+closed forms: visible query-key pairs under the masks, and the byte and flop
+totals of the workloads whose roofline the benchmark reports."""
+import pytest
+
+import bench
+from head_attention_fmha_amd import inputs as I
+
+
+def pairs_of(flops, w):
+    return flops / (4.0 * w.hd * w.batch * w.n_h)
+
+
+@pytest.mark.parametrize("w", I.MHA_PREFILL_GRID, ids=lambda w: w.name)
+def test_causal_pairs_closed_form(w):
+    """Queries at the last T positions under a causal mask see
+    T (s_k - T) + T (T + 1) / 2 keys in all."""
+    flops, _, kv = bench.forward_work(w)
+    assert pairs_of(flops, w) == w.T * (w.s_k - w.T) + w.T * (w.T + 1) // 2
+    # every key is visible to the last query: K and V are read whole, once
+    assert kv == 4 * w.batch * w.n_kv_h * w.s_k * w.hd
+
+
+def test_sliding_window_prefill_work():
+    """Causal + window W with W <= position + 1 for every query: T W pairs;
+    the keys seen by any query are the last T + W - 1."""
+    w = I.SWA_MQA_PREFILL
+    flops, byts, kv = bench.forward_work(w)
+    assert pairs_of(flops, w) == w.T * w.window
+    assert kv == 4 * w.batch * w.n_kv_h * (w.T + w.window - 1) * w.hd
+    assert round(flops / 1e9, 3) == 1.074
+    assert round(byts / 2**20, 2) == 9.01
+
+
+def test_largest_causal_prefill_point():
+    flops, byts, _ = bench.forward_work(I.mha_causal_prefill(128, 512, 512))
+    assert round(flops / 1e9, 3) == 15.049
+    assert round(byts / 2**20, 2) == 160.06
+
+
+def test_unmasked_decode_work():
+    """Decode without a mask: every key, once; Q + O in bf16 and lse in fp32."""
+    for w in [I.SINGLE_HEAD_DECODE] + I.MQA_DECODE_GRID:
+        flops, byts, kv = bench.forward_work(w)
+        assert pairs_of(flops, w) == w.s_k
+        assert kv == 4 * w.batch * w.n_kv_h * w.s_k * w.hd
+        assert byts == kv + 2 * 2 * w.batch * w.n_h * w.hd + 4 * w.batch * w.n_h
+
+
+def test_split_decode_bytes_per_launch():
+    """The GQA split-KV decode kernel reads K, V, Q and writes the fp32
+    partials: 1 141 899 264 bytes per launch; K + V alone are 1 GiB."""
+    kv, split_kernel, merge_kernel = bench.decode_bytes(I.GQA_SPLITKV_DECODE)
+    assert kv == 2**30
+    assert split_kernel == 1_141_899_264
+    w = I.GQA_SPLITKV_DECODE
+    partials = 4 * w.batch * w.n_h * w.n_split * (w.hd + 1)
+    assert merge_kernel == partials + 2 * w.batch * w.n_h * w.hd + 4 * w.batch * w.n_h
