@@ -582,6 +582,49 @@ def test_split_then_merge_matches_oracle(hd, split_len, causal, window, T):
 
 
 @pytest.mark.parametrize("hd", [64, 128, 256, 512])
+def test_split_mqa_head_stride_zero_is_bitwise_one_kv_head(hd):
+    """Split-KV with K/V given once per query head at head stride 0 runs as
+    one KV head: the partials are bitwise those of n_kv_h = 1."""
+    b, n_h, s_k = 3, 16, 700
+    q = I.randn_bf16((b, 1, n_h, hd), 60 + hd)
+    k = I.randn_bf16((b, s_k, 1, hd), 61 + hd).to(DEV)
+    v = I.randn_bf16((b, s_k, 1, hd), 62 + hd).to(DEV)
+    a = gpu_split(q, k, v, 0.07, 128)
+    c = gpu_split(q, k.expand(b, s_k, n_h, hd), v.expand(b, s_k, n_h, hd), 0.07, 128)
+    for x, y in zip(a, c):
+        assert torch.equal(x, y)
+
+
+def test_split_and_merge_with_strided_layouts():
+    """Split-KV on BHSD-ordered Q memory and padded K/V token strides, merged
+    into a strided output view; nothing outside the view is written."""
+    b, T, n_h, n_kv_h, s_k, hd, split_len = 2, 5, 8, 2, 900, 128, 128
+    scale = 1.0 / math.sqrt(hd)
+    q = I.randn_bf16((b, T, n_h, hd), 71)
+    k = I.randn_bf16((b, s_k, n_kv_h, hd), 72)
+    v = I.randn_bf16((b, s_k, n_kv_h, hd), 73)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=True, window=300)
+    q_bhsd = q.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3)
+    kpad = torch.zeros((b, s_k, n_kv_h + 1, hd + 64), dtype=torch.bfloat16, device=DEV)
+    kpad[:, :, :n_kv_h, :hd] = k.to(DEV)
+    vpad = torch.zeros((b, s_k + 5, n_kv_h, hd), dtype=torch.bfloat16, device=DEV)
+    vpad[:, :s_k] = v.to(DEV)
+    k_view, v_view = kpad[:, :, :n_kv_h, :hd], vpad[:, :s_k]
+    ns = fa.n_split_for(s_k, split_len)
+    o_part = nan_f32(b, n_h, T, ns, hd)
+    lse_part = nan_f32(b, n_h, T, ns)
+    fa.fmha_decode_splitkv(q_bhsd, k_view, v_view, o_part, lse_part, split_len=split_len, scale=scale,
+                           window=300, causal=True)
+    obuf = nan_bf16(b, n_h, T, hd + 16)
+    o_view = obuf[..., :hd].permute(0, 2, 1, 3)
+    lse = nan_f32(b, n_h, T)
+    fa.fmha_lse_merge(o_part, lse_part, o_view, lse)
+    torch.cuda.synchronize()
+    check_attention(o_view, lse, o_ref, lse_ref, what="strided split + merge")
+    assert torch.isnan(obuf[..., hd:].float()).all(), "writes outside the output view"
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
 @pytest.mark.parametrize("n_split", [1, 3, 64, 77])
 def test_merge_kernel_against_oracle_merge(hd, n_split):
     b, n_h, T = 3, 5, 2
