@@ -235,6 +235,68 @@ def test_ragged_shapes_all_masks(hd, heads, T):
         check_attention(o, lse, o_ref, lse_ref, what=f"hd{hd} h{n_h}/{n_kv_h} T{T} sk{s_k} c{causal} w{window}")
 
 
+def _one_hot_problem(b, T, n_h, n_kv_h, hd, s_k=64):
+    """Key j of every KV head is the unit vector on column j * (hd / s_k), so
+    the codes spread over every 16-column block; query (b, t, h) carries the
+    code of key (5 t + 3 h + b) mod s_k.  V[j, d] = ((37 j + 11 d) mod 251 -
+    125) / 256 is exact in bf16 and differs across keys and columns.  With
+    scale 200 every other key's weight is exp(-200), zero in fp32, so O is the
+    target key's V row bit for bit."""
+    stride = hd // s_k
+    k = torch.zeros((b, s_k, n_kv_h, hd), dtype=torch.bfloat16)
+    for j in range(s_k):
+        k[:, j, :, j * stride] = 1.0
+    q = torch.zeros((b, T, n_h, hd), dtype=torch.bfloat16)
+    target = torch.zeros((b, T, n_h), dtype=torch.long)
+    for bi, t, h in itertools.product(range(b), range(T), range(n_h)):
+        target[bi, t, h] = (5 * t + 3 * h + bi) % s_k
+        q[bi, t, h, target[bi, t, h] * stride] = 1.0
+    jj = torch.arange(s_k).view(s_k, 1)
+    dd = torch.arange(hd).view(1, hd)
+    vrow = (((37 * jj + 11 * dd) % 251 - 125).float() / 256).to(torch.bfloat16)
+    v = vrow.view(1, s_k, 1, hd).expand(b, s_k, n_kv_h, hd).contiguous()
+    expect = vrow[target]  # [b, T, n_h, hd]
+    return q, k, v, expect
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+@pytest.mark.parametrize("heads", [(8, 8), (16, 2), (12, 1)], ids=["mha", "gqa8", "mqa12"])
+@pytest.mark.parametrize("T", [1, 19])
+def test_one_hot_attention_returns_the_target_v_row_exactly(hd, heads, T):
+    """Regression for a wrong V-operand layout and for Q columns read in the
+    wrong blocks: one-hot attention over structured V, fused and split."""
+    n_h, n_kv_h = heads
+    q, k, v, expect = _one_hot_problem(2, T, n_h, n_kv_h, hd)
+    o, lse = gpu_forward(q, k, v, 200.0)
+    assert torch.equal(o.cpu(), expect)
+    assert torch.allclose(lse.cpu(), torch.full_like(lse.cpu(), 200.0), rtol=0, atol=1e-3)
+    o2, _, _, _ = gpu_split(q, k, v, 200.0, 16)
+    assert torch.equal(o2.cpu(), expect)
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+@pytest.mark.parametrize("s_k", [1, 7, 100, 127, 129, 200])
+def test_memory_past_the_cache_is_never_read(hd, s_k):
+    """K and V are views of the first s_k rows of buffers whose later rows
+    hold NaN: a read past the last key would reach the output (a masked key
+    still multiplies its V row by its zero weight)."""
+    b, n_h, n_kv_h, T = 2, 8, 2, min(s_k, 5)
+    q = I.randn_bf16((b, T, n_h, hd), 90 + s_k)
+    k = I.randn_bf16((b, s_k, n_kv_h, hd), 91 + s_k)
+    v = I.randn_bf16((b, s_k, n_kv_h, hd), 92 + s_k)
+    kbuf = nan_bf16(b, s_k + 64, n_kv_h, hd)
+    vbuf = nan_bf16(b, s_k + 64, n_kv_h, hd)
+    kbuf[:, :s_k] = k.to(DEV)
+    vbuf[:, :s_k] = v.to(DEV)
+    scale = 1.0 / math.sqrt(hd)
+    for causal in (False, True):
+        o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=causal)
+        o, lse = gpu_forward(q, kbuf[:, :s_k], vbuf[:, :s_k], scale, causal)
+        check_attention(o, lse, o_ref, lse_ref, what=f"s_k {s_k} causal {causal}")
+        o2, lse2, _, _ = gpu_split(q, kbuf[:, :s_k], vbuf[:, :s_k], scale, 64, causal)
+        check_attention(o2, lse2, o_ref, lse_ref, what=f"split s_k {s_k} causal {causal}")
+
+
 @pytest.mark.parametrize("hd", [64, 128, 256, 512])
 def test_single_key_is_exact(hd):
     """s_k = 1: the weight is exactly 1, so O is V_0 bit for bit."""
