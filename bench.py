@@ -9,11 +9,16 @@ inputs resident in HBM.  The 1 GiB of K/V is four times the Infinity Cache,
 so every step streams it from HBM.
 
 Also reported on the same line:
-  roofline      the split kernel (the dominant one): algorithmic bytes per
-                launch / its mean duration from HIP events recorded around
-                each launch on the launch stream, against 8 TB/s.
-  cpu_baseline  the fp64 CPU oracle computing the same workload (split +
-                merge) on the host cores, as KV-read GB/s.
+  repeats       the timed region measured five more times (median beside
+                the contract's single region).
+  roofline      the split kernel (the dominant one; its name is the one the
+                library's plan query gives): algorithmic bytes per launch /
+                its duration, the median of five timings of K back-to-back
+                launches with nothing between them, against 8 TB/s.
+  cpu_baseline  the fp64 CPU oracle on the host cores, a baseline only: the
+                same decode workload (split + merge) as KV-read GB/s, plus
+                four fused workloads, each with one thread and with the
+                host's share of threads; core count and CPU model recorded.
   ragged_decode the same decode shapes with per-row key counts uniform on
                 1..8192 (split + merge), as GB/s of the K/V actually read.
   sharded_decode_one_gpu_share
@@ -137,44 +142,48 @@ def run_decode(args, torch, fa, I):
     def merge():
         fa.fmha_lse_merge(o_part, lse_part, o, lse, stream=stream)
 
-    for _ in range(args.warmup):
-        split()
-        merge()
-    torch.cuda.synchronize()
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    # the timed steps: nothing but the two launches between the two events
-    t0, t1 = E(), E()
-    t0.record(stream)
-    for _ in range(args.steps):
-        split()
-        merge()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-    # per-kernel durations from events around each launch, in a second pass
-    # (the events themselves add a few microseconds per step)
-    evs = [(E(), E(), E()) for _ in range(args.steps)]
-    for a, b, c in evs:
+
+    def timed_steps(fn, n):
+        """ms per call of n back-to-back calls of fn, between two events on the
+        launch stream (nothing else in between)."""
+        a, b = E(), E()
         a.record(stream)
-        split()
+        for _ in range(n):
+            fn()
         b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    def step():
+        split()
         merge()
-        c.record(stream)
+
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
-    split_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / args.steps
-    merge_ms = sum(b.elapsed_time(c) for _, b, c in evs) / args.steps
+    # the timed steps: nothing but the two launches between the two events
+    ms_per_step = timed_steps(step, args.steps)
+    # the same measurement repeated five more times (reported beside it)
+    repeats = [timed_steps(step, args.steps) for _ in range(5)]
+    # the split kernel alone, back to back without instrumentation between its
+    # launches: its duration for the roofline (each launch streams the whole
+    # 1 GiB of K/V and writes the partials, as in the step)
+    split_reps = [timed_steps(split, args.steps) for _ in range(5)]
+    split_ms = sorted(split_reps)[len(split_reps) // 2]
+    merge_ms = max(1e-6, sorted(repeats)[len(repeats) // 2] - split_ms)
     kv_bytes, split_bytes, merge_bytes = decode_bytes(w)
-    log(f"decode: {ms_per_step * 1e3:.1f} us/step (split {split_ms * 1e3:.1f} us, merge {merge_ms * 1e3:.1f} us)")
+    log(f"decode: {ms_per_step * 1e3:.1f} us/step (repeats {', '.join(f'{r * 1e3:.1f}' for r in repeats)}); "
+        f"split alone {split_ms * 1e3:.1f} us, merge + launch gap {merge_ms * 1e3:.1f} us")
     res = {
-        "w": w, "ms_per_step": ms_per_step, "split_ms": split_ms, "merge_ms": merge_ms,
+        "w": w, "ms_per_step": ms_per_step, "repeats_ms": repeats, "split_ms": split_ms, "merge_ms": merge_ms,
+        "split_reps_ms": split_reps,
         "value": kv_bytes / (ms_per_step * 1e-3) / 1e9,
         "split_gbs": split_bytes / (split_ms * 1e-3) / 1e9,
         "merge_gbs": merge_bytes / (merge_ms * 1e-3) / 1e9,
         "split_bytes": split_bytes, "kv_bytes": kv_bytes,
-        "host_qkv": None,
+        "plan": fa.fmha_attention_plan(w.batch, w.n_h, w.n_kv_h, w.T, w.s_k, w.hd, split_len=w.split_len),
     }
-    if not args.no_cpu_baseline:
-        res["host_qkv"] = (q.cpu(), k.cpu(), v.cpu())
     return res
 
 
@@ -490,24 +499,64 @@ def run_attainable(torch):
                    "4096 rounds of 4 independent v_mfma_f32_32x32x16_bf16"}
 
 
-def run_cpu_baseline(res, seconds):
+def cpu_model():
+    """The host CPU's model name (lscpu), or None."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for ln in out.splitlines():
+        if ln.startswith("Model name:"):
+            return ln.split(":", 1)[1].strip()
+    return None
+
+
+def run_cpu_baseline(I, torch, budget_s):
+    """The fp64 oracle on the host cores, as a baseline (not a target): the
+    GQA split-KV decode workload (split + merge, the bench step) and the
+    single-head decode, the largest MQA decode point, the largest causal MHA
+    prefill point and the sliding-window prefill (one fused call each), each
+    with one thread and with the machine's CPU share.  Runs are repeated up to
+    three times within the budget; the median is reported, excluding input
+    generation.  The headline `value` is the decode step with all threads."""
     import oracle
-    w = res["w"]
-    q, k, v = res["host_qkv"]
-    threads = oracle.default_threads()
-    log(f"cpu baseline: fp64 oracle on the full workload, {threads} threads")
-    runs, t0 = 0, time.perf_counter()
-    while True:
-        op, lp = oracle.split(q, k, v, w.scale, w.split_len, threads=threads)
-        oracle.merge(op, lp)
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or el / runs * (runs + 1) > 3 * seconds:
-            break
-    per = el / runs
-    return {"value": round(res["kv_bytes"] / per / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole workload (split into 64 partitions + LSE merge, fp64), run {runs}x, "
-                      f"{per:.2f} s each"}
+    threads_all = oracle.default_threads()
+    decode = I.GQA_SPLITKV_DECODE
+    cases = [("decode", decode), ("fused", I.SINGLE_HEAD_DECODE), ("fused", I.mqa_decode(512, 512)),
+             ("fused", I.SWA_MQA_PREFILL), ("fused", I.mha_causal_prefill(128, 512, 512))]
+    per = []
+    t_start = time.perf_counter()
+    headline = None
+    for kind, w in cases:
+        q, k, v = I.make_qkv(w)  # seeded CPU draws (the oracle's own recipe)
+        flops, byts, kvb = forward_work(w)
+        for threads in (1, threads_all):
+            times = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                if kind == "decode":
+                    op, lp = oracle.split(q, k, v, w.scale, w.split_len, threads=threads)
+                    oracle.merge(op, lp)
+                else:
+                    oracle.attention(q, k, v, w.scale, causal=w.causal, window=w.window, threads=threads)
+                times.append(time.perf_counter() - t0)
+                if time.perf_counter() - t_start > budget_s or times[-1] > budget_s / 8:
+                    break
+            t = sorted(times)[len(times) // 2]
+            rec = {"workload": w.name, "threads": threads, "s": round(t, 6), "runs": len(times),
+                   "kv_gbs": round(kvb / t / 1e9, 4), "gflops": round(flops / t / 1e9, 3)}
+            per.append(rec)
+            log(f"cpu baseline {w.name}, {threads} thread(s): {t:.3f} s")
+            if kind == "decode" and threads == threads_all:
+                headline = rec
+    return {"value": headline["kv_gbs"], "unit": "GB/s", "cores": threads_all, "kind": "oracle",
+            "sample": f"{decode.name}: the whole workload (split into {decode.n_split} partitions + LSE merge, "
+                      f"fp64), median of {headline['runs']} run(s) of {headline['s']:.2f} s on {threads_all} threads",
+            "host_logical_cpus": os.cpu_count(), "host_cpu_model": cpu_model(),
+            "threads_note": f"all-core runs use min(os.cpu_count(), 16) = {threads_all} threads, the host share of "
+                            f"one GPU",
+            "per_workload": per}
 
 
 def main():
@@ -521,7 +570,8 @@ def main():
                     help="skip the ragged decode line (profiler runs of the headline kernel)")
     ap.add_argument("--no-shards", action="store_true",
                     help="skip the per-GPU share lines of the sharded decode (profiler runs of the headline kernel)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=40.0,
+                    help="time budget of the CPU oracle baseline (all its workloads)")
     ap.add_argument("--only-prefill", action="store_true",
                     help="time only the prefill workloads (for profiler runs); prints no JSON line")
     ap.add_argument("--grid", metavar="PATH",
@@ -561,6 +611,10 @@ def main():
         if args.calibrate_copy:
             calibrate_copy()
         return
+    # the attainable-peak probes run first: a few tens of milliseconds of
+    # sustained load that also bring the GPU's clocks to the state every later
+    # measurement runs in
+    att = run_attainable(torch)
     res = run_decode(args, torch, fa, I)
     if args.calibrate_copy:
         calibrate_copy()
@@ -568,15 +622,16 @@ def main():
     shards = None if args.no_shards else run_shards(torch, fa, I)
     prefill = None if args.no_prefill else run_prefill(torch, fa, I)
     mx_out = None if args.no_prefill else run_mx_output(torch, fa, I)
-    cpu = None if args.no_cpu_baseline else run_cpu_baseline(res, args.cpu_seconds)
-    att = run_attainable(torch)
+    cpu = None if args.no_cpu_baseline else run_cpu_baseline(I, torch, args.cpu_seconds)
     best_bw = max(att["hbm_read_gbs"], att["hbm_read_nt_gbs"])
     for p in prefill or []:
         t_att = max(p["alg_mib"] * 2**20 / (best_bw * 1e9), p["alg_gflop"] * 1e9 / (att["mfma_bf16_tflops"] * 1e12))
         p["frac_of_attainable_roofline"] = round(t_att * 1e6 / p["us_per_call"], 4)
     w = res["w"]
     split_us = res["split_ms"] * 1e3
-    split_tag = "attn_kernel_hd128_split_gqa_decode"
+    kernel = res["plan"]["kernel"]
+    # counter summaries are keyed by the kernel family and the workload
+    split_tag = kernel.split("<")[0] + "_hd128_split_gqa_decode"
     line = {
         "metric": METRIC,
         "value": round(res["value"], 2),
@@ -595,11 +650,15 @@ def main():
                    "step": "fmha_decode_splitkv + fmha_lse_merge",
                    "split_us": round(split_us, 2), "merge_us": round(res["merge_ms"] * 1e3, 2),
                    "merge_gbs": round(res["merge_gbs"], 1)},
-        "roofline": {"kernel": "attn_kernel<128, 4, 4, 1, 1, true, true, true> (hd 128; 4 waves = 4 key groups x 1 "
-                               "head part; 1 tile; split; one slice; streamed)", "bound": "hbm",
+        "repeats": {"ms_per_step": [round(r, 5) for r in res["repeats_ms"]],
+                    "median_ms_per_step": round(sorted(res["repeats_ms"])[2], 5),
+                    "how": f"the timed region ({args.steps} steps) measured five more times right after it"},
+        "roofline": {"kernel": kernel, "bound": "hbm",
                      "achieved": round(res["split_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(res["split_gbs"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(split_tag),
                      "alg_bytes_per_launch": res["split_bytes"], "launch_us": round(split_us, 2),
+                     "launch_us_how": f"median of 5 timings of {args.steps} back-to-back split launches "
+                                      f"(no instrumentation between launches)",
                      "frac_of_attainable": round(res["split_gbs"] / best_bw, 4)},
         "attainable": att,
         "cpu_baseline": cpu,

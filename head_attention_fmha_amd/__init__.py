@@ -53,7 +53,8 @@ class FmhaStrides(ctypes.Structure):
 class FmhaPlan(ctypes.Structure):
     _fields_ = [("waves_per_group", ctypes.c_int), ("tiles_per_group", ctypes.c_int),
                 ("one_slice", ctypes.c_int), ("streaming", ctypes.c_int), ("row_parallel", ctypes.c_int),
-                ("workgroups", ctypes.c_int64)]
+                ("workgroups", ctypes.c_int64), ("threads_per_group", ctypes.c_int),
+                ("kernel", ctypes.c_char * 96)]
 
 
 def library_path() -> str:
@@ -255,7 +256,9 @@ def fmha_attention_plan(batch, n_h, n_kv_h, T, s_k, hd, *, window=0, causal=Fals
     plan = FmhaPlan()
     _check(load_library().fmha_attention_plan(batch, n_h, n_kv_h, T, s_k, hd, kv_st, kv_st, int(window),
                                               int(bool(causal)), int(split_len), ctypes.byref(plan)))
-    return {name: getattr(plan, name) for name, _ in FmhaPlan._fields_}
+    out = {name: getattr(plan, name) for name, _ in FmhaPlan._fields_}
+    out["kernel"] = plan.kernel.decode()
+    return out
 
 
 MX_FP8_E4M3 = 1

@@ -8,10 +8,12 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdio>
 
 #include "fmha.h"
 #include "attn_kernel.hpp"
 #include "rows_kernel.hpp"
+#include "stream_kernel.hpp"
 #include "merge_kernel.hpp"
 
 namespace {
@@ -39,16 +41,32 @@ constexpr int kMaxT = 1 << 20;
 constexpr int kMaxKeys = 1 << 30;
 constexpr int64_t kMaxRows = int64_t(1) << 30;  // stacked rows (group * T) per KV head
 
-// Sizes and mask arguments of an attention call.
-int validate_dims(int batch, int n_h, int n_kv_h, int T, int s_k, int hd, int window, int causal) {
+// K and V both with head stride 0 hold one KV head for every query head: the
+// call runs as MQA (n_kv_h = 1), streaming K/V once per batch row.
+int effective_kv_heads(int n_kv_h, const fmha_strides &k_st, const fmha_strides &v_st) {
+    return (k_st.head == 0 && v_st.head == 0) ? 1 : n_kv_h;
+}
+
+// Sizes and mask arguments of an attention call.  The row limit applies to
+// the stacked rows per KV head the kernels will see: with K/V head strides of
+// 0 all n_h query heads share one KV head.
+int validate_dims(int batch, int n_h, int n_kv_h, int T, int s_k, int hd, int window, int causal,
+                  const fmha_strides &k_st, const fmha_strides &v_st) {
     if (batch <= 0 || n_h <= 0 || n_kv_h <= 0 || T <= 0 || s_k <= 0 || hd <= 0) return FMHA_ERR_INVALID_ARG;
     if (n_h % n_kv_h != 0) return FMHA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FMHA_ERR_INVALID_ARG;
     if (window < 0) return FMHA_ERR_INVALID_ARG;
     if ((causal || window > 0) && T > s_k) return FMHA_ERR_INVALID_ARG;
-    if (!hd_supported(hd) || T > kMaxT || s_k > kMaxKeys || (int64_t)(n_h / n_kv_h) * T > kMaxRows)
+    const int kv_eff = effective_kv_heads(n_kv_h, k_st, v_st);
+    if (!hd_supported(hd) || T > kMaxT || s_k > kMaxKeys || (int64_t)(n_h / kv_eff) * T > kMaxRows)
         return FMHA_ERR_UNSUPPORTED;
     return FMHA_OK;
+}
+
+// A dispatch packet counts work-items in 32 bits: a grid of `workgroups`
+// workgroups of `threads` work-items each must stay below 2^32.
+bool grid_fits(int64_t workgroups, int threads) {
+    return workgroups > 0 && workgroups * threads <= int64_t(0xffffffff);
 }
 
 // Shared validation of fmha_forward / fmha_decode_splitkv.
@@ -57,7 +75,7 @@ int validate_attention(const void *q, const void *k, const void *v, const void *
                        const fmha_strides &q_st, const fmha_strides &k_st, const fmha_strides &v_st,
                        const fmha_strides *o_st, int window, int causal) {
     if (!q || !k || !v || !out0 || (out1_required && !out1)) return FMHA_ERR_INVALID_ARG;
-    const int rc = validate_dims(batch, n_h, n_kv_h, T, s_k, hd, window, causal);
+    const int rc = validate_dims(batch, n_h, n_kv_h, T, s_k, hd, window, causal, k_st, v_st);
     if (rc != FMHA_OK) return rc;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out0) || (out1 && !aligned16(out1)))
         return FMHA_ERR_ALIGNMENT;
@@ -70,9 +88,7 @@ int validate_attention(const void *q, const void *k, const void *v, const void *
 FwdParams make_params(const void *q, const void *k, const void *v, int batch, int n_h, int n_kv_h, int T,
                       int s_k, const fmha_strides &q_st, const fmha_strides &k_st, const fmha_strides &v_st,
                       float scale, int window, int causal) {
-    // K and V both with head stride 0 hold one KV head for every query
-    // head: run it as MQA (n_kv_h = 1), streaming K/V once per batch.
-    if (k_st.head == 0 && v_st.head == 0) n_kv_h = 1;
+    n_kv_h = effective_kv_heads(n_kv_h, k_st, v_st);
     FwdParams p{};
     p.q = static_cast<const uint16_t *>(q);
     p.k = static_cast<const uint16_t *>(k);
@@ -118,10 +134,22 @@ bool rows_loads_fit(const FwdParams &p, int hd) {
     return (int64_t)(1024 / (2 * hd) - 1) * st * 2 + 2 * hd < (int64_t(1) << 31);
 }
 
+// Kernel variants the dispatcher launches (one template family each).
+enum Variant : int {
+    kRowsTwoTiles,  // rows_kernel<HD, 2, 32>: 128 rows per workgroup (hd <= 128)
+    kRowsOneTile,   // rows_kernel<HD, 1, rows_chunk_keys(HD)>: 64 rows per workgroup
+    kAttnEight,     // attn_kernel, eight waves, several slices (hd >= 256)
+    kStream,        // stream_kernel<128>: one pass, non-temporal whole-line K/V loads
+    kAttnOneStream, // attn_kernel, one slice, streamed
+    kAttnOne,       // attn_kernel, one slice, K/V shared with other row blocks
+    kAttnTwoTiles,  // attn_kernel, several slices, two tiles per workgroup
+    kAttnOneTile,   // attn_kernel, several slices, one tile per workgroup
+};
+
 // The kernel variant and grid for one call.  A workgroup serves MT 16-row
 // tiles of one (batch, KV head, partition); its NW waves split head-dim
 // columns (NH parts) and keys (NK = NW / NH groups of 32-key slices).
-fmha_plan plan_attention(const FwdParams &p, int hd) {
+fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_out = nullptr) {
     fmha_plan pl{};
     // the widest key range any 16-row tile can see
     int span = p.split_len < p.s_k ? p.split_len : p.s_k;
@@ -170,6 +198,30 @@ fmha_plan plan_attention(const FwdParams &p, int hd) {
     // one slice and one row block per KV head: nothing another workgroup reads
     pl.streaming = (pl.one_slice && row_blocks == 1) ? 1 : 0;
     pl.workgroups = (int64_t)row_blocks * p.n_split * p.n_kv_h * p.batch;
+    pl.threads_per_group = 64 * pl.waves_per_group;
+
+    // the variant, and the kernel template instance it launches
+    int var;
+    const int nh = head_parts(hd);
+    const char *sp = split ? "true" : "false";
+    if (pl.row_parallel) {
+        var = (hd <= 128 && pl.tiles_per_group == 8) ? kRowsTwoTiles : kRowsOneTile;
+        snprintf(pl.kernel, sizeof pl.kernel, "rows_kernel<%d, %d, %d, %s>", hd, var == kRowsTwoTiles ? 2 : 1,
+                 var == kRowsTwoTiles ? 32 : rows_chunk_keys(hd), sp);
+    } else if (pl.one_slice && pl.streaming && hd == 128) {
+        var = kStream;
+        snprintf(pl.kernel, sizeof pl.kernel, "stream_kernel<%d, %s>", hd, sp);
+    } else {
+        const int nw = pl.waves_per_group;
+        const bool one = pl.one_slice, stream = pl.one_slice && pl.streaming;
+        var = nw == 8 ? kAttnEight
+              : stream ? kAttnOneStream
+              : one ? kAttnOne
+              : pl.tiles_per_group == 2 ? kAttnTwoTiles : kAttnOneTile;
+        snprintf(pl.kernel, sizeof pl.kernel, "attn_kernel<%d, %d, %d, %d, %d, %s, %s, %s>", hd, nw, nw / nh, nh,
+                 pl.tiles_per_group, sp, one ? "true" : "false", stream ? "true" : "false");
+    }
+    if (variant_out) *variant_out = var;
     return pl;
 }
 
@@ -182,29 +234,36 @@ void launch_kernel(const FwdParams &p, hipStream_t stream) {
 }
 
 template <int HD, bool SPLIT>
-void launch_hd(const FwdParams &p, const fmha_plan &pl, hipStream_t s) {
-    if (pl.row_parallel) {
-        if (HD <= 128 && pl.tiles_per_group == 8)
-            hipLaunchKernelGGL((fmha::rows_kernel<HD, HD <= 128 ? 2 : 1, 32, SPLIT>), dim3(p.n_units), dim3(256), 0, s,
-                               p);
-        else
+void launch_hd(const FwdParams &p, int var, hipStream_t s) {
+    switch (var) {
+        case kRowsTwoTiles:
+            if constexpr (HD <= 128)
+                hipLaunchKernelGGL((fmha::rows_kernel<HD, 2, 32, SPLIT>), dim3(p.n_units), dim3(256), 0, s, p);
+            break;
+        case kRowsOneTile:
             hipLaunchKernelGGL((fmha::rows_kernel<HD, 1, rows_chunk_keys(HD), SPLIT>), dim3(p.n_units), dim3(256), 0,
                                s, p);
-    } else if (pl.waves_per_group == 8) {
-        // chosen only for several slices per wave (never one-slice), hd >= 256
-        if constexpr (HD >= 256) launch_kernel<HD, 8, 1, SPLIT, false, false>(p, s);
-    } else {
-        if (pl.one_slice && pl.streaming) launch_kernel<HD, 4, 1, SPLIT, true, true>(p, s);
-        else if (pl.one_slice) launch_kernel<HD, 4, 1, SPLIT, true, false>(p, s);
-        else if (pl.tiles_per_group == 2) launch_kernel<HD, 4, 2, SPLIT, false, false>(p, s);
-        else launch_kernel<HD, 4, 1, SPLIT, false, false>(p, s);
+            break;
+        case kAttnEight:
+            // chosen only for several slices per wave (never one-slice), hd >= 256
+            if constexpr (HD >= 256) launch_kernel<HD, 8, 1, SPLIT, false, false>(p, s);
+            break;
+        case kStream:
+            if constexpr (HD == 128)
+                hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT>), dim3(p.n_units), dim3(256), 0, s, p);
+            break;
+        case kAttnOneStream: launch_kernel<HD, 4, 1, SPLIT, true, true>(p, s); break;
+        case kAttnOne: launch_kernel<HD, 4, 1, SPLIT, true, false>(p, s); break;
+        case kAttnTwoTiles: launch_kernel<HD, 4, 2, SPLIT, false, false>(p, s); break;
+        default: launch_kernel<HD, 4, 1, SPLIT, false, false>(p, s); break;
     }
 }
 
 template <bool SPLIT>
 int launch_attention(FwdParams p, int hd, void *stream) {
-    const fmha_plan pl = plan_attention(p, hd);
-    if (pl.workgroups > 0x7fffffff) return FMHA_ERR_UNSUPPORTED;
+    int var = 0;
+    const fmha_plan pl = plan_attention(p, hd, SPLIT, &var);
+    if (!grid_fits(pl.workgroups, pl.threads_per_group)) return FMHA_ERR_UNSUPPORTED;
     p.n_row_blocks = (p.rows + 16 * pl.tiles_per_group - 1) / (16 * pl.tiles_per_group);
     p.n_units = (int)pl.workgroups;
     // only row blocks share data across workgroups; streaming units run best
@@ -212,10 +271,10 @@ int launch_attention(FwdParams p, int hd, void *stream) {
     p.xcd_remap = (p.n_row_blocks > 1 && p.n_units % 8 == 0) ? 1 : 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (hd) {
-        case 64: launch_hd<64, SPLIT>(p, pl, s); break;
-        case 128: launch_hd<128, SPLIT>(p, pl, s); break;
-        case 256: launch_hd<256, SPLIT>(p, pl, s); break;
-        default: launch_hd<512, SPLIT>(p, pl, s); break;
+        case 64: launch_hd<64, SPLIT>(p, var, s); break;
+        case 128: launch_hd<128, SPLIT>(p, var, s); break;
+        case 256: launch_hd<256, SPLIT>(p, var, s); break;
+        default: launch_hd<512, SPLIT>(p, var, s); break;
     }
     return hipGetLastError() == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
 }
@@ -233,7 +292,7 @@ int launch_merge(MergeParams p, int batch, int n_h, int T, int hd, int n_split, 
         default: rpw = fmha::MergeShape<512>::RPW; break;
     }
     const int64_t blocks = (rows + rpw - 1) / rpw;
-    if (rows > 0x7fffffff || blocks > 0x7fffffff) return FMHA_ERR_UNSUPPORTED;
+    if (rows > 0x7fffffff || !grid_fits(blocks, 256)) return FMHA_ERR_UNSUPPORTED;
     p.rows = (int)rows;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)blocks), block(256);
@@ -376,14 +435,16 @@ int fmha_lse_merge_mx(const float *o_part, const float *lse_part, void *o_codes,
 int fmha_attention_plan(int batch, int n_h, int n_kv_h, int T, int s_k, int hd, fmha_strides k_st,
                         fmha_strides v_st, int window, int causal, int split_len, fmha_plan *plan) {
     if (!plan || split_len < 0) return FMHA_ERR_INVALID_ARG;
-    const int rc = validate_dims(batch, n_h, n_kv_h, T, s_k, hd, window, causal);
+    const int rc = validate_dims(batch, n_h, n_kv_h, T, s_k, hd, window, causal, k_st, v_st);
     if (rc != FMHA_OK) return rc;
     const fmha_strides none{0, 0, 0};
     FwdParams p = make_params(nullptr, nullptr, nullptr, batch, n_h, n_kv_h, T, s_k, none, k_st, v_st, 1.f,
                               window, causal);
     p.split_len = split_len == 0 ? s_k : split_len;
     p.n_split = (int)(((int64_t)s_k + p.split_len - 1) / p.split_len);
-    *plan = plan_attention(p, hd);
+    *plan = plan_attention(p, hd, split_len > 0);
+    // the same limit the launch applies
+    if (!grid_fits(plan->workgroups, plan->threads_per_group)) return FMHA_ERR_UNSUPPORTED;
     return FMHA_OK;
 }
 

@@ -56,7 +56,13 @@
  *   - Supported sizes: hd in {64, 128, 256, 512}; 1 <= T <= 2^20;
  *     1 <= s_k <= 2^30; n_h a multiple of n_kv_h with (n_h / n_kv_h) * T
  *     <= 2^30; K and V token strides below 2^32 elements (key rows are
- *     addressed with 32-bit products; FMHA_ERR_UNSUPPORTED otherwise).  With causal or window set, T must not exceed s_k.  Decode
+ *     addressed with 32-bit products; FMHA_ERR_UNSUPPORTED otherwise).
+ *     With K and V head strides both 0 all n_h query heads share one KV
+ *     head, and the row limit reads n_h * T <= 2^30.  A launch must fit one
+ *     dispatch packet: fewer than 2^32 work-items in its grid (for example
+ *     the merge runs 256 per output row, so batch * n_h * T < 2^24);
+ *     FMHA_ERR_UNSUPPORTED otherwise.  With causal or window set, T must not
+ *     exceed s_k.  Decode
  *     (T = 1), short prefill and long prefill (T up to s_k, the prefill the
  *     "Next steps" of CURRENT_ISSUE.md call for) share the entry points.
  */
@@ -251,11 +257,15 @@ int fmha_lse_merge_mx(const float *o_part, const float *lse_part, void *o_codes,
  *   row_parallel     1 when each wave owns whole rows and the waves share
  *                    K/V chunks staged in LDS (many rows per KV head)
  *   workgroups       grid size
+ *   threads_per_group  work-items per workgroup (64 * waves_per_group)
+ *   kernel           NUL-terminated name of the kernel template instance the
+ *                    call launches, e.g. "stream_kernel<128, true>"
  * k_st / v_st matter through their head strides (both 0 = MQA) and their
  * token strides: the row-parallel kernel stages K/V by 1 KiB buffer loads
  * with 32-bit offsets from the load's first key row, so it is chosen only
  * when (1024 / (2 hd) - 1) * token stride * 2 + 2 hd < 2^31 bytes.
- * Errors: as fmha_forward for sizes and mask arguments;
+ * Errors: as fmha_forward for sizes and mask arguments (including
+ * FMHA_ERR_UNSUPPORTED for a grid of 2^32 work-items or more);
  * FMHA_ERR_INVALID_ARG for a null plan or split_len < 0.
  */
 typedef struct {
@@ -265,6 +275,8 @@ typedef struct {
     int streaming;
     int row_parallel;
     int64_t workgroups;
+    int threads_per_group;
+    char kernel[96];
 } fmha_plan;
 
 int fmha_attention_plan(int batch, int n_h, int n_kv_h, int T, int s_k, int hd,

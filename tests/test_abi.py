@@ -241,3 +241,64 @@ def merge_mx(lib, codes=OP, scales=ctypes.c_void_p(0x70000), fmt=2, hd=128, n_sp
 ])
 def test_mx_entry_points_reject(lib, call, kw, code):
     assert call(lib, **kw) == code
+
+
+# ---------------------------------------------------------------------------
+# Size limits that the dispatch packet and the int row index impose
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("args,kw", [
+    # 2 x 2^23 partitions of 128 keys: 2^24 workgroups of 256 work-items = 2^32
+    ((2, 1, 1, 1, 1 << 30, 64), dict(split_len=128)),
+    # causal T = s_k = 2^20 with 64 query heads on one KV head, split at 4096
+    ((1, 64, 1, 1 << 20, 1 << 20, 64), dict(causal=True, split_len=4096)),
+])
+def test_plan_rejects_grids_of_2_32_work_items(lib, args, kw):
+    with pytest.raises(fa.FmhaError) as e:
+        fa.fmha_attention_plan(*args, **kw)
+    assert e.value.status == UNSUPPORTED
+
+
+def test_plan_accepts_the_largest_grid_below_2_32_work_items(lib):
+    # 2^24 - 1 workgroups of 256 work-items (1 x 1 x (2^24 - 1) partitions of one key)
+    got = fa.fmha_attention_plan(1, 1, 1, 1, (1 << 24) - 1, 64, split_len=1)
+    assert got["workgroups"] * got["threads_per_group"] < 1 << 32
+
+
+def test_split_call_rejects_grids_of_2_32_work_items(lib):
+    st = FmhaStrides(0, 64, 64)
+    q_st = FmhaStrides(128, 64, 64)
+    rc = lib.fmha_decode_splitkv(QP, KP, VP, OP, LP, 2, 1, 1, 1, 1 << 30, 64, q_st, st, st, 0.1, 0, 0, 128, None)
+    assert rc == UNSUPPORTED
+
+
+@pytest.mark.parametrize("b,n_h,T,code", [
+    # one 256-work-item workgroup per output row: 2^24 rows reach 2^32 work-items
+    (1, 64, 1 << 18, UNSUPPORTED), (1, 1, 1 << 24, UNSUPPORTED),
+])
+def test_merge_rejects_grids_of_2_32_work_items(lib, b, n_h, T, code):
+    st = FmhaStrides(T * n_h * 64, n_h * 64, 64)
+    assert lib.fmha_lse_merge(QP, KP, OP, None, b, n_h, T, 64, 4, st, None) == code
+
+
+@pytest.mark.parametrize("n_h", [2048, 4096])
+def test_head_stride_zero_counts_every_query_head_as_a_row(lib, n_h):
+    """K/V head strides of 0 run as one KV head, so n_h * T rows must stay
+    within 2^30 exactly as with n_kv_h = 1."""
+    with pytest.raises(fa.FmhaError) as e:
+        fa.fmha_attention_plan(1, n_h, n_h, 1 << 20, 1 << 20, 64, mqa_stride0=True)
+    assert e.value.status == UNSUPPORTED
+    with pytest.raises(fa.FmhaError) as e:
+        fa.fmha_attention_plan(1, n_h, 1, 1 << 20, 1 << 20, 64)
+    assert e.value.status == UNSUPPORTED
+    # the same call with real per-head K/V strides has n_h / n_kv_h = 1 row per position
+    got = fa.fmha_attention_plan(1, n_h, n_h, 1 << 10, 1 << 10, 64)
+    assert got["workgroups"] > 0
+
+
+def test_forward_with_head_stride_zero_rejects_too_many_rows(lib):
+    n_h, T = 2048, 1 << 20
+    q_st = FmhaStrides(T * n_h * 64, n_h * 64, 64)
+    kv_st = FmhaStrides(T * 64, 64, 0)
+    rc = lib.fmha_forward(QP, KP, VP, OP, None, 1, n_h, n_h, T, T, 64, q_st, kv_st, kv_st, q_st, 0.1, 0, 1, None)
+    assert rc == UNSUPPORTED

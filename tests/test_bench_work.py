@@ -56,3 +56,14 @@ def test_split_decode_bytes_per_launch():
     w = I.GQA_SPLITKV_DECODE
     partials = 4 * w.batch * w.n_h * w.n_split * (w.hd + 1)
     assert merge_kernel == partials + 2 * w.batch * w.n_h * w.hd + 4 * w.batch * w.n_h
+
+
+def test_roofline_kernel_is_the_planned_one():
+    """The kernel the bench line names for the roofline is the one the
+    library's plan query says the split decode launches."""
+    import head_attention_fmha_amd as fa
+    w = I.GQA_SPLITKV_DECODE
+    plan = fa.fmha_attention_plan(w.batch, w.n_h, w.n_kv_h, w.T, w.s_k, w.hd, split_len=w.split_len)
+    assert plan["kernel"] == "stream_kernel<128, true>"
+    assert plan["workgroups"] == w.batch * w.n_kv_h * w.n_split
+    assert plan["threads_per_group"] == 256

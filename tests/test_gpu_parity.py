@@ -865,7 +865,7 @@ def test_mx_forward_codes_are_the_quantised_fp32_output(name, dims, split_len, c
     scale = 1.0 / math.sqrt(hd)
     plan_f = fa.fmha_attention_plan(b, n_h, n_kv_h, T, s_k, hd, window=window, causal=causal)
     plan_s = fa.fmha_attention_plan(b, n_h, n_kv_h, T, s_k, hd, window=window, causal=causal, split_len=s_k)
-    assert plan_f == plan_s
+    assert VS.same_variant(plan_f, plan_s), (plan_f, plan_s)
     o_part = nan_f32(b, n_h, T, 1, hd)
     lse_part = nan_f32(b, n_h, T, 1)
     fa.fmha_decode_splitkv(q, k, v, o_part, lse_part, split_len=s_k, scale=scale, window=window, causal=causal)

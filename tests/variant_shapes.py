@@ -44,3 +44,26 @@ EXPECTED = {
     512: {"row-parallel", "eight-waves", "one-slice-streamed", "one-slice-shared", "multi-one-tile",
           "multi-two-tiles"},
 }
+
+
+# position of the SPLIT template argument in each kernel family's name
+_SPLIT_ARG = {"attn_kernel": 5, "rows_kernel": 3, "stream_kernel": 1}
+
+
+def split_twin(kernel: str) -> str:
+    """The name of the split-output instance of a forward kernel instance:
+    the same template arguments with SPLIT = true."""
+    family, args = kernel.split("<", 1)
+    args = args.rstrip(">").split(", ")
+    i = _SPLIT_ARG[family]
+    assert args[i] == "false", kernel
+    args[i] = "true"
+    return f"{family}<{', '.join(args)}>"
+
+
+def same_variant(plan_fwd: dict, plan_split: dict) -> bool:
+    """A forward plan and a split plan launch the same kernel variant (the
+    same template arguments apart from the output mode)."""
+    a = {k: v for k, v in plan_fwd.items() if k != "kernel"}
+    b = {k: v for k, v in plan_split.items() if k != "kernel"}
+    return a == b and split_twin(plan_fwd["kernel"]) == plan_split["kernel"]
