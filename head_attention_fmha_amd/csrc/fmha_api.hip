@@ -134,6 +134,14 @@ bool rows_loads_fit(const FwdParams &p, int hd) {
     return (int64_t)(1024 / (2 * hd) - 1) * st * 2 + 2 * hd < (int64_t(1) << 31);
 }
 
+// The stream kernel stores a workgroup's split partials by buffer stores with
+// 32-bit byte offsets from its first row: its (at most 16) rows lie within
+// 16 * n_split_total rows of hd fp32 values.
+bool stream_offsets_fit(const FwdParams &p, int hd) {
+    const int64_t slots = p.n_split_total > 0 ? p.n_split_total : p.n_split;
+    return (int64_t)16 * slots * hd * 4 < (int64_t(1) << 31);
+}
+
 // Kernel variants the dispatcher launches (one template family each).
 enum Variant : int {
     kRowsTwoTiles,  // rows_kernel<HD, 2, 32>: 128 rows per workgroup (hd <= 128)
@@ -208,7 +216,7 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
         var = (hd <= 128 && pl.tiles_per_group == 8) ? kRowsTwoTiles : kRowsOneTile;
         snprintf(pl.kernel, sizeof pl.kernel, "rows_kernel<%d, %d, %d, %s>", hd, var == kRowsTwoTiles ? 2 : 1,
                  var == kRowsTwoTiles ? 32 : rows_chunk_keys(hd), sp);
-    } else if (pl.one_slice && pl.streaming && hd == 128) {
+    } else if (pl.one_slice && pl.streaming && hd == 128 && stream_offsets_fit(p, hd)) {
         var = kStream;
         snprintf(pl.kernel, sizeof pl.kernel, "stream_kernel<%d, %s>", hd, sp);
     } else {

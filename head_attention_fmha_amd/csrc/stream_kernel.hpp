@@ -32,7 +32,8 @@
 // running max / running sum of the e4ee9fdc commit log of the pages with one
 // slice per wave -- and the four are combined once, in a fixed order,
 // through LDS, each wave combining and storing one quarter of the columns
-// (whole 128-byte lines of fp32 partials per store instruction).  Scores are base 2 (x = q.k * scale * log2 e); O is
+// (whole 128-byte lines of fp32 partials per store instruction, with the
+// device-scope cache policy).  Scores are base 2 (x = q.k * scale * log2 e); O is
 // normalised by the sum of the bf16-rounded weights the PV product consumes
 // and lse uses the fp32 sum, as in attn_kernel.hpp.
 #pragma once
@@ -247,9 +248,12 @@ __global__ __launch_bounds__(256, 4) void stream_kernel(const FwdParams p) {
         const float lse_val = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
         o = o * inv;
         if constexpr (SPLIT) {
-            const int64_t r = (((int64_t)b * p.n_h + h_o) * p.T + t_o) * p.n_split_total + p.part_offset + part;
-            __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(p.o_part + r * HD + c));
-            if (wave == 0 && q == 0) p.lse_part[r] = lse_val;
+            // rows of this workgroup: r0 + ((rr % group) T + rr / group) n_split_total;
+            // byte offsets from the first fit 32 bits (the host checks it)
+            const int64_t r0 = ((int64_t)b * p.n_h + kvh * p.group) * p.T * p.n_split_total + p.part_offset + part;
+            const int64_t dr = ((int64_t)(rr % p.group) * p.T + rr / p.group) * p.n_split_total;
+            store16_device_scope(p.o_part + r0 * HD, (unsigned)((dr * HD + c) * 4), o);
+            if (wave == 0 && q == 0) p.lse_part[r0 + dr] = lse_val;
         } else {
             if (p.out_format != kOutBf16) {
                 // the wave's 32 columns are one MX block, over the 8 lanes of the row

@@ -9,8 +9,16 @@ The 1e-2 bound is read as stated wherever the bf16 output format can meet
 it.  Once |O_ref| >= 2 one bf16 ulp (2^-6 and up) exceeds 1e-2 and rounding
 alone can leave a correct result more than 1e-2 away (e.g. 4.0156 lies
 0.0156 from both of its bf16 neighbours); there the bound is one bf16 ulp
-of the reference value.  Rows attending to one or two keys with large V
-entries reach such magnitudes.
+of the reference value: half an ulp for the output rounding, plus the
+error of the value before rounding.  That error comes from the bf16
+weights the PV product consumes: O = sum p~_j v_j / sum p~_j with
+p~_j = p_j (1 + d_j), |d_j| <= 2^-9, differs from the exact O by at most
+2^-9 * (1 + 2^-8) * sum_j p_j |v_j - O| / sum_j p_j, which for rows this
+large (one or two visible keys with V entries of 2 to 5) reaches a few
+thousandths -- above what half an ulp leaves under 1e-2 in [2, 4), below
+the other half ulp.  Every check records how many elements fell under that
+bound and how close they came to it (`RECORDS`, summed at the end of the
+pytest session).
 """
 import math
 
@@ -22,6 +30,10 @@ def bf16_ulp(x: torch.Tensor) -> torch.Tensor:
     ax = x.abs().clamp_min(2.0 ** -126)
     return torch.pow(2.0, torch.floor(torch.log2(ax)) - 7)
 
+
+# one record per check_attention call: (what, elements, elements under the
+# one-ulp bound, their worst |err| / ulp, max |err|, min cosine, max lse err)
+RECORDS = []
 
 MAX_ABS = 1e-2
 MIN_COS = 0.99999
@@ -56,7 +68,10 @@ def check_attention(o_gpu, lse_gpu, o_ref, lse_ref, *, max_abs=MAX_ABS, min_cos=
     cos = (a[live] * r[live]).sum(1) / (na[live] * nr[live])
     min_c = cos.min().item() if cos.numel() else 1.0
     assert min_c >= min_cos, f"{what}: min cosine {min_c:.7f} < {min_cos}"
-    out = {"max_abs": max_err, "min_cos": min_c, "n_ulp_bound": int((o_ref.abs() >= 2).sum())}
+    big = o_ref.abs() >= 2
+    n_ulp = int(big.sum())
+    ulp_excess = (err[big] / bf16_ulp(o_ref[big])).max().item() if n_ulp else 0.0
+    out = {"max_abs": max_err, "min_cos": min_c, "n_ulp_bound": n_ulp, "ulp_excess": ulp_excess}
     if lse_gpu is not None:
         lg = lse_gpu.detach().to("cpu", torch.float64)
         assert lg.shape == lse_ref.shape
@@ -66,4 +81,8 @@ def check_attention(o_gpu, lse_gpu, o_ref, lse_ref, *, max_abs=MAX_ABS, min_cos=
         lerr = (lg[fin] - lse_ref[fin]).abs().max().item() if fin.any() else 0.0
         assert lerr <= lse_tol, f"{what}: lse err {lerr:.3e} > {lse_tol}"
         out["lse_err"] = lerr
+    RECORDS.append((what, og.numel(), n_ulp, ulp_excess, max_err, min_c, out.get("lse_err", 0.0)))
+    if n_ulp:
+        print(f"[parity] {what}: {n_ulp} of {og.numel()} elements judged by the one-ulp bound "
+              f"(worst |err| = {ulp_excess:.3f} ulp)", flush=True)
     return out

@@ -302,3 +302,17 @@ def test_forward_with_head_stride_zero_rejects_too_many_rows(lib):
     kv_st = FmhaStrides(T * 64, 64, 0)
     rc = lib.fmha_forward(QP, KP, VP, OP, None, 1, n_h, n_h, T, T, 64, q_st, kv_st, kv_st, q_st, 0.1, 0, 1, None)
     assert rc == UNSUPPORTED
+
+
+def test_stream_kernel_serves_the_split_decode_while_its_offsets_fit(lib):
+    """The hd-128 streaming decode runs the stream kernel; with so many
+    partition slots that a workgroup's 16 rows of fp32 partials span 2 GiB or
+    more (its buffer stores take 32-bit offsets) the per-wave kernel runs."""
+    got = fa.fmha_attention_plan(32, 64, 8, 1, 8192, 128, split_len=128)
+    assert got["kernel"] == "stream_kernel<128, true>"
+    ok = fa.fmha_attention_plan(1, 1, 1, 1, (1 << 18) - 1, 128, split_len=1)
+    assert ok["kernel"] == "stream_kernel<128, true>"
+    big = fa.fmha_attention_plan(1, 1, 1, 1, 1 << 18, 128, split_len=1)
+    assert big["kernel"] == "attn_kernel<128, 4, 4, 1, 1, true, true, true>"
+    # fused calls (no partials) with one slice and one row block
+    assert fa.fmha_attention_plan(4, 32, 32, 1, 128, 128)["kernel"] == "stream_kernel<128, false>"
