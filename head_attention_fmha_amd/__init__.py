@@ -9,6 +9,8 @@ fails, the error propagates.
 
 Entry points carry the C names:
   fmha_forward(q, k, v, o, lse=None, *, scale=None, window=0, causal=False)
+  fmha_forward_ws(q, k, v, o, lse=None, workspace=None, *, ...)   (workspace from workspace_for(q, k, ...))
+  fmha_forward_ws_size(batch, n_h, n_kv_h, T, s_k, hd, *, window=0, causal=False, mqa_stride0=False)
   fmha_decode_splitkv(q, k, v, o_part, lse_part, *, split_len, scale=None, window=0, causal=False)
   fmha_lse_merge(o_part, lse_part, o, lse=None)
   fmha_forward_varlen(q, k, v, seqlens_k, o, lse=None, *, scale=None, window=0, causal=False)
@@ -30,7 +32,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["FmhaError", "fmha_forward", "fmha_forward_varlen", "fmha_decode_splitkv", "fmha_decode_splitkv_segment",
+__all__ = ["FmhaError", "fmha_forward", "fmha_forward_ws", "fmha_forward_ws_size", "workspace_for",
+           "fmha_forward_varlen", "fmha_decode_splitkv", "fmha_decode_splitkv_segment",
            "fmha_lse_merge", "fmha_forward_mx", "fmha_lse_merge_mx", "MX_FP8_E4M3", "MX_FP4_E2M1", "mx_shapes",
            "fmha_status_string",
            "fmha_attention_plan", "n_split_for", "library_path", "load_library", "FmhaStrides", "FmhaPlan"]
@@ -72,6 +75,10 @@ def load_library():
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, FmhaStrides
     lib.fmha_forward.argtypes = [P, P, P, P, P, I, I, I, I, I, I, S, S, S, S, F, I, I, P]
     lib.fmha_forward.restype = I
+    lib.fmha_forward_ws.argtypes = [P, P, P, P, P, I, I, I, I, I, I, S, S, S, S, F, I, I, P, ctypes.c_size_t, P]
+    lib.fmha_forward_ws.restype = I
+    lib.fmha_forward_ws_size.argtypes = [I, I, I, I, I, I, S, S, I, I, ctypes.POINTER(ctypes.c_size_t)]
+    lib.fmha_forward_ws_size.restype = I
     lib.fmha_decode_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, S, S, S, F, I, I, I, P]
     lib.fmha_decode_splitkv.restype = I
     lib.fmha_forward_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, S, S, S, S, F, I, I, P]
@@ -156,6 +163,50 @@ def fmha_forward(q, k, v, o, lse=None, *, scale=None, window=0, causal=False, st
     _check(load_library().fmha_forward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, n_h, n_kv_h, T, s_k, hd,
         _st(q), _st(k), _st(v), _st(o), _scale(scale, hd), int(window), int(bool(causal)), _stream(stream)))
+
+
+def fmha_forward_ws_size(batch, n_h, n_kv_h, T, s_k, hd, *, window=0, causal=False, mqa_stride0=False) -> int:
+    """Workspace bytes fmha_forward_ws needs for a call of these sizes (0:
+    it runs fused); see include/fmha.h."""
+    head = 0 if mqa_stride0 else hd
+    kv_st = FmhaStrides(0, n_kv_h * hd, head)
+    out = ctypes.c_size_t(0)
+    _check(load_library().fmha_forward_ws_size(batch, n_h, n_kv_h, T, s_k, hd, kv_st, kv_st, int(window),
+                                               int(bool(causal)), ctypes.byref(out)))
+    return int(out.value)
+
+
+def workspace_for(q, k, *, window=0, causal=False):
+    """A workspace tensor (uint8, on q's device) of the size fmha_forward_ws
+    needs for these inputs, or None when the call runs fused."""
+    b, T, n_h, hd = q.shape
+    _, s_k, n_kv_h, _ = k.shape
+    nbytes = fmha_forward_ws_size(b, n_h, n_kv_h, T, s_k, hd, window=window, causal=causal,
+                                  mqa_stride0=k.stride(2) == 0 and n_kv_h > 1)
+    return torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+
+
+def fmha_forward_ws(q, k, v, o, lse=None, workspace=None, *, scale=None, window=0, causal=False,
+                    stream=None) -> None:
+    """fmha_forward with a workspace (a uint8 device tensor, or None when the
+    call runs fused): few-unit calls split over the keys and merge; see
+    include/fmha.h."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _dev4(t, n)
+    b, T, n_h, hd = q.shape
+    _, s_k, n_kv_h, _ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape) or k.shape[0] != b or k.shape[3] != hd:
+        raise ValueError("shape mismatch between q, k, v, o")
+    _dense(lse, (b, n_h, T), "lse")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws_ptr, ws_bytes = ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+    _check(load_library().fmha_forward_ws(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, n_h, n_kv_h, T, s_k, hd,
+        _st(q), _st(k), _st(v), _st(o), _scale(scale, hd), int(window), int(bool(causal)), ws_ptr, ws_bytes,
+        _stream(stream)))
 
 
 def fmha_decode_splitkv(q, k, v, o_part, lse_part, *, split_len, scale=None, window=0, causal=False,

@@ -14,6 +14,7 @@
 #include "attn_kernel.hpp"
 #include "rows_kernel.hpp"
 #include "stream_kernel.hpp"
+#include "pass_kernel.hpp"
 #include "merge_kernel.hpp"
 
 namespace {
@@ -148,6 +149,7 @@ enum Variant : int {
     kRowsOneTile,   // rows_kernel<HD, 1, rows_chunk_keys(HD)>: 64 rows per workgroup
     kAttnEight,     // attn_kernel, eight waves, several slices (hd >= 256)
     kStream,        // stream_kernel<128>: one pass, non-temporal whole-line K/V loads
+    kPass,          // pass_kernel<HD>: one pass over <= 128 keys, every load up front (hd >= 256)
     kAttnOneStream, // attn_kernel, one slice, streamed
     kAttnOne,       // attn_kernel, one slice, K/V shared with other row blocks
     kAttnTwoTiles,  // attn_kernel, several slices, two tiles per workgroup
@@ -201,6 +203,14 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
             pl.tiles_per_group = (hd <= 128 && groups2 >= 2 * kComputeUnits) ? 8 : 4;
         }
     }
+    // hd 256 / 512 with every tile's keys within one 128-key pass (and not the
+    // row-parallel kernel's many-row work): the one-pass kernel, eight waves
+    const bool pass = !pl.row_parallel && hd >= 256 && span <= 128;
+    if (pass) {
+        pl.waves_per_group = 8;
+        pl.tiles_per_group = 1;
+        pl.one_slice = 1;
+    }
     const int rows_per_group = 16 * pl.tiles_per_group;
     const int row_blocks = (p.rows + rows_per_group - 1) / rows_per_group;
     // one slice and one row block per KV head: nothing another workgroup reads
@@ -216,6 +226,9 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
         var = (hd <= 128 && pl.tiles_per_group == 8) ? kRowsTwoTiles : kRowsOneTile;
         snprintf(pl.kernel, sizeof pl.kernel, "rows_kernel<%d, %d, %d, %s>", hd, var == kRowsTwoTiles ? 2 : 1,
                  var == kRowsTwoTiles ? 32 : rows_chunk_keys(hd), sp);
+    } else if (pass) {
+        var = kPass;
+        snprintf(pl.kernel, sizeof pl.kernel, "pass_kernel<%d, %s>", hd, sp);
     } else if (pl.one_slice && pl.streaming && hd == 128 && stream_offsets_fit(p, hd)) {
         var = kStream;
         snprintf(pl.kernel, sizeof pl.kernel, "stream_kernel<%d, %s>", hd, sp);
@@ -260,8 +273,17 @@ void launch_hd(const FwdParams &p, int var, hipStream_t s) {
             if constexpr (HD == 128)
                 hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT>), dim3(p.n_units), dim3(256), 0, s, p);
             break;
-        case kAttnOneStream: launch_kernel<HD, 4, 1, SPLIT, true, true>(p, s); break;
-        case kAttnOne: launch_kernel<HD, 4, 1, SPLIT, true, false>(p, s); break;
+        case kPass:
+            if constexpr (HD >= 256)
+                hipLaunchKernelGGL((fmha::pass_kernel<HD, SPLIT>), dim3(p.n_units), dim3(512), 0, s, p);
+            break;
+        // one-slice work at hd >= 256 runs the one-pass kernel
+        case kAttnOneStream:
+            if constexpr (HD <= 128) launch_kernel<HD, 4, 1, SPLIT, true, true>(p, s);
+            break;
+        case kAttnOne:
+            if constexpr (HD <= 128) launch_kernel<HD, 4, 1, SPLIT, true, false>(p, s);
+            break;
         case kAttnTwoTiles: launch_kernel<HD, 4, 2, SPLIT, false, false>(p, s); break;
         default: launch_kernel<HD, 4, 1, SPLIT, false, false>(p, s); break;
     }
@@ -313,6 +335,88 @@ int launch_merge(MergeParams p, int batch, int n_h, int T, int hd, int n_split, 
     return hipGetLastError() == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
 }
 
+// ---- few-unit calls split over the keys (fmha_forward_ws) --------------------
+//
+// A call with fewer 16-row tiles than compute units leaves most of the chip
+// idle, each workgroup walking its tile's keys alone (the MQA decode of 128
+// query heads over one KV head has 8 tiles per batch row).  With a workspace
+// the keys are split into partitions -- the split-KV decode of the pages'
+// "D2 multi-CTA" -- so the grid covers the chip, and the D5 merge ("Next
+// steps", item 4 of CURRENT_ISSUE.md) combines them in a second launch.
+
+// fused work per tile (keys x hd) from which the split pays for the second
+// launch and the partial traffic
+constexpr int64_t kSplitMinWork = 96 * 1024;
+
+struct SplitChoice {
+    int split_len = 0;  // 0: run fused
+    int n_split = 1;
+};
+
+SplitChoice choose_split(const FwdParams &p, int hd) {
+    SplitChoice c;
+    const int64_t tiles = (int64_t)((p.rows + 15) / 16) * p.n_kv_h * p.batch;
+    if (tiles >= kComputeUnits) return c;
+    int64_t span = p.s_k;
+    const int ppt = tile_positions(p.group);
+    if (p.causal && p.window > 0 && (int64_t)p.window + ppt - 1 < span) span = p.window + ppt - 1;
+    if (span * hd < kSplitMinWork) return c;
+    // partitions of at most 128 keys (one pass of the one-slice kernels), as
+    // many as it takes to give every compute unit a workgroup
+    const int64_t want = (kComputeUnits + tiles - 1) / tiles;
+    int64_t len = (p.s_k + want - 1) / want;
+    len = ((len + 31) / 32) * 32;
+    if (len > 128) len = 128;
+    if (len >= p.s_k) return c;
+    c.split_len = (int)len;
+    c.n_split = (int)((p.s_k + len - 1) / len);
+    return c;
+}
+
+// workspace layout: o_part [rows][n_split][hd] fp32, then lse_part [rows][n_split]
+// fp32 at the next 256-byte boundary
+int64_t split_workspace_bytes(int64_t rows, int n_split, int hd) {
+    const int64_t o_bytes = (rows * n_split * hd * 4 + 255) / 256 * 256;
+    return o_bytes + rows * n_split * 4;
+}
+
+// fmha_forward through a workspace: split + merge when choose_split says so,
+// the fused call otherwise.  `ws` is device memory of at least the bytes
+// split_workspace_bytes gives (checked by the callers).
+int forward_split_or_fused(FwdParams p, int hd, const SplitChoice &c, void *ws, const fmha_strides &o_st,
+                           void *stream) {
+    if (c.split_len == 0) {
+        p.split_len = p.s_k;
+        p.n_split = 1;
+        p.n_split_total = 1;
+        return launch_attention<false>(p, hd, stream);
+    }
+    const int64_t rows = (int64_t)p.batch * p.n_h * p.T;
+    float *o_part = static_cast<float *>(ws);
+    float *lse_part = reinterpret_cast<float *>(static_cast<unsigned char *>(ws) +
+                                                (rows * c.n_split * hd * 4 + 255) / 256 * 256);
+    uint16_t *o = p.o;
+    float *lse = p.lse;
+    p.o = nullptr;
+    p.lse = nullptr;
+    p.o_part = o_part;
+    p.lse_part = lse_part;
+    p.split_len = c.split_len;
+    p.n_split = c.n_split;
+    p.part_offset = 0;
+    p.n_split_total = c.n_split;
+    int rc = launch_attention<true>(p, hd, stream);
+    if (rc != FMHA_OK) return rc;
+    MergeParams m{};
+    m.o_part = o_part;
+    m.lse_part = lse_part;
+    m.o = o;
+    m.lse = lse;
+    m.o_sb = o_st.batch; m.o_st = o_st.token; m.o_sh = o_st.head;
+    m.out_format = fmha::kOutBf16;
+    return launch_merge(m, p.batch, p.n_h, p.T, hd, c.n_split, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -331,6 +435,39 @@ int fmha_forward(const void *q, const void *k, const void *v, void *o, float *ls
     p.n_split = 1;
     p.n_split_total = 1;
     return launch_attention<false>(p, hd, stream);
+}
+
+int fmha_forward_ws_size(int batch, int n_h, int n_kv_h, int T, int s_k, int hd, fmha_strides k_st,
+                         fmha_strides v_st, int window, int causal, size_t *bytes) {
+    if (!bytes) return FMHA_ERR_INVALID_ARG;
+    const int rc = validate_dims(batch, n_h, n_kv_h, T, s_k, hd, window, causal, k_st, v_st);
+    if (rc != FMHA_OK) return rc;
+    const fmha_strides none{0, 0, 0};
+    const FwdParams p = make_params(nullptr, nullptr, nullptr, batch, n_h, n_kv_h, T, s_k, none, k_st, v_st, 1.f,
+                                    window, causal);
+    const SplitChoice c = choose_split(p, hd);
+    *bytes = c.split_len ? (size_t)split_workspace_bytes((int64_t)batch * n_h * T, c.n_split, hd) : 0;
+    return FMHA_OK;
+}
+
+int fmha_forward_ws(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int n_h,
+                    int n_kv_h, int T, int s_k, int hd, fmha_strides q_st, fmha_strides k_st, fmha_strides v_st,
+                    fmha_strides o_st, float scale, int window, int causal, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    int rc = validate_attention(q, k, v, o, lse, false, batch, n_h, n_kv_h, T, s_k, hd, q_st, k_st, v_st, &o_st,
+                                window, causal);
+    if (rc != FMHA_OK) return rc;
+    FwdParams p = make_params(q, k, v, batch, n_h, n_kv_h, T, s_k, q_st, k_st, v_st, scale, window, causal);
+    p.o = static_cast<uint16_t *>(o);
+    p.lse = lse;
+    p.o_sb = o_st.batch; p.o_st = o_st.token; p.o_sh = o_st.head;
+    const SplitChoice c = choose_split(p, hd);
+    if (c.split_len) {
+        const int64_t need = split_workspace_bytes((int64_t)batch * n_h * T, c.n_split, hd);
+        if (!workspace || (int64_t)workspace_bytes < need) return FMHA_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return FMHA_ERR_ALIGNMENT;
+    }
+    return forward_split_or_fused(p, hd, c, workspace, o_st, stream);
 }
 
 int fmha_forward_varlen(const void *q, const void *k, const void *v, const int *seqlens_k, void *o, float *lse,
@@ -465,6 +602,8 @@ const char *fmha_status_string(int status) {
                                           "s_k at most 2^30 and (n_h / n_kv_h) * T at most 2^30";
         case FMHA_ERR_ALIGNMENT: return "FMHA_ERR_ALIGNMENT: pointers must be 16-byte aligned and strides multiples of 8 elements";
         case FMHA_ERR_LAUNCH: return "FMHA_ERR_LAUNCH: the HIP kernel launch failed";
+        case FMHA_ERR_WORKSPACE: return "FMHA_ERR_WORKSPACE: the call needs a workspace of more bytes than were "
+                                        "given (fmha_forward_ws_size tells how many)";
         default: return "unknown fmha status";
     }
 }

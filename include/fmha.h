@@ -69,6 +69,7 @@
 #ifndef FMHA_H
 #define FMHA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -88,7 +89,8 @@ typedef enum {
                                  arguments, T > s_k with a mask, split_len <= 0 */
     FMHA_ERR_UNSUPPORTED = 2, /* hd not in {64,128,256,512}, or a size over its limit */
     FMHA_ERR_ALIGNMENT = 3,   /* pointer not 16-byte aligned or stride not a multiple of 8 */
-    FMHA_ERR_LAUNCH = 4       /* the HIP launch failed */
+    FMHA_ERR_LAUNCH = 4,      /* the HIP launch failed */
+    FMHA_ERR_WORKSPACE = 5    /* workspace missing or smaller than the call needs */
 } fmha_status;
 
 /*
@@ -112,6 +114,41 @@ int fmha_forward(const void *q, const void *k, const void *v, void *o, float *ls
                  int batch, int n_h, int n_kv_h, int T, int s_k, int hd,
                  fmha_strides q_st, fmha_strides k_st, fmha_strides v_st, fmha_strides o_st,
                  float scale, int window, int causal, void *stream);
+
+/*
+ * fmha_forward_ws -- fmha_forward with a caller-provided workspace, for grids
+ * of few units.  A call with fewer 16-row tiles (rows = query positions x
+ * query heads per KV head) than the GPU has compute units, whose tiles each
+ * see many keys, is split over the keys into partitions of at most 128 keys
+ * -- the multi-CTA split ("D2 multi-CTA" in the 593bc25a log) -- written as
+ * fp32 partial outputs into the workspace, and combined by the D5 merge
+ * ("Next steps", item 4 of CURRENT_ISSUE.md) in a second launch on the same
+ * stream.  Other calls run exactly as fmha_forward and leave the workspace
+ * untouched.  The result is the attention defined above either way.
+ *
+ *   workspace        device memory, 16-byte aligned, owned by the caller; its
+ *                    contents on entry do not matter, and on return it holds
+ *                    the partials (valid once the stream reaches that point)
+ *   workspace_bytes  its size; fmha_forward_ws_size gives the bytes a call of
+ *                    given sizes needs (0 when it runs fused, where workspace
+ *                    may be NULL)
+ * The other arguments are as for fmha_forward.  Errors: as fmha_forward;
+ * FMHA_ERR_WORKSPACE when the call splits and the workspace is NULL or
+ * smaller than needed; FMHA_ERR_ALIGNMENT for a misaligned workspace.  Two
+ * calls in flight at once must not share a workspace.
+ */
+int fmha_forward_ws(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int batch, int n_h, int n_kv_h, int T, int s_k, int hd,
+                    fmha_strides q_st, fmha_strides k_st, fmha_strides v_st, fmha_strides o_st,
+                    float scale, int window, int causal,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace fmha_forward_ws needs for a call of these sizes (0 when
+ * it runs fused): host-only, launches nothing.  k_st / v_st matter through
+ * their head strides (both 0 = MQA).  Errors: as fmha_forward for sizes and
+ * mask arguments; FMHA_ERR_INVALID_ARG for a null `bytes`. */
+int fmha_forward_ws_size(int batch, int n_h, int n_kv_h, int T, int s_k, int hd,
+                         fmha_strides k_st, fmha_strides v_st, int window, int causal, size_t *bytes);
 
 /*
  * fmha_decode_splitkv -- attention per KV partition (split-KV, "D2

@@ -12,7 +12,7 @@ from head_attention_fmha_amd import FmhaStrides
 import variant_shapes as VS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, INVALID, UNSUPPORTED, ALIGN, LAUNCH = 0, 1, 2, 3, 4
+OK, INVALID, UNSUPPORTED, ALIGN, LAUNCH, WORKSPACE = 0, 1, 2, 3, 4, 5
 
 
 @pytest.fixture(scope="module")
@@ -31,8 +31,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fmha_attention_plan", "fmha_decode_splitkv", "fmha_decode_splitkv_segment",
-                                    "fmha_forward", "fmha_forward_mx", "fmha_forward_varlen", "fmha_lse_merge",
-                                    "fmha_lse_merge_mx", "fmha_status_string"]
+                                    "fmha_forward", "fmha_forward_mx", "fmha_forward_varlen", "fmha_forward_ws",
+                                    "fmha_forward_ws_size", "fmha_lse_merge", "fmha_lse_merge_mx",
+                                    "fmha_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (OK, INVALID, UNSUPPORTED, ALIGN, LAUNCH):
+    for code in (OK, INVALID, UNSUPPORTED, ALIGN, LAUNCH, WORKSPACE):
         s = fa.fmha_status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in fa.fmha_status_string(99)
@@ -172,13 +173,29 @@ def test_merge_rejects(lib, kw, code):
     # single-head decode
     ((1, 1, 1, 1, 128, 64), {}, (4, 1, 1, 1, 1)),
     # sliding window MQA prefill: a 16-row tile is one position (16 heads) and
-    # sees 128 keys, more than one pass of the eight waves' two key groups
-    ((2, 16, 1, 128, 4096, 512), dict(causal=True, window=128), (8, 1, 0, 0, 256)),
+    # sees its 128-key window: one pass of the one-pass kernel
+    ((2, 16, 1, 128, 4096, 512), dict(causal=True, window=128), (8, 1, 1, 0, 256)),
+    # MQA decode over 128 keys at hd 512 and 256, and its 128-key split partitions
+    ((8, 128, 1, 1, 128, 512), {}, (8, 1, 1, 0, 64)),
+    ((8, 128, 1, 1, 512, 256), dict(split_len=128), (8, 1, 1, 0, 256)),
 ])
 def test_plan_of_each_workload(lib, args, kw, want):
     got = fa.fmha_attention_plan(*args, **kw)
     assert (got["waves_per_group"], got["tiles_per_group"], got["one_slice"], got["streaming"],
             got["workgroups"]) == want
+
+
+@pytest.mark.parametrize("args,kw,kernel", [
+    ((32, 64, 8, 1, 8192, 128), dict(split_len=128), "stream_kernel<128, true>"),
+    ((8, 128, 1, 1, 512, 512), {}, "attn_kernel<512, 8, 2, 4, 1, false, false, false>"),
+    ((8, 128, 1, 1, 512, 512), dict(split_len=128), "pass_kernel<512, true>"),
+    ((2, 16, 1, 128, 4096, 512), dict(causal=True, window=128), "pass_kernel<512, false>"),
+    ((4, 32, 32, 128, 512, 512), dict(causal=True), "rows_kernel<512, 1, 32, false>"),
+    ((2, 32, 8, 4096, 4096, 128), dict(causal=True), "rows_kernel<128, 2, 32, false>"),
+    ((1, 1, 1, 1, 128, 64), {}, "attn_kernel<64, 4, 4, 1, 1, false, true, true>"),
+])
+def test_plan_names_the_kernel_of_each_workload(lib, args, kw, kernel):
+    assert fa.fmha_attention_plan(*args, **kw)["kernel"] == kernel
 
 
 @pytest.mark.parametrize("hd,token_stride,row_parallel", [
@@ -316,3 +333,51 @@ def test_stream_kernel_serves_the_split_decode_while_its_offsets_fit(lib):
     assert big["kernel"] == "attn_kernel<128, 4, 4, 1, 1, true, true, true>"
     # fused calls (no partials) with one slice and one row block
     assert fa.fmha_attention_plan(4, 32, 32, 1, 128, 128)["kernel"] == "stream_kernel<128, false>"
+
+
+
+# ---------------------------------------------------------------------------
+# fmha_forward_ws: few-unit calls split over the keys into a workspace
+# ---------------------------------------------------------------------------
+
+def ws_call(lib, ws, nbytes, b=8, n_h=128, hd=512, s_k=512):
+    q_st = FmhaStrides(n_h * hd, n_h * hd, hd)
+    kv_st = FmhaStrides(s_k * hd, hd, hd)
+    return lib.fmha_forward_ws(QP, KP, VP, OP, LP, b, n_h, 1, 1, s_k, hd, q_st, kv_st, kv_st, q_st, 0.1, 0, 0, ws,
+                               nbytes, None)
+
+
+def test_ws_size_of_the_mqa_decode_grid(lib):
+    """Split where a tile's fused work (keys x hd) is large: 4 partitions, so
+    the 64 tiles of the MQA decode become 256 workgroups; fused below."""
+    for hd in (64, 128, 256, 512):
+        for s_k in (128, 256, 384, 512):
+            nbytes = fa.fmha_forward_ws_size(8, 128, 1, 1, s_k, hd)
+            split = s_k * hd >= 96 * 1024
+            rows = 8 * 128
+            want = 0
+            if split:
+                o_bytes = (rows * 4 * hd * 4 + 255) // 256 * 256
+                want = o_bytes + rows * 4 * 4
+            assert nbytes == want, (hd, s_k, nbytes)
+    # many tiles already (the GQA decode workload, one causal prefill): fused
+    assert fa.fmha_forward_ws_size(32, 64, 8, 1, 8192, 128) == 0
+    assert fa.fmha_forward_ws_size(4, 32, 32, 128, 512, 512, causal=True) == 0
+
+
+@pytest.mark.parametrize("ws,nbytes,code", [
+    (None, 0, WORKSPACE),
+    (ctypes.c_void_p(0x80000), 1 << 20, WORKSPACE),           # smaller than the 8 MiB the call needs
+    (ctypes.c_void_p(0x80008), 64 << 20, ALIGN),
+])
+def test_ws_rejects_a_missing_or_short_workspace(lib, ws, nbytes, code):
+    assert ws_call(lib, ws, nbytes) == code
+
+
+def test_ws_validates_like_forward(lib):
+    assert ws_call(lib, ctypes.c_void_p(0x80000), 64 << 20, hd=96) == UNSUPPORTED
+    assert ws_call(lib, ctypes.c_void_p(0x80000), 64 << 20, b=0) == INVALID
+    out = ctypes.c_size_t(7)
+    st = FmhaStrides(0, 64, 64)
+    assert lib.fmha_forward_ws_size(1, 1, 1, 1, 128, 64, st, st, 0, 0, None) == INVALID
+    assert lib.fmha_forward_ws_size(1, 1, 1, 1, 128, 96, st, st, 0, 0, ctypes.byref(out)) == UNSUPPORTED

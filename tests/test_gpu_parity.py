@@ -1029,3 +1029,68 @@ def test_split_decode_with_partition_slots_past_the_stream_kernel_offsets():
     check_attention(o, lse, o_ref, lse_ref, what="2^18 one-key partitions")
     _, lp_ref = oracle.split(q, k, v, scale, 1)
     assert (lse_part.cpu().double() - lp_ref).abs().max().item() <= 1e-3
+
+
+# ---------------------------------------------------------------------------
+# fmha_forward_ws: few-unit calls split over the keys into a workspace
+# ---------------------------------------------------------------------------
+
+def gpu_forward_ws(q, k, v, scale, causal=False, window=0):
+    qd, kd, vd = (x if x.is_cuda else x.to(DEV) for x in (q, k, v))
+    b, T, n_h, hd = qd.shape
+    o = nan_bf16(b, T, n_h, hd)
+    lse = nan_f32(b, n_h, T)
+    ws = fa.workspace_for(qd, kd, window=window, causal=causal)
+    if ws is not None:
+        ws.fill_(0xFF)  # NaN bit patterns: every partial the merge reads must be written
+    fa.fmha_forward_ws(qd, kd, vd, o, lse, ws, scale=scale, window=window, causal=causal)
+    torch.cuda.synchronize()
+    return o, lse, ws
+
+
+@pytest.mark.parametrize("w", I.MQA_DECODE_GRID, ids=lambda w: w.name)
+def test_forward_ws_mqa_decode_grid(w):
+    """Every point of the MQA decode grid through the workspace entry (split
+    + merge where the tiles' work is large, fused elsewhere) against the
+    oracle; where it runs fused the output is bitwise fmha_forward's."""
+    q, k, v = I.make_qkv(w)
+    o, lse, ws = gpu_forward_ws(q, k, v, w.scale)
+    o_ref, lse_ref = oracle.attention(q, k, v, w.scale)
+    check_attention(o, lse, o_ref, lse_ref, what=f"{w.name} (fmha_forward_ws)")
+    split = w.s_k * w.hd >= 96 * 1024
+    assert (ws is not None) == split
+    if not split:
+        o_f, lse_f = gpu_forward(q, k, v, w.scale)
+        assert torch.equal(o, o_f) and torch.equal(lse, lse_f)
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+@pytest.mark.parametrize("dims,causal,window", [
+    ((1, 8, 1, 3, 2000), True, 0),      # few tiles, long keys, causal: partitions past a row are empty
+    ((2, 16, 2, 5, 2001), True, 1600),  # sliding window: partitions outside the window are empty
+    ((1, 4, 4, 1, 3000), False, 0),     # MHA decode, ragged last partition
+    ((1, 32, 1, 2, 1601), False, 0),    # MQA, two positions per tile
+])
+def test_forward_ws_split_shapes(hd, dims, causal, window):
+    b, n_h, n_kv_h, T, s_k = dims
+    seed = 700 + hd + s_k
+    q = I.randn_bf16((b, T, n_h, hd), seed)
+    k = I.randn_bf16((b, s_k, n_kv_h, hd), seed + 1)
+    v = I.randn_bf16((b, s_k, n_kv_h, hd), seed + 2)
+    scale = 1.0 / math.sqrt(hd)
+    o, lse, ws = gpu_forward_ws(q, k, v, scale, causal=causal, window=window)
+    assert ws is not None, "these shapes split"
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=causal, window=window)
+    check_attention(o, lse, o_ref, lse_ref, what=f"fmha_forward_ws {dims} hd {hd}")
+
+
+def test_forward_ws_head_stride_zero_is_bitwise_one_kv_head():
+    w = I.mqa_decode(512, 512)
+    q, k, v = I.make_qkv(w)
+    o1, l1, ws1 = gpu_forward_ws(q, k, v, w.scale)
+    kd, vd = k.to(DEV), v.to(DEV)
+    k0 = kd.expand(w.batch, w.s_k, w.n_h, w.hd)
+    v0 = vd.expand(w.batch, w.s_k, w.n_h, w.hd)
+    o2, l2, ws2 = gpu_forward_ws(q, k0, v0, w.scale)
+    assert ws1 is not None and ws2 is not None and ws1.numel() == ws2.numel()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

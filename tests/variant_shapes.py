@@ -23,31 +23,34 @@ HEAD_DIMS = (64, 128, 256, 512)
 
 
 def branch(plan: dict) -> str:
-    """The kernel variant a plan launches."""
-    if plan["row_parallel"]:
-        return "row-parallel-two-tiles" if plan["tiles_per_group"] == 8 else "row-parallel"
-    if plan["waves_per_group"] == 8:
-        return "eight-waves"
-    if plan["one_slice"]:
-        return "one-slice-streamed" if plan["streaming"] else "one-slice-shared"
-    return "multi-two-tiles" if plan["tiles_per_group"] == 2 else "multi-one-tile"
+    """The kernel variant a plan launches: the kernel template instance with
+    its output mode (fused or split) left out."""
+    family, args = plan["kernel"].split("<", 1)
+    args = args.rstrip(">").split(", ")
+    del args[_SPLIT_ARG[family]]
+    return f"{family}<{', '.join(args)}>"
 
 
-# every variant instantiated for a head dimension
+# every variant the dispatcher launches at a head dimension (the hd-128
+# split decode falls back to the per-wave one-slice streamed kernel only past
+# 2^18 partition slots; test_split_decode_with_partition_slots_past_the_
+# stream_kernel_offsets covers that case)
 EXPECTED = {
-    64: {"row-parallel", "row-parallel-two-tiles", "one-slice-streamed", "one-slice-shared", "multi-one-tile",
-         "multi-two-tiles"},
-    128: {"row-parallel", "row-parallel-two-tiles", "one-slice-streamed", "one-slice-shared", "multi-one-tile",
-          "multi-two-tiles"},
-    256: {"row-parallel", "eight-waves", "one-slice-streamed", "one-slice-shared", "multi-one-tile",
-          "multi-two-tiles"},
-    512: {"row-parallel", "eight-waves", "one-slice-streamed", "one-slice-shared", "multi-one-tile",
-          "multi-two-tiles"},
+    64: {"attn_kernel<64, 4, 4, 1, 1, false, false>", "attn_kernel<64, 4, 4, 1, 2, false, false>",
+         "attn_kernel<64, 4, 4, 1, 1, true, false>", "attn_kernel<64, 4, 4, 1, 1, true, true>",
+         "rows_kernel<64, 1, 64>", "rows_kernel<64, 2, 32>"},
+    128: {"attn_kernel<128, 4, 4, 1, 1, false, false>", "attn_kernel<128, 4, 4, 1, 2, false, false>",
+          "attn_kernel<128, 4, 4, 1, 1, true, false>", "stream_kernel<128>",
+          "rows_kernel<128, 1, 64>", "rows_kernel<128, 2, 32>"},
+    256: {"attn_kernel<256, 4, 2, 2, 1, false, false>", "attn_kernel<256, 4, 2, 2, 2, false, false>",
+          "attn_kernel<256, 8, 4, 2, 1, false, false>", "pass_kernel<256>", "rows_kernel<256, 1, 32>"},
+    512: {"attn_kernel<512, 4, 1, 4, 1, false, false>", "attn_kernel<512, 4, 1, 4, 2, false, false>",
+          "attn_kernel<512, 8, 2, 4, 1, false, false>", "pass_kernel<512>", "rows_kernel<512, 1, 32>"},
 }
 
 
 # position of the SPLIT template argument in each kernel family's name
-_SPLIT_ARG = {"attn_kernel": 5, "rows_kernel": 3, "stream_kernel": 1}
+_SPLIT_ARG = {"attn_kernel": 5, "rows_kernel": 3, "stream_kernel": 1, "pass_kernel": 1}
 
 
 def split_twin(kernel: str) -> str:
