@@ -11,6 +11,7 @@ Entry points carry the C names:
   fmha_forward(q, k, v, o, lse=None, *, scale=None, window=0, causal=False)
   fmha_forward_ws(q, k, v, o, lse=None, workspace=None, *, ...)   (workspace from workspace_for(q, k, ...))
   fmha_forward_ws_size(batch, n_h, n_kv_h, T, s_k, hd, *, window=0, causal=False, mqa_stride0=False)
+  fmha_forward_noalloc(q, k, v, o, lse=None, *, ...)   (static device scratch; allocates nothing)
   fmha_decode_splitkv(q, k, v, o_part, lse_part, *, split_len, scale=None, window=0, causal=False)
   fmha_lse_merge(o_part, lse_part, o, lse=None)
   fmha_forward_varlen(q, k, v, seqlens_k, o, lse=None, *, scale=None, window=0, causal=False)
@@ -33,6 +34,7 @@ from typing import Optional
 import torch
 
 __all__ = ["FmhaError", "fmha_forward", "fmha_forward_ws", "fmha_forward_ws_size", "workspace_for",
+           "fmha_forward_noalloc",
            "fmha_forward_varlen", "fmha_decode_splitkv", "fmha_decode_splitkv_segment",
            "fmha_lse_merge", "fmha_forward_mx", "fmha_lse_merge_mx", "MX_FP8_E4M3", "MX_FP4_E2M1", "mx_shapes",
            "fmha_status_string",
@@ -77,6 +79,8 @@ def load_library():
     lib.fmha_forward.restype = I
     lib.fmha_forward_ws.argtypes = [P, P, P, P, P, I, I, I, I, I, I, S, S, S, S, F, I, I, P, ctypes.c_size_t, P]
     lib.fmha_forward_ws.restype = I
+    lib.fmha_forward_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, I, S, S, S, S, F, I, I, P]
+    lib.fmha_forward_noalloc.restype = I
     lib.fmha_forward_ws_size.argtypes = [I, I, I, I, I, I, S, S, I, I, ctypes.POINTER(ctypes.c_size_t)]
     lib.fmha_forward_ws_size.restype = I
     lib.fmha_decode_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, S, S, S, F, I, I, I, P]
@@ -207,6 +211,21 @@ def fmha_forward_ws(q, k, v, o, lse=None, workspace=None, *, scale=None, window=
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, n_h, n_kv_h, T, s_k, hd,
         _st(q), _st(k), _st(v), _st(o), _scale(scale, hd), int(window), int(bool(causal)), ws_ptr, ws_bytes,
         _stream(stream)))
+
+
+def fmha_forward_noalloc(q, k, v, o, lse=None, *, scale=None, window=0, causal=False, stream=None) -> None:
+    """fmha_forward_ws with the library's static device scratch in place of
+    a workspace (allocates nothing); see include/fmha.h."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _dev4(t, n)
+    b, T, n_h, hd = q.shape
+    _, s_k, n_kv_h, _ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape) or k.shape[0] != b or k.shape[3] != hd:
+        raise ValueError("shape mismatch between q, k, v, o")
+    _dense(lse, (b, n_h, T), "lse")
+    _check(load_library().fmha_forward_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, n_h, n_kv_h, T, s_k, hd,
+        _st(q), _st(k), _st(v), _st(o), _scale(scale, hd), int(window), int(bool(causal)), _stream(stream)))
 
 
 def fmha_decode_splitkv(q, k, v, o_part, lse_part, *, split_len, scale=None, window=0, causal=False,

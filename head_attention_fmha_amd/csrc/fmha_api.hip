@@ -9,6 +9,7 @@
 
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "fmha.h"
 #include "attn_kernel.hpp"
@@ -417,6 +418,36 @@ int forward_split_or_fused(FwdParams p, int hd, const SplitChoice &c, void *ws, 
     return launch_merge(m, p.batch, p.n_h, p.T, hd, c.n_split, stream);
 }
 
+// ---- the static scratch of fmha_forward_noalloc -------------------------------
+//
+// For callers that cannot allocate (code under graph capture, serving loops
+// that forbid it): the split path's partials go to this array instead of a
+// workspace.  Every GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device address: kernels and copies get the address hipGetSymbolAddress
+// returns, fetched once per device and kept in scratch_ptr_of.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr_of[kMaxDevices] = {};
+
+// The scratch address on the current device (looked up on its first use).
+int scratch_address(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FMHA_ERR_LAUNCH;
+    if (dev < 0 || dev >= kMaxDevices) return FMHA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr_of[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return FMHA_ERR_LAUNCH;
+        scratch_ptr_of[dev] = ptr;
+    }
+    *out = scratch_ptr_of[dev];
+    return FMHA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -468,6 +499,29 @@ int fmha_forward_ws(const void *q, const void *k, const void *v, void *o, float 
         if (!aligned16(workspace)) return FMHA_ERR_ALIGNMENT;
     }
     return forward_split_or_fused(p, hd, c, workspace, o_st, stream);
+}
+
+int fmha_forward_noalloc(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int n_h,
+                         int n_kv_h, int T, int s_k, int hd, fmha_strides q_st, fmha_strides k_st, fmha_strides v_st,
+                         fmha_strides o_st, float scale, int window, int causal, void *stream) {
+    int rc = validate_attention(q, k, v, o, lse, false, batch, n_h, n_kv_h, T, s_k, hd, q_st, k_st, v_st, &o_st,
+                                window, causal);
+    if (rc != FMHA_OK) return rc;
+    FwdParams p = make_params(q, k, v, batch, n_h, n_kv_h, T, s_k, q_st, k_st, v_st, scale, window, causal);
+    p.o = static_cast<uint16_t *>(o);
+    p.lse = lse;
+    p.o_sb = o_st.batch; p.o_st = o_st.token; p.o_sh = o_st.head;
+    const SplitChoice c = choose_split(p, hd);
+    void *ws = nullptr;
+    if (c.split_len) {
+        // every partial slot the merge reads is written by the split launch
+        // first, so nothing in the scratch needs clearing between calls
+        if (split_workspace_bytes((int64_t)batch * n_h * T, c.n_split, hd) > (int64_t)kScratchBytes)
+            return FMHA_ERR_WORKSPACE;
+        rc = scratch_address(&ws);
+        if (rc != FMHA_OK) return rc;
+    }
+    return forward_split_or_fused(p, hd, c, ws, o_st, stream);
 }
 
 int fmha_forward_varlen(const void *q, const void *k, const void *v, const int *seqlens_k, void *o, float *lse,
@@ -603,7 +657,8 @@ const char *fmha_status_string(int status) {
         case FMHA_ERR_ALIGNMENT: return "FMHA_ERR_ALIGNMENT: pointers must be 16-byte aligned and strides multiples of 8 elements";
         case FMHA_ERR_LAUNCH: return "FMHA_ERR_LAUNCH: the HIP kernel launch failed";
         case FMHA_ERR_WORKSPACE: return "FMHA_ERR_WORKSPACE: the call needs a workspace of more bytes than were "
-                                        "given (fmha_forward_ws_size tells how many)";
+                                        "given (fmha_forward_ws_size tells how many; fmha_forward_noalloc has "
+                                        "32 MiB of static scratch)";
         default: return "unknown fmha status";
     }
 }

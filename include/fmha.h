@@ -143,6 +143,25 @@ int fmha_forward_ws(const void *q, const void *k, const void *v, void *o, float 
                     float scale, int window, int causal,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * fmha_forward_noalloc -- fmha_forward_ws for callers that cannot allocate
+ * (code under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc): the same computation and kernels, with the split path's
+ * partials in 32 MiB of static device scratch that the library holds on each
+ * GPU it runs on until the process ends, instead of a caller workspace.  The
+ * call allocates nothing.  A call whose split needs more than 32 MiB (as
+ * fmha_forward_ws_size reports) is rejected before any HIP call.  The scratch
+ * of a GPU is shared by every call on it: calls that overlap on one GPU
+ * (different streams, or threads) race and must not be issued; the first
+ * call on a GPU looks the scratch address up once (hipGetSymbolAddress).
+ * Errors: as fmha_forward_ws; FMHA_ERR_WORKSPACE when the split needs more
+ * than the 32 MiB; FMHA_ERR_LAUNCH if the scratch address cannot be found.
+ */
+int fmha_forward_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                         int batch, int n_h, int n_kv_h, int T, int s_k, int hd,
+                         fmha_strides q_st, fmha_strides k_st, fmha_strides v_st, fmha_strides o_st,
+                         float scale, int window, int causal, void *stream);
+
 /* Bytes of workspace fmha_forward_ws needs for a call of these sizes (0 when
  * it runs fused): host-only, launches nothing.  k_st / v_st matter through
  * their head strides (both 0 = MQA).  Errors: as fmha_forward for sizes and

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fmha_attention_plan", "fmha_decode_splitkv", "fmha_decode_splitkv_segment",
-                                    "fmha_forward", "fmha_forward_mx", "fmha_forward_varlen", "fmha_forward_ws",
+                                    "fmha_forward", "fmha_forward_mx", "fmha_forward_noalloc", "fmha_forward_varlen", "fmha_forward_ws",
                                     "fmha_forward_ws_size", "fmha_lse_merge", "fmha_lse_merge_mx",
                                     "fmha_status_string"]
 
@@ -381,3 +381,17 @@ def test_ws_validates_like_forward(lib):
     st = FmhaStrides(0, 64, 64)
     assert lib.fmha_forward_ws_size(1, 1, 1, 1, 128, 64, st, st, 0, 0, None) == INVALID
     assert lib.fmha_forward_ws_size(1, 1, 1, 1, 128, 96, st, st, 0, 0, ctypes.byref(out)) == UNSUPPORTED
+
+
+
+def test_noalloc_rejects_a_split_beyond_its_scratch_before_any_hip_call(lib):
+    """The static scratch holds 32 MiB: a call whose split needs more is
+    rejected on the host (this container has no GPU, so any HIP call would
+    fail differently)."""
+    b, n_h, hd, s_k = 1, 128, 512, 32768  # 128 rows x 256 partitions of 128 keys x 2 KiB = 64 MiB of partials
+    assert fa.fmha_forward_ws_size(b, n_h, 1, 1, s_k, hd) > 32 << 20
+    q_st = FmhaStrides(n_h * hd, n_h * hd, hd)
+    kv_st = FmhaStrides(s_k * hd, hd, hd)
+    rc = lib.fmha_forward_noalloc(QP, KP, VP, OP, LP, b, n_h, 1, 1, s_k, hd, q_st, kv_st, kv_st, q_st, 0.1, 0, 0,
+                                  None)
+    assert rc == WORKSPACE
