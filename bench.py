@@ -410,6 +410,21 @@ def run_grid(torch, fa, I, path):
                 return step
             split_us = rotated_time_us(torch, [mk_split(bf) for bf in bufs])
             del o_part, lse_part
+        # the one-call workspace entry: few-unit points split over the keys
+        # into partitions of at most 128 keys and merged (two launches)
+        ws_us = None
+        ws_bytes = fa.fmha_forward_ws_size(w.batch, w.n_h, w.n_kv_h, w.T, w.s_k, w.hd, window=w.window,
+                                           causal=w.causal)
+        if ws_bytes:
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+            def mk_ws(bf):
+                return lambda: fa.fmha_forward_ws(bf[0], bf[1], bf[2], bf[3], bf[4], ws, scale=w.scale,
+                                                  window=w.window, causal=w.causal,
+                                                  stream=torch.cuda.current_stream())
+            ws_us = rotated_time_us(torch, [mk_ws(bf) for bf in bufs]) if cold else \
+                rotated_time_us(torch, [mk_ws(bufs[0])])
+            del ws
         plan = fa.fmha_attention_plan(w.batch, w.n_h, w.n_kv_h, w.T, w.s_k, w.hd, window=w.window, causal=w.causal)
         pt = {"workload": w.name, "T": w.T, "s_k": w.s_k, "hd": w.hd, "us": round(us, 2), "hot_us": round(hot_us, 2),
               "cold": cold, "kv_gbs": round(kv / (us * 1e-6) / 1e9, 1),
@@ -422,11 +437,16 @@ def run_grid(torch, fa, I, path):
         if split_us is not None:
             pt.update({"split_merge_us": round(split_us, 2), "split_len": SPLIT_DECODE_LEN,
                        "split_merge_frac_of_roofline": round(t_roof_us / split_us, 4)})
+        pt["kernel"] = plan["kernel"]
+        if ws_us is not None:
+            pt.update({"ws_us": round(ws_us, 2), "ws_frac_of_roofline": round(t_roof_us / ws_us, 4),
+                       "ws_bytes": ws_bytes})
         points.append(pt)
         log(f"grid {w.name}: {us:.2f} us (hot {hot_us:.2f}), {pt['kv_gbs']:.0f} GB/s K+V, "
             f"{pt['total_gbs']:.0f} GB/s total, {tfs:.1f} TFLOP/s, {t_roof_us / us:.1%} of roofline"
             f"{' (launch-bound)' if pt['launch_bound'] else ''}"
-            f"{f'; split-KV + merge {split_us:.2f} us' if split_us is not None else ''}")
+            f"{f'; split-KV + merge {split_us:.2f} us' if split_us is not None else ''}"
+            f"{f'; fmha_forward_ws {ws_us:.2f} us' if ws_us is not None else ''}")
         del bufs, q, k, v
         torch.cuda.empty_cache()
     with open(path, "w") as f:

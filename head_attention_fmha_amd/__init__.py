@@ -41,7 +41,9 @@ __all__ = ["FmhaError", "fmha_forward", "fmha_forward_ws", "fmha_forward_ws_size
            "fmha_attention_plan", "n_split_for", "library_path", "load_library", "FmhaStrides", "FmhaPlan"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "libfmha.so")
+# FMHA_LIBRARY names another build of the same sources to load instead (the
+# sanitizer test loads a host-only build under AddressSanitizer/UBSan)
+_LIB_PATH = os.environ.get("FMHA_LIBRARY") or os.path.join(_PKG, "libfmha.so")
 _lib = None
 
 
