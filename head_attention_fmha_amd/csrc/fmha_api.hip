@@ -276,7 +276,8 @@ void launch_hd(const FwdParams &p, int var, hipStream_t s) {
             break;
         case kPass:
             if constexpr (HD >= 256)
-                hipLaunchKernelGGL((fmha::pass_kernel<HD, SPLIT>), dim3(p.n_units), dim3(512), 0, s, p);
+                hipLaunchKernelGGL((fmha::pass_kernel<HD, SPLIT>), dim3(p.n_units), dim3(64 * fmha::PassShape<HD>::NW),
+                                   0, s, p);
             break;
         // one-slice work at hd >= 256 runs the one-pass kernel
         case kAttnOneStream:
