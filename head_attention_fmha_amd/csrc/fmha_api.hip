@@ -136,12 +136,13 @@ bool rows_loads_fit(const FwdParams &p, int hd) {
     return (int64_t)(1024 / (2 * hd) - 1) * st * 2 + 2 * hd < (int64_t(1) << 31);
 }
 
-// The stream kernel stores a workgroup's split partials by buffer stores with
-// 32-bit byte offsets from its first row: its (at most 16) rows lie within
-// 16 * n_split_total rows of hd fp32 values.
+// The stream kernel stores split partials by buffer stores with 32-bit byte
+// offsets from the first partial row of the KV head: its rows (at least the
+// 16 of one tile) lie within rows * n_split_total rows of hd fp32 values.
 bool stream_offsets_fit(const FwdParams &p, int hd) {
     const int64_t slots = p.n_split_total > 0 ? p.n_split_total : p.n_split;
-    return (int64_t)16 * slots * hd * 4 < (int64_t(1) << 31);
+    const int64_t rows = p.rows > 16 ? p.rows : 16;
+    return rows * slots * hd * 4 < (int64_t(1) << 31);
 }
 
 // Kernel variants the dispatcher launches (one template family each).
@@ -149,7 +150,8 @@ enum Variant : int {
     kRowsTwoTiles,  // rows_kernel<HD, 2, 32>: 128 rows per workgroup (hd <= 128)
     kRowsOneTile,   // rows_kernel<HD, 1, rows_chunk_keys(HD)>: 64 rows per workgroup
     kAttnEight,     // attn_kernel, eight waves, several slices (hd >= 256)
-    kStream,        // stream_kernel<128>: one pass, non-temporal whole-line K/V loads
+    kStream,        // stream_kernel<128, STREAM = true>: one pass, non-temporal whole-line K/V loads
+    kStreamShared,  // stream_kernel<128, STREAM = false>: one pass, row blocks sharing K/V through L2
     kPass,          // pass_kernel<HD>: one pass over <= 128 keys, every load up front (hd >= 256)
     kAttnOneStream, // attn_kernel, one slice, streamed
     kAttnOne,       // attn_kernel, one slice, K/V shared with other row blocks
@@ -230,9 +232,9 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
     } else if (pass) {
         var = kPass;
         snprintf(pl.kernel, sizeof pl.kernel, "pass_kernel<%d, %s>", hd, sp);
-    } else if (pl.one_slice && pl.streaming && hd == 128 && stream_offsets_fit(p, hd)) {
-        var = kStream;
-        snprintf(pl.kernel, sizeof pl.kernel, "stream_kernel<%d, %s>", hd, sp);
+    } else if (pl.one_slice && hd == 128 && (!split || stream_offsets_fit(p, hd))) {
+        var = pl.streaming ? kStream : kStreamShared;
+        snprintf(pl.kernel, sizeof pl.kernel, "stream_kernel<%d, %s, %s>", hd, sp, pl.streaming ? "true" : "false");
     } else {
         const int nw = pl.waves_per_group;
         const bool one = pl.one_slice, stream = pl.one_slice && pl.streaming;
@@ -272,7 +274,11 @@ void launch_hd(const FwdParams &p, int var, hipStream_t s) {
             break;
         case kStream:
             if constexpr (HD == 128)
-                hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT>), dim3(p.n_units), dim3(256), 0, s, p);
+                hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, true>), dim3(p.n_units), dim3(256), 0, s, p);
+            break;
+        case kStreamShared:
+            if constexpr (HD == 128)
+                hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, false>), dim3(p.n_units), dim3(256), 0, s, p);
             break;
         case kPass:
             if constexpr (HD >= 256)

@@ -1,7 +1,6 @@
-// stream_kernel.hpp -- one-pass attention for streaming work at hd 128 on
-// gfx950: every workgroup's keys fit one 128-key pass and no other
-// workgroup reads its K/V (the split-KV decode with 128-key partitions;
-// short caches with one row block per KV head).
+// stream_kernel.hpp -- one-pass attention at hd 128 on gfx950: every
+// workgroup's keys fit one 128-key pass (the split-KV decode with 128-key
+// partitions; caches of at most 128 keys).
 //
 // Such work is bound by HBM bandwidth alone, and this GPU streams reads at
 // its best only with the non-temporal hint on loads that fetch whole cache
@@ -44,7 +43,11 @@
 
 namespace fmha {
 
-template <int HD, bool SPLIT>
+// STREAM: one row block per KV head -- nobody else reads this workgroup's
+// K/V, which is then loaded with the non-temporal hint.  Otherwise the row
+// blocks of a KV head share its K/V through L2 (plain loads, units
+// regrouped per XCD).
+template <int HD, bool SPLIT, bool STREAM>
 __global__ __launch_bounds__(256, 4) void stream_kernel(const FwdParams p) {
     static_assert(HD == 128, "the stream kernel serves hd 128: one 16-lane run covers a key row");
     constexpr int KSTEPS = HD / 32;     // QK MFMA steps over the head dim
@@ -62,27 +65,36 @@ __global__ __launch_bounds__(256, 4) void stream_kernel(const FwdParams p) {
     const int lr = lane & 15;
     const int lg = lane >> 4;
 
-    // ---- work unit (one row block per KV head): partitions fastest, then KV
-    // heads, then batch rows -- neighbouring workgroups read neighbouring
-    // cache rows and write neighbouring partials ----------------------------
+    // ---- work unit: row blocks fastest (regrouped per XCD, last block first;
+    // streaming work has one), then partitions, KV heads, batch rows --
+    // neighbouring workgroups read neighbouring cache rows and write
+    // neighbouring partials --------------------------------------------------
     int bid = blockIdx.x;
+    if (!STREAM && p.xcd_remap) {
+        const int per = p.n_units >> 3;
+        bid = (bid & 7) * per + (bid >> 3);
+    }
+    const int rb = STREAM ? 0 : p.n_row_blocks - 1 - bid % p.n_row_blocks;
+    if (!STREAM) bid /= p.n_row_blocks;
     const int part = bid % p.n_split;
     bid /= p.n_split;
     const int kvh = bid % p.n_kv_h;
     const int b = bid / p.n_kv_h;
     const int s_k = p.seqlens ? min(max(p.seqlens[b], 0), p.s_k) : p.s_k;
 
-    const int row_last = min(16, p.rows) - 1;
-    const int pos_lo = s_k - p.T;
+    const int row0 = 16 * rb;
+    const int row_last = min(row0 + 16, p.rows) - 1;
+    const int pos_lo = s_k - p.T + row0 / p.group;
     const int pos_hi = s_k - p.T + row_last / p.group;
     int klo = part * p.split_len;
     int khi = min(klo + p.split_len, s_k);
     if (p.causal) khi = min(khi, pos_hi + 1);
     if (p.window > 0) klo = max(klo, pos_lo - p.window + 1);
 
-    const bool row_ok = lr < p.rows;
-    const int t_row = row_ok ? lr / p.group : 0;
-    const int h_row = kvh * p.group + (row_ok ? lr % p.group : 0);
+    const int row = row0 + lr;
+    const bool row_ok = row < p.rows;
+    const int t_row = row_ok ? row / p.group : 0;
+    const int h_row = kvh * p.group + (row_ok ? row % p.group : 0);
     int r_lo, r_hi;  // visible keys of row lr
     {
         const int pos = s_k - p.T + t_row;
@@ -118,7 +130,7 @@ __global__ __launch_bounds__(256, 4) void stream_kernel(const FwdParams p) {
             const int r = 4 * it + (lane >> 4);
             const int chunk = (lr - rot_of(r)) & (CHUNKS - 1);
             const int key = min(k0 + r, khi - 1);
-            load_lds_16<true>(kbase + key_offset(key, p.k_st) + 8 * chunk, sKw + it * 1024);
+            load_lds_16<STREAM>(kbase + key_offset(key, p.k_st) + 8 * chunk, sKw + it * 1024);
         }
         __builtin_amdgcn_sched_barrier(0);  // Q, then K, then V: the waits below count on that order
         // V: eight wave-wide register loads of four whole key rows each
@@ -126,7 +138,8 @@ __global__ __launch_bounds__(256, 4) void stream_kernel(const FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int key = min(k0 + 8 * lg + i, khi - 1);
-            vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vbase + key_offset(key, p.v_st)));
+            const u32x4 *vp = reinterpret_cast<const u32x4 *>(vbase + key_offset(key, p.v_st));
+            vr[i] = STREAM ? __builtin_nontemporal_load(vp) : *vp;
         }
         __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
     }
@@ -242,16 +255,17 @@ __global__ __launch_bounds__(256, 4) void stream_kernel(const FwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] += wgt * rec[(3 + 4 * (j0 + e) + t0) * 64];
         }
-        if (rr >= p.rows) continue;
-        const int t_o = rr / p.group, h_o = kvh * p.group + rr % p.group;
+        const int rw = row0 + rr;
+        if (rw >= p.rows) continue;
+        const int t_o = rw / p.group, h_o = kvh * p.group + rw % p.group;
         const float inv = LQ > 0.f ? 1.f / LQ : 0.f;
         const float lse_val = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
         o = o * inv;
         if constexpr (SPLIT) {
-            // rows of this workgroup: r0 + ((rr % group) T + rr / group) n_split_total;
+            // rows of this KV head: r0 + ((rw % group) T + rw / group) n_split_total;
             // byte offsets from the first fit 32 bits (the host checks it)
             const int64_t r0 = ((int64_t)b * p.n_h + kvh * p.group) * p.T * p.n_split_total + p.part_offset + part;
-            const int64_t dr = ((int64_t)(rr % p.group) * p.T + rr / p.group) * p.n_split_total;
+            const int64_t dr = ((int64_t)(rw % p.group) * p.T + rw / p.group) * p.n_split_total;
             store16_device_scope(p.o_part + r0 * HD, (unsigned)((dr * HD + c) * 4), o);
             if (wave == 0 && q == 0) p.lse_part[r0 + dr] = lse_val;
         } else {

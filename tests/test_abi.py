@@ -186,7 +186,7 @@ def test_plan_of_each_workload(lib, args, kw, want):
 
 
 @pytest.mark.parametrize("args,kw,kernel", [
-    ((32, 64, 8, 1, 8192, 128), dict(split_len=128), "stream_kernel<128, true>"),
+    ((32, 64, 8, 1, 8192, 128), dict(split_len=128), "stream_kernel<128, true, true>"),
     ((8, 128, 1, 1, 512, 512), {}, "attn_kernel<512, 8, 2, 4, 1, false, false, false>"),
     ((8, 128, 1, 1, 512, 512), dict(split_len=128), "pass_kernel<512, true>"),
     ((2, 16, 1, 128, 4096, 512), dict(causal=True, window=128), "pass_kernel<512, false>"),
@@ -326,13 +326,15 @@ def test_stream_kernel_serves_the_split_decode_while_its_offsets_fit(lib):
     partition slots that a workgroup's 16 rows of fp32 partials span 2 GiB or
     more (its buffer stores take 32-bit offsets) the per-wave kernel runs."""
     got = fa.fmha_attention_plan(32, 64, 8, 1, 8192, 128, split_len=128)
-    assert got["kernel"] == "stream_kernel<128, true>"
+    assert got["kernel"] == "stream_kernel<128, true, true>"
     ok = fa.fmha_attention_plan(1, 1, 1, 1, (1 << 18) - 1, 128, split_len=1)
-    assert ok["kernel"] == "stream_kernel<128, true>"
+    assert ok["kernel"] == "stream_kernel<128, true, true>"
     big = fa.fmha_attention_plan(1, 1, 1, 1, 1 << 18, 128, split_len=1)
     assert big["kernel"] == "attn_kernel<128, 4, 4, 1, 1, true, true, true>"
     # fused calls (no partials) with one slice and one row block
-    assert fa.fmha_attention_plan(4, 32, 32, 1, 128, 128)["kernel"] == "stream_kernel<128, false>"
+    assert fa.fmha_attention_plan(4, 32, 32, 1, 128, 128)["kernel"] == "stream_kernel<128, false, true>"
+    # row blocks sharing K/V (128 query heads over one KV head): the shared form
+    assert fa.fmha_attention_plan(8, 128, 1, 1, 128, 128)["kernel"] == "stream_kernel<128, false, false>"
 
 
 

@@ -31,16 +31,17 @@ def branch(plan: dict) -> str:
     return f"{family}<{', '.join(args)}>"
 
 
-# every variant the dispatcher launches at a head dimension (the hd-128
-# split decode falls back to the per-wave one-slice streamed kernel only past
-# 2^18 partition slots; test_split_decode_with_partition_slots_past_the_
+# every variant the dispatcher launches at a head dimension (at hd 128 the
+# split decode falls back to the per-wave one-slice kernels only when the
+# stream kernel's 32-bit partial offsets do not reach -- 2^18 partition slots
+# for one 16-row tile; test_split_decode_with_partition_slots_past_the_
 # stream_kernel_offsets covers that case)
 EXPECTED = {
     64: {"attn_kernel<64, 4, 4, 1, 1, false, false>", "attn_kernel<64, 4, 4, 1, 2, false, false>",
          "attn_kernel<64, 4, 4, 1, 1, true, false>", "attn_kernel<64, 4, 4, 1, 1, true, true>",
          "rows_kernel<64, 1, 64>", "rows_kernel<64, 2, 32>"},
     128: {"attn_kernel<128, 4, 4, 1, 1, false, false>", "attn_kernel<128, 4, 4, 1, 2, false, false>",
-          "attn_kernel<128, 4, 4, 1, 1, true, false>", "stream_kernel<128>",
+          "stream_kernel<128, true>", "stream_kernel<128, false>",
           "rows_kernel<128, 1, 64>", "rows_kernel<128, 2, 32>"},
     256: {"attn_kernel<256, 4, 2, 2, 1, false, false>", "attn_kernel<256, 4, 2, 2, 2, false, false>",
           "attn_kernel<256, 8, 4, 2, 1, false, false>", "pass_kernel<256>", "rows_kernel<256, 1, 32>"},
