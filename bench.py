@@ -455,6 +455,28 @@ def run_grid(torch, fa, I, path):
     log(f"grid: {len(points)} points written to {path}")
 
 
+def run_small(torch, fa, I, calls=20):
+    """The few-unit workloads, each called `calls` times back to back (for
+    profiler runs; nothing is reported): the MQA decode at hd 128 and 512
+    over 128 and 512 keys through fmha_forward and fmha_forward_ws, and the
+    sliding-window MQA prefill."""
+    for w in (I.mqa_decode(128, 128), I.mqa_decode(128, 512), I.mqa_decode(512, 128), I.mqa_decode(512, 512),
+              I.SWA_MQA_PREFILL):
+        q, k, v = I.make_qkv(w, device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty((w.batch, w.n_h, w.T), dtype=torch.float32, device="cuda")
+        ws = fa.workspace_for(q, k, window=w.window, causal=w.causal)
+        for _ in range(calls):
+            fa.fmha_forward(q, k, v, o, lse, scale=w.scale, window=w.window, causal=w.causal)
+        if ws is not None:
+            for _ in range(calls):
+                fa.fmha_forward_ws(q, k, v, o, lse, ws, scale=w.scale, window=w.window, causal=w.causal)
+        torch.cuda.synchronize()
+        log(f"small {w.name}: {calls} fmha_forward calls" + (f" + {calls} fmha_forward_ws calls" if ws is not None
+                                                             else ""))
+        del q, k, v, o, lse, ws
+
+
 def run_mx_output(torch, fa, I):
     """The largest causal MHA prefill point with the output written as MX
     codes (FP8 E4M3, FP4 E2M1) instead of bf16, each timed like the prefill
@@ -592,6 +614,9 @@ def main():
                     help="skip the per-GPU share lines of the sharded decode (profiler runs of the headline kernel)")
     ap.add_argument("--cpu-seconds", type=float, default=40.0,
                     help="time budget of the CPU oracle baseline (all its workloads)")
+    ap.add_argument("--only-small", action="store_true",
+                    help="run only the few-unit workloads (MQA decode, sliding-window prefill) for profiler runs; "
+                         "prints no JSON line")
     ap.add_argument("--only-prefill", action="store_true",
                     help="time only the prefill workloads (for profiler runs); prints no JSON line")
     ap.add_argument("--grid", metavar="PATH",
@@ -625,6 +650,9 @@ def main():
 
     if args.grid:
         run_grid(torch, fa, I, args.grid)
+        return
+    if args.only_small:
+        run_small(torch, fa, I)
         return
     if args.only_prefill:
         run_prefill(torch, fa, I)
