@@ -99,11 +99,23 @@ __device__ __forceinline__ void load_lds_16(const void *gptr, void *lds_base) {
 // buffer form leaves the compiler's waits for LDS reads exact, so reads
 // issued ahead of their use stay in flight.  Raw buffer, 32-bit data format,
 // range check off (records = 2^32 - 1).
+template <bool NT = false>
 __device__ __forceinline__ void load_lds_buf(const void *base, unsigned voffset, void *lds_base) {
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, -1, 0x00020000);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds_base, 16,
-                                             voffset, 0, 0, 0);
+                                             voffset, 0, 0, NT ? 2 : 0);
+}
+
+// 16 bytes per lane into registers by a buffer load: base wave-uniform,
+// voffset the lane's byte offset from it (below 2^31); NT as above.  Lanes
+// then address rows by one 32-bit multiply-add instead of 64-bit pointer
+// arithmetic per load.
+template <bool NT = false>
+__device__ __forceinline__ u32x4 load16_buf(const void *base, unsigned voffset) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, -1, 0x00020000);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, 0, NT ? 2 : 0));
 }
 
 // 16 bytes per lane stored by a buffer store with the device-scope cache

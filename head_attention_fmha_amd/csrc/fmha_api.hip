@@ -145,13 +145,25 @@ bool stream_offsets_fit(const FwdParams &p, int hd) {
     return rows * slots * hd * 4 < (int64_t(1) << 31);
 }
 
+// The stream kernel loads K/V by buffer loads from each wave's first key
+// row with 32-bit lane offsets: a wave's rows (at most 64) must lie within
+// 2^31 bytes.
+bool stream_loads_fit(const FwdParams &p) {
+    const int64_t st = p.k_st > p.v_st ? p.k_st : p.v_st;
+    return 63 * st * 2 + 2 * 128 < (int64_t(1) << 31);
+}
+
 // Kernel variants the dispatcher launches (one template family each).
 enum Variant : int {
     kRowsTwoTiles,  // rows_kernel<HD, 2, 32>: 128 rows per workgroup (hd <= 128)
     kRowsOneTile,   // rows_kernel<HD, 1, rows_chunk_keys(HD)>: 64 rows per workgroup
     kAttnEight,     // attn_kernel, eight waves, several slices (hd >= 256)
-    kStream,        // stream_kernel<128, STREAM = true>: one pass, non-temporal whole-line K/V loads
-    kStreamShared,  // stream_kernel<128, STREAM = false>: one pass, row blocks sharing K/V through L2
+    kStream,        // stream_kernel<128, STREAM = true, 4, 1>: one pass, non-temporal whole-line K/V loads
+    kStreamShared,  // stream_kernel<128, STREAM = false, 4, 1>: one pass, row blocks sharing K/V through L2
+    kStreamWide,    // stream_kernel<128, true, 8, 1>: one pass of up to 256 keys, eight waves
+    kStreamWideShared,
+    kStreamWide2,   // stream_kernel<128, true, 8, 2>: one pass of up to 512 keys, eight waves
+    kStreamWide2Shared,
     kPass,          // pass_kernel<HD>: one pass over <= 128 keys, every load up front (hd >= 256)
     kAttnOneStream, // attn_kernel, one slice, streamed
     kAttnOne,       // attn_kernel, one slice, K/V shared with other row blocks
@@ -209,7 +221,13 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
     // hd 256 / 512 with every tile's keys within one 128-key pass (and not the
     // row-parallel kernel's many-row work): the one-pass kernel, eight waves
     const bool pass = !pl.row_parallel && hd >= 256 && span <= 128;
-    if (pass) {
+    // hd 128, up to 512 keys per tile and at most one tile per compute unit:
+    // each workgroup must take in its whole key range, and whole-row loads
+    // (the stream kernel, eight waves of 32 or 64 keys) reach it at about
+    // three times the rate of loads in the MFMA operand shape
+    const bool wide = !pl.row_parallel && hd == 128 && !pl.one_slice && span <= 512 && units1 <= kComputeUnits &&
+                      stream_loads_fit(p) && (!split || stream_offsets_fit(p, hd));
+    if (pass || wide) {
         pl.waves_per_group = 8;
         pl.tiles_per_group = 1;
         pl.one_slice = 1;
@@ -232,9 +250,16 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
     } else if (pass) {
         var = kPass;
         snprintf(pl.kernel, sizeof pl.kernel, "pass_kernel<%d, %s>", hd, sp);
-    } else if (pl.one_slice && hd == 128 && (!split || stream_offsets_fit(p, hd))) {
+    } else if (wide) {
+        const int ks = span <= 256 ? 1 : 2;
+        var = ks == 1 ? (pl.streaming ? kStreamWide : kStreamWideShared)
+                      : (pl.streaming ? kStreamWide2 : kStreamWide2Shared);
+        snprintf(pl.kernel, sizeof pl.kernel, "stream_kernel<%d, %s, %s, 8, %d>", hd, sp,
+                 pl.streaming ? "true" : "false", ks);
+    } else if (pl.one_slice && hd == 128 && stream_loads_fit(p) && (!split || stream_offsets_fit(p, hd))) {
         var = pl.streaming ? kStream : kStreamShared;
-        snprintf(pl.kernel, sizeof pl.kernel, "stream_kernel<%d, %s, %s>", hd, sp, pl.streaming ? "true" : "false");
+        snprintf(pl.kernel, sizeof pl.kernel, "stream_kernel<%d, %s, %s, 4, 1>", hd, sp,
+                 pl.streaming ? "true" : "false");
     } else {
         const int nw = pl.waves_per_group;
         const bool one = pl.one_slice, stream = pl.one_slice && pl.streaming;
@@ -274,11 +299,27 @@ void launch_hd(const FwdParams &p, int var, hipStream_t s) {
             break;
         case kStream:
             if constexpr (HD == 128)
-                hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, true>), dim3(p.n_units), dim3(256), 0, s, p);
+                hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, true, 4, 1>), dim3(p.n_units), dim3(256), 0, s, p);
             break;
         case kStreamShared:
             if constexpr (HD == 128)
-                hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, false>), dim3(p.n_units), dim3(256), 0, s, p);
+                hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, false, 4, 1>), dim3(p.n_units), dim3(256), 0, s, p);
+            break;
+        case kStreamWide:
+            if constexpr (HD == 128)
+                hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, true, 8, 1>), dim3(p.n_units), dim3(512), 0, s, p);
+            break;
+        case kStreamWideShared:
+            if constexpr (HD == 128)
+                hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, false, 8, 1>), dim3(p.n_units), dim3(512), 0, s, p);
+            break;
+        case kStreamWide2:
+            if constexpr (HD == 128)
+                hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, true, 8, 2>), dim3(p.n_units), dim3(512), 0, s, p);
+            break;
+        case kStreamWide2Shared:
+            if constexpr (HD == 128)
+                hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, false, 8, 2>), dim3(p.n_units), dim3(512), 0, s, p);
             break;
         case kPass:
             if constexpr (HD >= 256)

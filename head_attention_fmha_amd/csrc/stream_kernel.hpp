@@ -1,6 +1,9 @@
 // stream_kernel.hpp -- one-pass attention at hd 128 on gfx950: every
-// workgroup's keys fit one 128-key pass (the split-KV decode with 128-key
-// partitions; caches of at most 128 keys).
+// workgroup's keys fit one pass of NW waves x 32 KS keys (four waves x 32:
+// the split-KV decode with 128-key partitions, caches of at most 128 keys;
+// eight waves x 32 or 64: ranges of up to 256 or 512 keys on grids of at
+// most one workgroup per compute unit, such as the MQA decode of 128 query
+// heads over one KV head, where a workgroup must take in its whole range).
 //
 // Such work is bound by HBM bandwidth alone, and this GPU streams reads at
 // its best only with the non-temporal hint on loads that fetch whole cache
@@ -26,13 +29,13 @@
 // stands, and the key order of the V registers.  The PV result leaves lane
 // (lr, lg) holding row lr's columns 32lg .. 32lg+31.
 //
-// Softmax: each of the four waves takes 32 consecutive keys of the pass and
-// computes its own (max, sum, output) in one step -- the multi-tile kernel's
-// running max / running sum of the e4ee9fdc commit log of the pages with one
-// slice per wave -- and the four are combined once, in a fixed order,
-// through LDS, each wave combining and storing one quarter of the columns
-// (whole 128-byte lines of fp32 partials per store instruction, with the
-// device-scope cache policy).  Scores are base 2 (x = q.k * scale * log2 e); O is
+// Softmax: each wave takes 32 KS consecutive keys of the pass and computes
+// its own (max, sum, output) in one step -- the multi-tile kernel's running
+// max / running sum of the e4ee9fdc commit log of the pages with one slice
+// per wave -- and the NW waves are combined once, in a fixed order, through
+// LDS, each wave combining and storing one quarter of the columns of eight
+// or sixteen rows (whole 128-byte lines of fp32 partials per store
+// instruction, with the device-scope cache policy).  Scores are base 2 (x = q.k * scale * log2 e); O is
 // normalised by the sum of the bf16-rounded weights the PV product consumes
 // and lse uses the fp32 sum, as in attn_kernel.hpp.
 #pragma once
@@ -47,16 +50,19 @@ namespace fmha {
 // K/V, which is then loaded with the non-temporal hint.  Otherwise the row
 // blocks of a KV head share its K/V through L2 (plain loads, units
 // regrouped per XCD).
-template <int HD, bool SPLIT, bool STREAM>
-__global__ __launch_bounds__(256, 4) void stream_kernel(const FwdParams p) {
+// NW waves of 32 KS keys each; four waves per SIMD for up to 32 keys per
+// wave (V takes 32 registers), two for 64.
+template <int HD, bool SPLIT, bool STREAM, int NW, int KS>
+__global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const FwdParams p) {
     static_assert(HD == 128, "the stream kernel serves hd 128: one 16-lane run covers a key row");
+    static_assert((NW == 4 && KS == 1) || (NW == 8 && (KS == 1 || KS == 2)), "4 x 32, 8 x 32 or 8 x 64 keys");
     constexpr int KSTEPS = HD / 32;     // QK MFMA steps over the head dim
     constexpr int CHUNKS = HD / 8;      // 16-byte chunks per key row
     constexpr int ROW_BYTES = HD * 2;
-    constexpr int WAVE_KEYS = 32;
-    constexpr int K_BYTES = 4 * WAVE_KEYS * ROW_BYTES;  // four waves' K slices (32 KiB)
-    constexpr int SLOTS = 3 + 32;                       // merge record per lane: m, l, lq, 32 outputs
-    constexpr int M_BYTES = 4 * SLOTS * 64 * 4;          // four waves' records (35 KiB)
+    constexpr int WAVE_KEYS = 32 * KS;
+    constexpr int K_BYTES = NW * WAVE_KEYS * ROW_BYTES;  // every wave's K slice (32, 64 or 128 KiB)
+    constexpr int REC = 36;                              // merge record per lane: 32 outputs, m, l, lq, pad
+    constexpr int M_BYTES = NW * 64 * REC * 4;           // every wave's records (36 or 72 KiB)
     // the K slices, then (after every wave's QK) the merge records
     __shared__ __attribute__((aligned(16))) unsigned char smem[M_BYTES > K_BYTES ? M_BYTES : K_BYTES];
 
@@ -107,13 +113,13 @@ __global__ __launch_bounds__(256, 4) void stream_kernel(const FwdParams p) {
     const bool active = k0 < khi;            // wave-uniform
 
     // rotation of LDS key row r: chunk c lives in slot (c + rot(r)) % 16, so
-    // the 16 rows one QK read touches (keys 8(i/4) + 4b + i%4) use 16
+    // the 16 rows one QK read touches (keys 32ks + 8(i/4) + 4b + i%4) use 16
     // different slots -- all the banks
     auto rot_of = [](int r) __attribute__((always_inline)) { return (r + 4 * (r >> 4)) & (CHUNKS - 1); };
     unsigned char *sKw = smem + wave * WAVE_KEYS * ROW_BYTES;
 
     u32x4 qraw[KSTEPS];  // Q^T B operand: Q[row lr][32s + 8lg .. +7]
-    u32x4 vr[8];        // V[key k0 + 8lg + i][8lr .. 8lr + 7]
+    u32x4 vr[KS][8];    // V[key k0 + 32ks + 8lg + i][8lr .. 8lr + 7]
     if (active) {
         const uint16_t *qp = p.q + (int64_t)b * p.q_sb + (int64_t)t_row * p.q_st + (int64_t)h_row * p.q_sh + 8 * lg;
         // rows past the end read row 0 of the group (valid memory); they are
@@ -121,26 +127,30 @@ __global__ __launch_bounds__(256, 4) void stream_kernel(const FwdParams p) {
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) qraw[s] = *reinterpret_cast<const u32x4 *>(qp + 32 * s);
         __builtin_amdgcn_sched_barrier(0);
-        // K: eight wave-wide loads of four whole key rows each, into the
-        // wave's LDS slice (lane L lands at byte 16 L of the load's 1 KiB);
-        // keys past the range read key khi - 1 (finite data, weight 0)
-        const uint16_t *kbase = p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
+        // K and V by buffer loads from the wave's first key row: a lane's
+        // byte offset is its row (clamped to the last key of the range:
+        // rows past it reread that key -- finite data, weight 0) times the
+        // token stride, one 32-bit multiply-add per load (the host keeps a
+        // wave's rows within 2^31 bytes)
+        const int last = khi - 1 - k0;  // >= 0: the wave is active
+        const uint16_t *kw = p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh + key_offset(k0, p.k_st);
+        const uint16_t *vw = p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh + key_offset(k0, p.v_st);
+        const unsigned kstride = (unsigned)p.k_st * 2u, vstride = (unsigned)p.v_st * 2u;
+        // K: 8 KS wave-wide loads of four whole key rows each, into the
+        // wave's LDS slice (lane L lands at byte 16 L of the load's 1 KiB)
 #pragma unroll
         for (int it = 0; it < WAVE_KEYS / 4; ++it) {
             const int r = 4 * it + (lane >> 4);
             const int chunk = (lr - rot_of(r)) & (CHUNKS - 1);
-            const int key = min(k0 + r, khi - 1);
-            load_lds_16<STREAM>(kbase + key_offset(key, p.k_st) + 8 * chunk, sKw + it * 1024);
+            load_lds_buf<STREAM>(kw, (unsigned)min(r, last) * kstride + 16u * chunk, sKw + it * 1024);
         }
         __builtin_amdgcn_sched_barrier(0);  // Q, then K, then V: the waits below count on that order
-        // V: eight wave-wide register loads of four whole key rows each
-        const uint16_t *vbase = p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh + 8 * lr;
+        // V: 8 KS wave-wide register loads of four whole key rows each
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int key = min(k0 + 8 * lg + i, khi - 1);
-            const u32x4 *vp = reinterpret_cast<const u32x4 *>(vbase + key_offset(key, p.v_st));
-            vr[i] = STREAM ? __builtin_nontemporal_load(vp) : *vp;
-        }
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                vr[ks][i] = load16_buf<STREAM>(vw, (unsigned)min(32 * ks + 8 * lg + i, last) * vstride + 16u * lr);
         __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
     }
 
@@ -150,139 +160,176 @@ __global__ __launch_bounds__(256, 4) void stream_kernel(const FwdParams p) {
     for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (active) {
-        // Q and K have landed (V's eight loads, issued last, may still fly)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+        // Q and K have landed (V's 8 KS loads, issued last, may still fly)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * KS));
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const unsigned qmask = row_ok ? 0xffffffffu : 0u;
         bf16x8 qf[KSTEPS];
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, qraw[s] & qmask);
-        f32x4 sc[2];
+        f32x4 sc[KS][2];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            const int r = 8 * (lr >> 2) + 4 * blk + (lr & 3);
-            const unsigned char *rowp = sKw + r * ROW_BYTES;
-            const int rot = rot_of(r);
-            sc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                const int slot = (4 * s + lg + rot) & (CHUNKS - 1);
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(rowp + 16 * slot);
-                sc[blk] = mfma_16x16x32(kf, qf[s], sc[blk]);
+            for (int blk = 0; blk < 2; ++blk) {
+                const int r = 32 * ks + 8 * (lr >> 2) + 4 * blk + (lr & 3);
+                const unsigned char *rowp = sKw + r * ROW_BYTES;
+                const int rot = rot_of(r);
+                sc[ks][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KSTEPS; ++s) {
+                    const int slot = (4 * s + lg + rot) & (CHUNKS - 1);
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(rowp + 16 * slot);
+                    sc[ks][blk] = mfma_16x16x32(kf, qf[s], sc[ks][blk]);
+                }
             }
-        }
-        // scores of keys k0 + 8lg + j, j = 0..7: block 0 holds j < 4, block 1 the rest
-        float x[8];
+        // scores of keys k0 + 32ks + 8lg + j, j = 0..7: block 0 holds j < 4,
+        // block 1 the rest
+        float x[KS][8];
+        float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int key = k0 + 8 * lg + j;
-            const float s = j < 4 ? sc[0][j] : sc[1][j - 4];
-            x[j] = (key >= r_lo && key < r_hi) ? s * p.scale_log2 : -INFINITY;
-        }
-        float mx = x[0];
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+            for (int j = 0; j < 8; ++j) {
+                const int key = k0 + 32 * ks + 8 * lg + j;
+                const float s = j < 4 ? sc[ks][0][j] : sc[ks][1][j - 4];
+                x[ks][j] = (key >= r_lo && key < r_hi) ? s * p.scale_log2 : -INFINITY;
+                mx = fmaxf(mx, x[ks][j]);
+            }
         m = row4_max(mx);
         const float m_use = (m == -INFINITY) ? 0.f : m;
-        bf16x8 pt;
+        bf16x8 pt[KS];
         float psum = 0.f, qsum = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float pj = fast_exp2(x[j] - m_use);
-            const __bf16 pb = to_bf16(pj);
-            pt[j] = pb;
-            psum += pj;
-            qsum += (float)pb;
-        }
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float pj = fast_exp2(x[ks][j] - m_use);
+                const __bf16 pb = to_bf16(pj);
+                pt[ks][j] = pb;
+                psum += pj;
+                qsum += (float)pb;
+            }
         l = psum;
         lq = qsum;
-        // V^T operands: element i of MFMA j's operand is V[key 8lg + i][8lr + j];
+        // V^T operands: element i of MFMA j's operand is V[key 32ks + 8lg + i][8lr + j];
         // dword u pairs keys 2u, 2u+1 -- the low (j even) or high (j odd)
         // halves of dword j/2 of registers 2u and 2u+1 (v_perm_b32)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
-            u32x4 a;
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) a[u] = __builtin_amdgcn_perm(vr[2 * u + 1][j >> 1], vr[2 * u][j >> 1], sel);
-            acc[j] = mfma_16x16x32(__builtin_bit_cast(bf16x8, a), pt, f32x4{0.f, 0.f, 0.f, 0.f});
-        }
+            for (int j = 0; j < 8; ++j) {
+                const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                u32x4 a;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    a[u] = __builtin_amdgcn_perm(vr[ks][2 * u + 1][j >> 1], vr[ks][2 * u][j >> 1], sel);
+                acc[j] = mfma_16x16x32(__builtin_bit_cast(bf16x8, a), pt[ks],
+                                       ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[j]);
+            }
     }
 
     l = row4_sum(l);
     lq = row4_sum(lq);
 
-    // ---- combine the four waves' (m, l, lq, O) and store, by column quarters:
-    // every wave publishes its record, then wave w merges columns 32w .. 32w+31
-    // of every row in a fixed order (g = 0..3).  Lane (rr, q) = (lane / 8,
-    // lane % 8) takes rows rr and rr + 8, columns 32w + 4q .. +3, so each store
-    // instruction covers 8 rows x 128 contiguous bytes (fp32 partials: whole
-    // cache lines; a lane-local 32-column layout stored directly would leave
-    // 16-byte pieces, which measured 23% slower on the split decode)
+    // ---- combine the NW waves' (m, l, lq, O) and store, by column quarters:
+    // every wave publishes its record, then wave w merges columns 32cb ..
+    // 32cb + 31 (cb = w % 4) of its rows in a fixed order (g = 0 .. NW-1).
+    // Lane (rr, q) = (lane / 8, lane % 8) takes columns 32cb + 4q .. +3 of
+    // rows rr and rr + 8 (four waves) or of row rr + 8 (w / 4) (eight), so
+    // each store instruction covers 8 rows x 128 contiguous bytes (fp32
+    // partials: whole cache lines; a lane-local 32-column layout stored
+    // directly would leave 16-byte pieces, which measured 23% slower on the
+    // split decode).  Records are lane-major -- lane (lr, lg)'s 32 columns
+    // 32lg .. 32lg + 31 of row lr in order, then (m, l, lq) -- so a combine
+    // read of four columns or of (m, l, lq) is one 16-byte read, and the 8
+    // lanes of a row read 128 contiguous bytes (a slot-major layout put all
+    // of a record in one bank: 8-way conflicts)
+    const int q = lane & 7;
+    const int cb = wave & 3;             // column quarter
+    const int c = 32 * cb + 4 * q;       // this lane's first column
+    constexpr int HALVES = NW == 4 ? 2 : 1;
+    // output addressing of this lane's rows, fixed before the barriers
+    int rows_rr[HALVES];
+    int64_t o_off[HALVES], l_off[HALVES];
+#pragma unroll
+    for (int hh = 0; hh < HALVES; ++hh) {
+        const int half = NW == 4 ? hh : (wave >> 2);
+        const int rr = (lane >> 3) + 8 * half;
+        rows_rr[hh] = rr;
+        const int rw = row0 + rr;
+        const int rwc = rw < p.rows ? rw : row0;
+        const int t_o = rwc / p.group, g_o = rwc % p.group, h_o = kvh * p.group + g_o;
+        if constexpr (SPLIT) {
+            // partial rows of this KV head: r0 + (g_o T + t_o) n_split_total
+            o_off[hh] = ((int64_t)g_o * p.T + t_o) * p.n_split_total;
+            l_off[hh] = o_off[hh];
+        } else {
+            o_off[hh] = p.out_format != kOutBf16 ? ((int64_t)b * p.T + t_o) * p.n_h + h_o
+                                                 : (int64_t)b * p.o_sb + (int64_t)t_o * p.o_st + (int64_t)h_o * p.o_sh;
+            l_off[hh] = ((int64_t)b * p.n_h + h_o) * p.T + t_o;
+        }
+    }
     __syncthreads();  // every wave is done reading its K slice
     float *red = reinterpret_cast<float *>(smem);
     {
-        float *mine = red + wave * SLOTS * 64 + lane;
-        mine[0] = m;
-        mine[64] = l;
-        mine[128] = lq;
+        float *mine = red + (wave * 64 + lane) * REC;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) mine[(3 + 4 * j + t) * 64] = acc[j][t];
+            for (int h = 0; h < 2; ++h)
+                *reinterpret_cast<f32x4 *>(mine + 8 * t + 4 * h) =
+                    f32x4{acc[4 * h][t], acc[4 * h + 1][t], acc[4 * h + 2][t], acc[4 * h + 3][t]};
+        *reinterpret_cast<f32x4 *>(mine + 32) = f32x4{m, l, lq, 0.f};
     }
     __syncthreads();
-    const int q = lane & 7;
-    const int c = 32 * wave + 4 * q;     // this lane's first column
-    const int src_lg = c >> 5;           // source lane group: columns 32 lg .. 32 lg + 31
-    const int j0 = c & 7, t0 = (c & 31) >> 3;  // columns c + e sit at acc[j0 + e][t0]
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int rr = (lane >> 3) + 8 * half;
-        const int src = rr + 16 * src_lg;
+    for (int hh = 0; hh < HALVES; ++hh) {
+        const int rr = rows_rr[hh];
+        const float *src = red + (rr + 16 * cb) * REC;  // lane (rr, cb) of wave g: + g * 64 * REC
+        f32x4 rec[NW], val[NW];
+#pragma unroll
+        for (int g = 0; g < NW; ++g) {
+            rec[g] = *reinterpret_cast<const f32x4 *>(src + g * 64 * REC + 32);
+            val[g] = *reinterpret_cast<const f32x4 *>(src + g * 64 * REC + 4 * q);
+        }
         float M = -INFINITY;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) M = fmaxf(M, red[g * SLOTS * 64 + src]);
+        for (int g = 0; g < NW; ++g) M = fmaxf(M, rec[g][0]);
         const float M_use = (M == -INFINITY) ? 0.f : M;
         float L = 0.f, LQ = 0.f;
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float *rec = red + g * SLOTS * 64 + src;
-            const float wgt = fast_exp2(rec[0] - M_use);  // 0 for a wave with no visible key
-            L += wgt * rec[64];
-            LQ += wgt * rec[128];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] += wgt * rec[(3 + 4 * (j0 + e) + t0) * 64];
+        for (int g = 0; g < NW; ++g) {
+            const float wgt = fast_exp2(rec[g][0] - M_use);  // 0 for a wave with no visible key
+            L += wgt * rec[g][1];
+            LQ += wgt * rec[g][2];
+            o += wgt * val[g];
         }
-        const int rw = row0 + rr;
-        if (rw >= p.rows) continue;
-        const int t_o = rw / p.group, h_o = kvh * p.group + rw % p.group;
+        if (row0 + rr >= p.rows) continue;
         const float inv = LQ > 0.f ? 1.f / LQ : 0.f;
         const float lse_val = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
         o = o * inv;
         if constexpr (SPLIT) {
-            // rows of this KV head: r0 + ((rw % group) T + rw / group) n_split_total;
-            // byte offsets from the first fit 32 bits (the host checks it)
+            // byte offsets from the KV head's first partial row fit 32 bits
+            // (the host checks it)
             const int64_t r0 = ((int64_t)b * p.n_h + kvh * p.group) * p.T * p.n_split_total + p.part_offset + part;
-            const int64_t dr = ((int64_t)(rw % p.group) * p.T + rw / p.group) * p.n_split_total;
-            store16_device_scope(p.o_part + r0 * HD, (unsigned)((dr * HD + c) * 4), o);
-            if (wave == 0 && q == 0) p.lse_part[r0 + dr] = lse_val;
+            store16_device_scope(p.o_part + r0 * HD, (unsigned)((o_off[hh] * HD + c) * 4), o);
+            if (cb == 0 && q == 0) p.lse_part[r0 + l_off[hh]] = lse_val;
         } else {
             if (p.out_format != kOutBf16) {
                 // the wave's 32 columns are one MX block, over the 8 lanes of the row
-                const int64_t orow = ((int64_t)b * p.T + t_o) * p.n_h + h_o;
+                const int64_t orow = o_off[hh];
                 const float v4[4] = {o[0], o[1], o[2], o[3]};
                 mx_store_block_8lanes(v4, p.out_format, p.o_codes + orow * (p.out_format == kOutMxFp8E4M3 ? HD : HD / 2),
-                                      p.o_scales + orow * (HD / 32), 32 * wave, q);
+                                      p.o_scales + orow * (HD / 32), 32 * cb, q);
             } else {
                 uint2 packed;
                 packed.x = (uint32_t)bf16_bits(o[0]) | ((uint32_t)bf16_bits(o[1]) << 16);
                 packed.y = (uint32_t)bf16_bits(o[2]) | ((uint32_t)bf16_bits(o[3]) << 16);
-                *reinterpret_cast<uint2 *>(p.o + (int64_t)b * p.o_sb + (int64_t)t_o * p.o_st + (int64_t)h_o * p.o_sh +
-                                           c) = packed;
+                *reinterpret_cast<uint2 *>(p.o + o_off[hh] + c) = packed;
             }
-            if (wave == 0 && q == 0 && p.lse != nullptr) p.lse[((int64_t)b * p.n_h + h_o) * p.T + t_o] = lse_val;
+            if (cb == 0 && q == 0 && p.lse != nullptr) p.lse[l_off[hh]] = lse_val;
         }
     }
 }

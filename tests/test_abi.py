@@ -167,9 +167,10 @@ def test_merge_rejects(lib, kw, code):
     # per workgroup (two per KV head); at hd 128 the same with 256 units
     ((4, 32, 32, 128, 512, 512), dict(causal=True), (4, 4, 0, 0, 256)),
     ((4, 32, 32, 128, 512, 128), dict(causal=True), (4, 4, 0, 0, 256)),
-    # causal prefill T = 32: 256 units, eight waves at hd 256 and 512 only
+    # causal prefill T = 32: 256 units, eight waves -- the multi-slice kernel
+    # at hd 256, one pass of the stream kernel (512 keys) at hd 128
     ((4, 32, 32, 32, 512, 256), dict(causal=True), (8, 1, 0, 0, 256)),
-    ((4, 32, 32, 32, 512, 128), dict(causal=True), (4, 1, 0, 0, 256)),
+    ((4, 32, 32, 32, 512, 128), dict(causal=True), (8, 1, 1, 0, 256)),
     # single-head decode
     ((1, 1, 1, 1, 128, 64), {}, (4, 1, 1, 1, 1)),
     # sliding window MQA prefill: a 16-row tile is one position (16 heads) and
@@ -186,13 +187,20 @@ def test_plan_of_each_workload(lib, args, kw, want):
 
 
 @pytest.mark.parametrize("args,kw,kernel", [
-    ((32, 64, 8, 1, 8192, 128), dict(split_len=128), "stream_kernel<128, true, true>"),
+    ((32, 64, 8, 1, 8192, 128), dict(split_len=128), "stream_kernel<128, true, true, 4, 1>"),
     ((8, 128, 1, 1, 512, 512), {}, "attn_kernel<512, 8, 2, 4, 1, false, false, false>"),
     ((8, 128, 1, 1, 512, 512), dict(split_len=128), "pass_kernel<512, true>"),
     ((2, 16, 1, 128, 4096, 512), dict(causal=True, window=128), "pass_kernel<512, false>"),
     ((4, 32, 32, 128, 512, 512), dict(causal=True), "rows_kernel<512, 1, 32, false>"),
     ((2, 32, 8, 4096, 4096, 128), dict(causal=True), "rows_kernel<128, 2, 32, false>"),
     ((1, 1, 1, 1, 128, 64), {}, "attn_kernel<64, 4, 4, 1, 1, false, true, true>"),
+    # MQA decode at hd 128 over 256 / 512 keys (64 tiles): one pass of eight waves
+    ((8, 128, 1, 1, 256, 128), {}, "stream_kernel<128, false, false, 8, 1>"),
+    ((8, 128, 1, 1, 512, 128), {}, "stream_kernel<128, false, false, 8, 2>"),
+    # causal MHA prefill T 1, hd 128, 512 keys (128 one-row tiles, nothing shared)
+    ((4, 32, 32, 1, 512, 128), dict(causal=True), "stream_kernel<128, false, true, 8, 2>"),
+    # more tiles than compute units: the per-wave kernel
+    ((32, 256, 1, 1, 512, 128), {}, "attn_kernel<128, 4, 4, 1, 1, false, false, false>"),
 ])
 def test_plan_names_the_kernel_of_each_workload(lib, args, kw, kernel):
     assert fa.fmha_attention_plan(*args, **kw)["kernel"] == kernel
@@ -326,15 +334,15 @@ def test_stream_kernel_serves_the_split_decode_while_its_offsets_fit(lib):
     partition slots that a workgroup's 16 rows of fp32 partials span 2 GiB or
     more (its buffer stores take 32-bit offsets) the per-wave kernel runs."""
     got = fa.fmha_attention_plan(32, 64, 8, 1, 8192, 128, split_len=128)
-    assert got["kernel"] == "stream_kernel<128, true, true>"
+    assert got["kernel"] == "stream_kernel<128, true, true, 4, 1>"
     ok = fa.fmha_attention_plan(1, 1, 1, 1, (1 << 18) - 1, 128, split_len=1)
-    assert ok["kernel"] == "stream_kernel<128, true, true>"
+    assert ok["kernel"] == "stream_kernel<128, true, true, 4, 1>"
     big = fa.fmha_attention_plan(1, 1, 1, 1, 1 << 18, 128, split_len=1)
     assert big["kernel"] == "attn_kernel<128, 4, 4, 1, 1, true, true, true>"
     # fused calls (no partials) with one slice and one row block
-    assert fa.fmha_attention_plan(4, 32, 32, 1, 128, 128)["kernel"] == "stream_kernel<128, false, true>"
+    assert fa.fmha_attention_plan(4, 32, 32, 1, 128, 128)["kernel"] == "stream_kernel<128, false, true, 4, 1>"
     # row blocks sharing K/V (128 query heads over one KV head): the shared form
-    assert fa.fmha_attention_plan(8, 128, 1, 1, 128, 128)["kernel"] == "stream_kernel<128, false, false>"
+    assert fa.fmha_attention_plan(8, 128, 1, 1, 128, 128)["kernel"] == "stream_kernel<128, false, false, 4, 1>"
 
 
 

@@ -64,6 +64,6 @@ def test_roofline_kernel_is_the_planned_one():
     import head_attention_fmha_amd as fa
     w = I.GQA_SPLITKV_DECODE
     plan = fa.fmha_attention_plan(w.batch, w.n_h, w.n_kv_h, w.T, w.s_k, w.hd, split_len=w.split_len)
-    assert plan["kernel"] == "stream_kernel<128, true, true>"
+    assert plan["kernel"] == "stream_kernel<128, true, true, 4, 1>"
     assert plan["workgroups"] == w.batch * w.n_kv_h * w.n_split
     assert plan["threads_per_group"] == 256

@@ -17,6 +17,10 @@ SHAPES = [
     ("row-parallel-two-tiles", (4, 128, 128, 100, 200), 0, True, 0),
     ("mqa-short-cache", (2, 32, 1, 1, 100), 0, False, 0),
     ("window-group7-straddling-tiles", (1, 7, 1, 40, 300), 0, True, 30),
+    ("wide-streamed-256", (2, 4, 4, 1, 250), 0, True, 0),
+    ("wide-shared-512", (2, 40, 1, 1, 500), 0, False, 0),
+    ("wide-streamed-split-512", (2, 8, 2, 3, 1300), 480, True, 0),
+    ("wide-shared-split-256", (1, 48, 2, 1, 700), 200, False, 0),
 ]
 
 HEAD_DIMS = (64, 128, 256, 512)
@@ -41,7 +45,9 @@ EXPECTED = {
          "attn_kernel<64, 4, 4, 1, 1, true, false>", "attn_kernel<64, 4, 4, 1, 1, true, true>",
          "rows_kernel<64, 1, 64>", "rows_kernel<64, 2, 32>"},
     128: {"attn_kernel<128, 4, 4, 1, 1, false, false>", "attn_kernel<128, 4, 4, 1, 2, false, false>",
-          "stream_kernel<128, true>", "stream_kernel<128, false>",
+          "stream_kernel<128, true, 4, 1>", "stream_kernel<128, false, 4, 1>",
+          "stream_kernel<128, true, 8, 1>", "stream_kernel<128, false, 8, 1>",
+          "stream_kernel<128, true, 8, 2>", "stream_kernel<128, false, 8, 2>",
           "rows_kernel<128, 1, 64>", "rows_kernel<128, 2, 32>"},
     256: {"attn_kernel<256, 4, 2, 2, 1, false, false>", "attn_kernel<256, 4, 2, 2, 2, false, false>",
           "attn_kernel<256, 8, 4, 2, 1, false, false>", "pass_kernel<256>", "rows_kernel<256, 1, 32>"},
