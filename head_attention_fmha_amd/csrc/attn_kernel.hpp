@@ -104,6 +104,7 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
     constexpr int VM_BYTES = V_BYTES > S::M_BYTES ? V_BYTES : S::M_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char smem[VM_BYTES + (ONE ? 1 : 2) * S::S_BUF];
 
+    fetch_launch_params(p);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int kg = wave / NH;  // key group

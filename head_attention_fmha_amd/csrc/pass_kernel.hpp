@@ -79,6 +79,7 @@ __global__ __launch_bounds__(512, 2) void pass_kernel(const FwdParams p) {
     constexpr int CPW = S::CPW, LPR = S::LPR, RPI = S::RPI;
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::SMEM];
 
+    fetch_launch_params(p);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int kg = wave / NH;  // key group
@@ -177,6 +178,9 @@ __global__ __launch_bounds__(512, 2) void pass_kernel(const FwdParams p) {
         bf16x8 qf[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) qf[s] = __builtin_bit_cast(bf16x8, qraw[s] & qmask);
+        // every K operand read issued before the first MFMA (a read waited
+        // for right before its MFMA costs a full LDS round trip each)
+        bf16x8 kf[4][KS][2];
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -184,10 +188,16 @@ __global__ __launch_bounds__(512, 2) void pass_kernel(const FwdParams p) {
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk) {
                     const int r = 32 * ks + 8 * (lr >> 2) + 4 * blk + (lr & 3);
-                    const bf16x8 kf =
+                    kf[s][ks][blk] =
                         *reinterpret_cast<const bf16x8 *>(sKw + r * 256 + 16 * ((4 * s + lg + rot_of(r)) & 15));
-                    sc[ks][blk] = mfma_16x16x32(kf, qf[s], sc[ks][blk]);
                 }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk) sc[ks][blk] = mfma_16x16x32(kf[s][ks][blk], qf[s], sc[ks][blk]);
     }
     float *sS = reinterpret_cast<float *>(smem + S::K_BYTES);
     // one 16-byte record per lane and 16-key block: [wave][ks][blk][lane]

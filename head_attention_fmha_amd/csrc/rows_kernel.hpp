@@ -76,6 +76,7 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
     __shared__ __attribute__((aligned(16))) unsigned char sV0[SLOT_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char sV1[SLOT_BYTES];
 
+    fetch_launch_params(p);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15;

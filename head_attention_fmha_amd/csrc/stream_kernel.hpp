@@ -66,6 +66,7 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
     // the K slices, then (after every wave's QK) the merge records
     __shared__ __attribute__((aligned(16))) unsigned char smem[M_BYTES > K_BYTES ? M_BYTES : K_BYTES];
 
+    fetch_launch_params(p);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15;
@@ -167,22 +168,30 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
         bf16x8 qf[KSTEPS];
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, qraw[s] & qmask);
+        // every K operand read is issued before the first MFMA (a read waited
+        // for right before its MFMA costs a full LDS round trip each); the
+        // MFMAs then alternate between the 2 KS independent accumulators
+        bf16x8 kf[KSTEPS][KS][2];
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk) {
+                    const int r = 32 * ks + 8 * (lr >> 2) + 4 * blk + (lr & 3);
+                    const int slot = (4 * s + lg + rot_of(r)) & (CHUNKS - 1);
+                    kf[s][ks][blk] = *reinterpret_cast<const bf16x8 *>(sKw + r * ROW_BYTES + 16 * slot);
+                }
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 sc[KS][2];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks) sc[ks][0] = sc[ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                const int r = 32 * ks + 8 * (lr >> 2) + 4 * blk + (lr & 3);
-                const unsigned char *rowp = sKw + r * ROW_BYTES;
-                const int rot = rot_of(r);
-                sc[ks][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
-                for (int s = 0; s < KSTEPS; ++s) {
-                    const int slot = (4 * s + lg + rot) & (CHUNKS - 1);
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(rowp + 16 * slot);
-                    sc[ks][blk] = mfma_16x16x32(kf, qf[s], sc[ks][blk]);
-                }
-            }
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk) sc[ks][blk] = mfma_16x16x32(kf[s][ks][blk], qf[s], sc[ks][blk]);
         // scores of keys k0 + 32ks + 8lg + j, j = 0..7: block 0 holds j < 4,
         // block 1 the rest
         float x[KS][8];
