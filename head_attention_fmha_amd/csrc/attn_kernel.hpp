@@ -185,18 +185,29 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
     const float c_scale = fabsf(p.scale_log2);
     const unsigned q_flip = (LAZY && p.scale_log2 < 0.f) ? 0x80008000u : 0u;
     const int col0 = hp * HDP;  // first head-dim column of this wave
-    bf16x8 qf[MT][KSTEPS];      // Q^T B operand: Q[row lr][col0 + 32*s + 8*lg + 0..7]
+    // Q^T B operand: Q[row lr][col0 + 32*s + 8*lg + 0..7], loaded
+    // unconditionally: a row past the end reads row 0 of the group (valid
+    // memory; its lanes' scores, softmax state and output stay in its own
+    // MFMA column and are never stored).  A load under a lane condition, or
+    // one used right away, was waited for on the spot, a full memory round
+    // trip before the first K/V load went out: only the lazy form's sign
+    // flip touches Q, once the first slice's loads are issued (finish_q)
+    u32x4 qraw[MT][KSTEPS];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const uint16_t *qp = p.q + (int64_t)b * p.q_sb + (int64_t)t_of[mt] * p.q_st + (int64_t)h_of[mt] * p.q_sh +
                              col0 + 8 * lg;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-            u32x4 raw = row_ok[mt] ? *reinterpret_cast<const u32x4 *>(qp + 32 * s) : u32x4{0u, 0u, 0u, 0u};
-            raw ^= q_flip;
-            qf[mt][s] = __builtin_bit_cast(bf16x8, raw);
-        }
+        for (int s = 0; s < KSTEPS; ++s) qraw[mt][s] = *reinterpret_cast<const u32x4 *>(qp + 32 * s);
     }
+    bf16x8 qf[MT][KSTEPS];
+    auto finish_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s)
+                qf[mt][s] = __builtin_bit_cast(bf16x8, LAZY ? qraw[mt][s] ^ q_flip : qraw[mt][s]);
+    };
 
     f32x4 acc[MT][NB];
     f32x4 accq[MT];  // LAZY: the bf16 weight sum of row lr, in every element (-> O)
@@ -435,6 +446,7 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
                 load_k(k0, kf);
                 __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
             }
+            finish_q();
             f32x4 s0[MT], s1[MT];
             scores(active, 0, kf, s0, s1);
             if (active) {
@@ -510,6 +522,7 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
                 load_k(klo + (n + 1) * chunk_keys + 32 * kg, kfB);
                 load_v(klo + (n + 1) * chunk_keys + 32 * kg, vrB);
                 __builtin_amdgcn_sched_barrier(0);  // keep all 2 x (K + V) loads ahead of the math
+                if (n == 0) finish_q();
                 step(n, kfA, vrA, nothing, nothing);
                 if (n + 1 < nslices) step(n + 1, kfB, vrB, nothing, nothing);
             }
@@ -524,6 +537,8 @@ __global__ __launch_bounds__(64 * NW, attn_min_waves(NW, NH, ONE)) void attn_ker
             // (valid memory; the last prefetch is never used)
             bf16x8 kf[2][KSTEPS];
             if (nslices > 0) load_k(klo + 32 * kg, kf);  // khi > klo >= 0: clamped keys are valid
+            __builtin_amdgcn_sched_barrier(0);
+            finish_q();
             for (int n = 0; n < nslices; ++n) {
                 const int k_cur = klo + n * chunk_keys + 32 * kg;
                 u32x4 vr[VLOADS];

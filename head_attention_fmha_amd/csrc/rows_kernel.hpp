@@ -145,18 +145,27 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
     // weight rounds to exactly 1, as with the scale 0 itself.
     const float c_scale = fmaxf(fabsf(p.scale_log2), FLT_MIN);
     const unsigned q_flip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
-    bf16x8 qf[RT][KSTEPS];  // Q^T B operand: Q[row lr][32*s + 8*lg + 0..7]
+    // Q^T B operand: Q[row lr][32*s + 8*lg + 0..7], loaded unconditionally (a
+    // row past the end reads row 0 of the group, valid memory) and zeroed and
+    // sign-flipped only once the first chunks' loads are issued: a load under
+    // a lane condition, or one used right away, was waited for on the spot,
+    // a full memory round trip before the first K/V load went out
+    u32x4 qraw[RT][KSTEPS];
 #pragma unroll
     for (int mt = 0; mt < RT; ++mt) {
         const uint16_t *qp =
             p.q + (int64_t)b * p.q_sb + (int64_t)t_of[mt] * p.q_st + (int64_t)h_of[mt] * p.q_sh + 8 * lg;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-            u32x4 raw = row_ok[mt] ? *reinterpret_cast<const u32x4 *>(qp + 32 * s) : u32x4{0u, 0u, 0u, 0u};
-            raw ^= q_flip;
-            qf[mt][s] = __builtin_bit_cast(bf16x8, raw);
-        }
+        for (int s = 0; s < KSTEPS; ++s) qraw[mt][s] = *reinterpret_cast<const u32x4 *>(qp + 32 * s);
     }
+    bf16x8 qf[RT][KSTEPS];
+    auto finish_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < RT; ++mt)
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s)
+                qf[mt][s] = __builtin_bit_cast(bf16x8, (qraw[mt][s] & (row_ok[mt] ? 0xffffffffu : 0u)) ^ q_flip);
+    };
 
     f32x4 acc[RT][NB];
     f32x4 accq[RT];  // every element: the running sum of row lr's bf16 weights (-> O)
@@ -235,6 +244,21 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
     // PITCH + 32 nb (the rotation of a row depends on its index mod 8 only)
     const int k_lane = lr * PITCH + (lg + rot_of(lr)) * 16;
     const int v_lane = tr_row0 * PITCH + ((tr_col >> 3) + rot_of(tr_row0)) * 16 + (tr_col & 7) * 2;
+    // one 32-key PV slice per chunk and at least four head-dim steps: the
+    // step runs in the explicit order below (operands read ahead of their
+    // MFMAs); rotated rows then need one address per head-dim step (K) and
+    // per column block (V^T) -- a row's rotation depends on its index mod 8,
+    // which 16-key block offsets keep
+    constexpr bool ORDERED = SHIFTED || (KS == 1 && KSTEPS >= 4 && NB >= 4);
+    constexpr int NKA = (ORDERED && !SHIFTED) ? KSTEPS : 1, NVA = (ORDERED && !SHIFTED) ? NB : 1;
+    int k_at[NKA], v_at[NVA];
+#pragma unroll
+    for (int st = 0; st < NKA; ++st) k_at[st] = lr * ROW_BYTES + ((4 * st + lg + rot_of(lr)) % CHUNKS) * 16;
+#pragma unroll
+    for (int nb = 0; nb < NVA; ++nb) {
+        const int c = 16 * nb + tr_col;
+        v_at[nb] = tr_row0 * ROW_BYTES + (((c >> 3) + rot_of(tr_row0)) % CHUNKS) * 16 + (c & 7) * 2;
+    }
 
     // ---- S^T of one staged chunk for every tile of this wave: KB blocks of 16
     // keys; each K operand read from LDS feeds the MFMAs of all the tiles.
@@ -372,16 +396,97 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
         }
     };
 
-    // ---- hd 512 (shifted rows): the straight-line part of a step -- chunk
-    // n+1's QK product, chunk n's weights and PV product -- in an explicit
-    // order.  One wave per SIMD has no other wave to cover LDS latency, so
-    // each K operand is read D head-dim steps before its MFMAs and each V^T
-    // operand D column blocks before its MFMA (the first D of them during the
-    // last QK steps), and the weights' vector work is spread over the QK
-    // steps, one element per step, beside the MFMAs.  The scheduling barriers
-    // keep the compiler from regrouping the phases: it would otherwise issue
-    // every read just before its use and wait for it there.
+    // ---- one 32-key PV slice per chunk (hd 128 and 256 at 32-key chunks):
+    // the straight-line part of a step -- chunk n's weights, then
+    // chunk n+1's QK product interleaved with chunk n's PV product -- in an
+    // explicit order.  The QK product has only RT KB accumulators (2 or 4),
+    // each a chain over the head-dim steps, and a 16x16x32 MFMA that depends
+    // on the one just issued waits for it: each QK step is therefore followed
+    // by the PV MFMAs of NB / KSTEPS column blocks (RT NB independent
+    // accumulators), so the MFMA pipe always has independent work.  One or
+    // two waves per SIMD leave little to cover LDS latency, so each K operand
+    // is read D head-dim steps and each V^T operand DV steps before its
+    // MFMAs; the scheduling barriers keep the compiler from regrouping (it
+    // would issue every read just before its use and wait for it there).
     auto fused = [&](const unsigned char *sK, f32x4 (&sn)[RT][KB], const f32x4 (&sc)[RT][KB],
+                     const unsigned char *sV) __attribute__((always_inline)) {
+        static_assert(!ORDERED || (KS == 1 && KSTEPS >= 4 && NB % KSTEPS == 0), "one PV slice per chunk");
+        constexpr int D = 4, R = D + 1;     // K read-ahead (head-dim steps), ring size
+        constexpr int BPS = NB / KSTEPS;    // PV column blocks per QK step
+        constexpr int DV = 2, RV = DV + 1;  // V^T read-ahead (steps), ring size
+        auto read_k = [&](int st, bf16x8 (&kf)[KB]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                kf[kb] = SHIFTED ? *reinterpret_cast<const bf16x8 *>(sK + k_lane + 16 * kb * PITCH + 64 * st)
+                                 : *reinterpret_cast<const bf16x8 *>(sK + k_at[st] + 16 * kb * ROW_BYTES);
+        };
+        auto read_v = [&](int nb) __attribute__((always_inline)) {
+            bf16x4 q2[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+                q2[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (__attribute__((address_space(3))) bf16x4 *)(sV + (SHIFTED ? v_lane + 16 * half * PITCH + 32 * nb
+                                                                                : v_at[nb] + 16 * half * ROW_BYTES)));
+            return __builtin_shufflevector(q2[0], q2[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        bf16x8 kf[R][KB];
+        bf16x8 vt[RV][BPS];
+#pragma unroll
+        for (int st = 0; st < D; ++st) read_k(st, kf[st]);
+#pragma unroll
+        for (int sv = 0; sv < DV; ++sv)
+#pragma unroll
+            for (int u = 0; u < BPS; ++u) vt[sv][u] = read_v(sv * BPS + u);
+        // chunk n's weights 2^(s c - m), their bf16 forms and sums
+        bf16x8 pt[RT];
+#pragma unroll
+        for (int mt = 0; mt < RT; ++mt) {
+            float psum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float pj = fast_exp2(fmaf(sc[mt][kb][j], c_scale, neg_m[mt]));
+                    pt[mt][kb * 4 + j] = to_bf16(pj);
+                    psum += pj;
+                }
+            l[mt] += psum;
+        }
+#pragma unroll
+        for (int mt = 0; mt < RT; ++mt)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) sn[mt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int mt = 0; mt < RT; ++mt) sn[mt][kb] = mfma_16x16x32(kf[st % R][kb], qf[mt][st], sn[mt][kb]);
+#pragma unroll
+            for (int u = 0; u < BPS; ++u)
+#pragma unroll
+                for (int mt = 0; mt < RT; ++mt)
+                    acc[mt][st * BPS + u] = mfma_16x16x32(vt[st % RV][u], pt[mt], acc[mt][st * BPS + u]);
+            if (st == 0) {
+#pragma unroll
+                for (int mt = 0; mt < RT; ++mt) accq[mt] = mfma_16x16x32(ones, pt[mt], accq[mt]);
+            }
+            if (st + D < KSTEPS) read_k(st + D, kf[(st + D) % R]);
+            if (st + DV < KSTEPS) {
+#pragma unroll
+                for (int u = 0; u < BPS; ++u) vt[(st + DV) % RV][u] = read_v((st + DV) * BPS + u);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- hd 512 (shifted rows, one wave per SIMD): the same step with the
+    // PV product after the QK product and the weights' vector work spread
+    // over the QK steps, one element per step (interleaving the two products
+    // as above measured 1.3% slower here: the single wave's weights then sit
+    // between the reads and the first MFMAs)
+    auto fused_shifted = [&](const unsigned char *sK, f32x4 (&sn)[RT][KB], const f32x4 (&sc)[RT][KB],
                      const unsigned char *sV) __attribute__((always_inline)) {
         static_assert(!SHIFTED || (KS == 1 && KSTEPS >= RT * KB * 4 && KSTEPS >= 4 && NB >= 4), "one PV slice per chunk");
         constexpr int D = 4, R = D + 1;  // read-ahead distance, ring size
@@ -448,11 +553,12 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
     // ---- the pipeline.  Step n starts with chunk n+1's K and chunk n's V on
     // chip and chunk n's scores in registers; it requests chunk n+2's K and
     // chunk n+1's V into the slots step n-1 finished with, then computes
-    // chunk n+1's scores alongside chunk n's weights, then chunk n's PV
-    // product.  One barrier per step: every wave's loads of the previous step
-    // have landed and every wave is done reading the slots about to be
-    // refilled.  After the last chunk the QK product reads a stale K slot;
-    // those scores are never used.
+    // chunk n+1's scores alongside chunk n's weights and PV product.  One
+    // barrier per step: every wave's loads of the previous step have landed
+    // and every wave is done reading the slots about to be refilled.  After
+    // the last chunk the QK product reads a stale K slot; those scores are
+    // never used.  (Loads issued two steps ahead, from a ring of three slots
+    // per operand at hd 128, measured 1-2% slower on the long prefill.)
     const int nchunks = khi > klo ? (khi - klo + KC - 1) / KC : 0;  // wave-uniform
     f32x4 sc[RT][KB];
     if (nchunks > 0) {
@@ -460,13 +566,15 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
         // chunk 0's V and chunk 1's K stay in flight during that product
         issue(kbase, p.k_st, ld_koff, klo, sK0);
         issue(vbase, p.v_st, ld_voff, klo, sV0);
+        if (nchunks > 1) issue(kbase, p.k_st, ld_koff, klo + KC, sK1);
+        __builtin_amdgcn_sched_barrier(0);  // every prologue load issued before Q is used
         if (nchunks > 1) {
-            issue(kbase, p.k_st, ld_koff, klo + KC, sK1);
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS));
         } else {
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS));
         }
         lds_barrier();
+        finish_q();
         qk(sK0, sc);
     }
     auto step = [&](int n, const unsigned char *sKnext, const unsigned char *sVcur, unsigned char *sKfill,
@@ -479,6 +587,8 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
         prep(k0, sc);
         f32x4 sn[RT][KB];
         if constexpr (SHIFTED) {
+            fused_shifted(sKnext, sn, sc, sVcur);
+        } else if constexpr (ORDERED) {
             fused(sKnext, sn, sc, sVcur);
         } else {
             qk(sKnext, sn);
