@@ -15,6 +15,7 @@
 #include "attn_kernel.hpp"
 #include "rows_kernel.hpp"
 #include "stream_kernel.hpp"
+#include "rows_split_kernel.hpp"
 #include "pass_kernel.hpp"
 #include "merge_kernel.hpp"
 
@@ -157,6 +158,7 @@ bool stream_loads_fit(const FwdParams &p) {
 enum Variant : int {
     kRowsTwoTiles,  // rows_kernel<HD, 2, 32>: 128 rows per workgroup (hd <= 128)
     kRowsOneTile,   // rows_kernel<HD, 1, rows_chunk_keys(HD)>: 64 rows per workgroup
+    kRowsSplit,     // rows_split_kernel<512>: 64 rows per workgroup, each tile's head dim over two waves
     kAttnEight,     // attn_kernel, eight waves, several slices (hd >= 256)
     kStream,        // stream_kernel<128, STREAM = true, 4, 1>: one pass, non-temporal whole-line K/V loads
     kStreamShared,  // stream_kernel<128, STREAM = false, 4, 1>: one pass, row blocks sharing K/V through L2
@@ -213,7 +215,9 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
         const int64_t groups2 = (int64_t)((p.rows + 127) / 128) * per_kv;
         if (groups1 >= kComputeUnits) {
             pl.row_parallel = 1;
-            pl.waves_per_group = 4;
+            // hd 512: every tile's head dimension over two waves (eight per
+            // workgroup, two per SIMD)
+            pl.waves_per_group = hd == 512 ? 8 : 4;
             // (two tiles of 256 or 512 columns would spill: one tile per wave)
             pl.tiles_per_group = (hd <= 128 && groups2 >= 2 * kComputeUnits) ? 8 : 4;
         }
@@ -243,7 +247,10 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
     int var;
     const int nh = head_parts(hd);
     const char *sp = split ? "true" : "false";
-    if (pl.row_parallel) {
+    if (pl.row_parallel && hd == 512) {
+        var = kRowsSplit;
+        snprintf(pl.kernel, sizeof pl.kernel, "rows_split_kernel<%d, %s>", hd, sp);
+    } else if (pl.row_parallel) {
         var = (hd <= 128 && pl.tiles_per_group == 8) ? kRowsTwoTiles : kRowsOneTile;
         snprintf(pl.kernel, sizeof pl.kernel, "rows_kernel<%d, %d, %d, %s>", hd, var == kRowsTwoTiles ? 2 : 1,
                  var == kRowsTwoTiles ? 32 : rows_chunk_keys(hd), sp);
@@ -290,8 +297,13 @@ void launch_hd(const FwdParams &p, int var, hipStream_t s) {
                 hipLaunchKernelGGL((fmha::rows_kernel<HD, 2, 32, SPLIT>), dim3(p.n_units), dim3(256), 0, s, p);
             break;
         case kRowsOneTile:
-            hipLaunchKernelGGL((fmha::rows_kernel<HD, 1, rows_chunk_keys(HD), SPLIT>), dim3(p.n_units), dim3(256), 0,
-                               s, p);
+            if constexpr (HD < 512)
+                hipLaunchKernelGGL((fmha::rows_kernel<HD, 1, rows_chunk_keys(HD), SPLIT>), dim3(p.n_units), dim3(256),
+                                   0, s, p);
+            break;
+        case kRowsSplit:
+            if constexpr (HD == 512)
+                hipLaunchKernelGGL((fmha::rows_split_kernel<HD, SPLIT>), dim3(p.n_units), dim3(512), 0, s, p);
             break;
         case kAttnEight:
             // chosen only for several slices per wave (never one-slice), hd >= 256

@@ -164,8 +164,9 @@ def test_merge_rejects(lib, kw, code):
     # the same through a head stride of 0 with n_kv_h = n_h: planned as MQA
     ((8, 128, 128, 1, 512, 512), dict(mqa_stride0=True), (8, 1, 0, 0, 64)),
     # causal prefill T = 128, s_k = 512, hd 512: the row-parallel kernel, 64 rows
-    # per workgroup (two per KV head); at hd 128 the same with 256 units
-    ((4, 32, 32, 128, 512, 512), dict(causal=True), (4, 4, 0, 0, 256)),
+    # per workgroup (two per KV head), each tile's head dim over two of its
+    # eight waves; at hd 128 four waves and the same 256 units
+    ((4, 32, 32, 128, 512, 512), dict(causal=True), (8, 4, 0, 0, 256)),
     ((4, 32, 32, 128, 512, 128), dict(causal=True), (4, 4, 0, 0, 256)),
     # causal prefill T = 32: 256 units, eight waves -- the multi-slice kernel
     # at hd 256, one pass of the stream kernel (512 keys) at hd 128
@@ -191,7 +192,7 @@ def test_plan_of_each_workload(lib, args, kw, want):
     ((8, 128, 1, 1, 512, 512), {}, "attn_kernel<512, 8, 2, 4, 1, false, false, false>"),
     ((8, 128, 1, 1, 512, 512), dict(split_len=128), "pass_kernel<512, true>"),
     ((2, 16, 1, 128, 4096, 512), dict(causal=True, window=128), "pass_kernel<512, false>"),
-    ((4, 32, 32, 128, 512, 512), dict(causal=True), "rows_kernel<512, 1, 32, false>"),
+    ((4, 32, 32, 128, 512, 512), dict(causal=True), "rows_split_kernel<512, false>"),
     ((2, 32, 8, 4096, 4096, 128), dict(causal=True), "rows_kernel<128, 2, 32, false>"),
     ((1, 1, 1, 1, 128, 64), {}, "attn_kernel<64, 4, 4, 1, 1, false, true, true>"),
     # MQA decode at hd 128 over 256 / 512 keys (64 tiles): one pass of eight waves
