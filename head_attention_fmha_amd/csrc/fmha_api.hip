@@ -134,7 +134,10 @@ constexpr int rows_chunk_keys(int hd) { return hd <= 128 ? 64 : 32; }
 // load (1024 / (2 hd) of them) must lie within 2^31 bytes.
 bool rows_loads_fit(const FwdParams &p, int hd) {
     const int64_t st = p.k_st > p.v_st ? p.k_st : p.v_st;
-    return (int64_t)(1024 / (2 * hd) - 1) * st * 2 + 2 * hd < (int64_t(1) << 31);
+    // (hd 512: the head-split kernel addresses a whole 32-key chunk from its
+    // first row)
+    const int64_t rows = hd == 512 ? 31 : 1024 / (2 * hd) - 1;
+    return rows * st * 2 + 2 * hd < (int64_t(1) << 31);
 }
 
 // The stream kernel stores split partials by buffer stores with 32-bit byte

@@ -141,14 +141,31 @@ __global__ __launch_bounds__(512, 2) void rows_split_kernel(const FwdParams p) {
     // LOADS w + LOADS - 1, one whole row per load, lane L fetching the 16-byte
     // chunk that belongs at slot L under the row's rotation; a row past khi
     // rereads row khi - 1 (finite data, weight 0)
-    unsigned ld_off[LOADS];
+    // A chunk inside the range is addressed from its first key row with fixed
+    // lane offsets (row times token stride plus the chunk; the host keeps a
+    // chunk's rows within 2^31 bytes), one scalar multiply per chunk; the last
+    // chunk of a range clamps row by row.
+    unsigned ld_off[LOADS], ld_koff[LOADS], ld_voff[LOADS];
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) ld_off[it] = 16u * ((lane - rot_of(LOADS * wave + it)) & (CHUNKS - 1));
-    auto issue = [&](const uint16_t *base, int64_t st, int k0, unsigned char *slot) __attribute__((always_inline)) {
+    for (int it = 0; it < LOADS; ++it) {
+        const int r = LOADS * wave + it;
+        ld_off[it] = 16u * ((lane - rot_of(r)) & (CHUNKS - 1));
+        ld_koff[it] = (unsigned)(r * p.k_st * 2) + ld_off[it];
+        ld_voff[it] = (unsigned)(r * p.v_st * 2) + ld_off[it];
+    }
+    auto issue = [&](const uint16_t *base, int64_t st, const unsigned (&full_off)[LOADS], int k0,
+                     unsigned char *slot) __attribute__((always_inline)) {
+        if (k0 + KC <= khi) {  // workgroup-uniform
+            const uint16_t *cb = base + key_offset(k0, st);
 #pragma unroll
-        for (int it = 0; it < LOADS; ++it) {
-            const int r = LOADS * wave + it;
-            load_lds_buf(base + key_offset(min(k0 + r, khi - 1), st), ld_off[it], slot + r * ROW_BYTES);
+            for (int it = 0; it < LOADS; ++it)
+                load_lds_buf(cb, full_off[it], slot + (LOADS * wave + it) * ROW_BYTES);
+        } else {
+#pragma unroll
+            for (int it = 0; it < LOADS; ++it) {
+                const int r = LOADS * wave + it;
+                load_lds_buf(base + key_offset(min(k0 + r, khi - 1), st), ld_off[it], slot + r * ROW_BYTES);
+            }
         }
     };
 
@@ -278,9 +295,9 @@ __global__ __launch_bounds__(512, 2) void rows_split_kernel(const FwdParams p) {
     const int nchunks = khi > klo ? (khi - klo + KC - 1) / KC : 0;  // workgroup-uniform
     f32x4 own[KB];
     if (nchunks > 0) {
-        issue(kbase, p.k_st, klo, sK0);
-        issue(vbase, p.v_st, klo, sV0);
-        if (nchunks > 1) issue(kbase, p.k_st, klo + KC, sK1);
+        issue(kbase, p.k_st, ld_koff, klo, sK0);
+        issue(vbase, p.v_st, ld_voff, klo, sV0);
+        if (nchunks > 1) issue(kbase, p.k_st, ld_koff, klo + KC, sK1);
         __builtin_amdgcn_sched_barrier(0);  // every prologue load issued before Q is used
         if (nchunks > 1) {
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS));
@@ -307,8 +324,8 @@ __global__ __launch_bounds__(512, 2) void rows_split_kernel(const FwdParams p) {
         const int k0 = klo + n * KC;
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         lds_barrier();
-        if (n + 2 < nchunks) issue(kbase, p.k_st, k0 + 2 * KC, sKfill);
-        if (n + 1 < nchunks) issue(vbase, p.v_st, k0 + KC, sVfill);
+        if (n + 2 < nchunks) issue(kbase, p.k_st, ld_koff, k0 + 2 * KC, sKfill);
+        if (n + 1 < nchunks) issue(vbase, p.v_st, ld_voff, k0 + KC, sVfill);
         f32x4 sc[KB];
         combine(n & 1, own, sc);
         prep(k0, sc);

@@ -212,8 +212,9 @@ def test_plan_names_the_kernel_of_each_workload(lib, args, kw, kernel):
     # load (1024 / (2 hd) of them) by 32-bit offsets from the first
     (128, 128, 1), (128, (1 << 31) // 6 - 128, 1), (128, (1 << 31) // 6, 0),
     (64, (1 << 31) // 14 - 64, 1), (64, (1 << 31) // 14, 0),
-    # at hd 512 a load is one row: any token stride below 2^32 elements
-    (512, (1 << 32) - 512, 1),
+    # at hd 512 (the head-split kernel) a whole 32-key chunk is addressed
+    # from its first row: 31 strides plus a row below 2^31 bytes
+    (512, ((1 << 31) - 1024) // 62, 1), (512, ((1 << 31) - 1024) // 62 + 1, 0),
 ])
 def test_plan_row_parallel_token_stride_limit(lib, hd, token_stride, row_parallel):
     got = fa.fmha_attention_plan(4, 32, 32, 128, 512, hd, causal=True, kv_token_stride=token_stride)
