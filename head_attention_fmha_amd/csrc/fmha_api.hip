@@ -149,7 +149,7 @@ bool stream_offsets_fit(const FwdParams &p, int hd) {
     return rows * slots * hd * 4 < (int64_t(1) << 31);
 }
 
-// The stream kernel loads K/V by buffer loads from each wave's first key
+// The stream and pass kernels load K/V by buffer loads from each wave's first key
 // row with 32-bit lane offsets: a wave's rows (at most 64) must lie within
 // 2^31 bytes.
 bool stream_loads_fit(const FwdParams &p) {
@@ -170,6 +170,7 @@ enum Variant : int {
     kStreamWide2,   // stream_kernel<128, true, 8, 2>: one pass of up to 512 keys, eight waves
     kStreamWide2Shared,
     kPass,          // pass_kernel<HD>: one pass over <= 128 keys, every load up front (hd >= 256)
+    kPassLoop,      // pass_loop_kernel<HD>: 128-key passes, few-unit grids (hd >= 256)
     kAttnOneStream, // attn_kernel, one slice, streamed
     kAttnOne,       // attn_kernel, one slice, K/V shared with other row blocks
     kAttnTwoTiles,  // attn_kernel, several slices, two tiles per workgroup
@@ -225,9 +226,13 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
             pl.tiles_per_group = (hd <= 128 && groups2 >= 2 * kComputeUnits) ? 8 : 4;
         }
     }
-    // hd 256 / 512 with every tile's keys within one 128-key pass (and not the
-    // row-parallel kernel's many-row work): the one-pass kernel, eight waves
-    const bool pass = !pl.row_parallel && hd >= 256 && span <= 128;
+    // hd 256 / 512, not the row-parallel kernel's many-row work: the pass
+    // kernel (eight waves, 128-key passes) when every tile's keys fit one pass
+    // or the grid holds at most one tile per compute unit (each workgroup then
+    // takes in its whole range: whole-row loads, one pass's loads in flight
+    // behind the other's math)
+    const bool pass = !pl.row_parallel && hd >= 256 && (span <= 128 || units1 <= kComputeUnits) &&
+                      stream_loads_fit(p);
     // hd 128, up to 512 keys per tile and at most one tile per compute unit:
     // each workgroup must take in its whole key range, and whole-row loads
     // (the stream kernel, eight waves of 32 or 64 keys) reach it at about
@@ -237,7 +242,7 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
     if (pass || wide) {
         pl.waves_per_group = 8;
         pl.tiles_per_group = 1;
-        pl.one_slice = 1;
+        pl.one_slice = (wide || span <= 128) ? 1 : 0;  // (the pass kernel may take several passes)
     }
     const int rows_per_group = 16 * pl.tiles_per_group;
     const int row_blocks = (p.rows + rows_per_group - 1) / rows_per_group;
@@ -258,8 +263,8 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
         snprintf(pl.kernel, sizeof pl.kernel, "rows_kernel<%d, %d, %d, %s>", hd, var == kRowsTwoTiles ? 2 : 1,
                  var == kRowsTwoTiles ? 32 : rows_chunk_keys(hd), sp);
     } else if (pass) {
-        var = kPass;
-        snprintf(pl.kernel, sizeof pl.kernel, "pass_kernel<%d, %s>", hd, sp);
+        var = span <= 128 ? kPass : kPassLoop;
+        snprintf(pl.kernel, sizeof pl.kernel, "%s<%d, %s>", var == kPass ? "pass_kernel" : "pass_loop_kernel", hd, sp);
     } else if (wide) {
         const int ks = span <= 256 ? 1 : 2;
         var = ks == 1 ? (pl.streaming ? kStreamWide : kStreamWideShared)
@@ -340,6 +345,11 @@ void launch_hd(const FwdParams &p, int var, hipStream_t s) {
             if constexpr (HD >= 256)
                 hipLaunchKernelGGL((fmha::pass_kernel<HD, SPLIT>), dim3(p.n_units), dim3(64 * fmha::PassShape<HD>::NW),
                                    0, s, p);
+            break;
+        case kPassLoop:
+            if constexpr (HD >= 256)
+                hipLaunchKernelGGL((fmha::pass_loop_kernel<HD, SPLIT>), dim3(p.n_units),
+                                   dim3(64 * fmha::PassShape<HD>::NW), 0, s, p);
             break;
         // one-slice work at hd >= 256 runs the one-pass kernel
         case kAttnOneStream:

@@ -305,21 +305,26 @@ int fmha_lse_merge_mx(const float *o_part, const float *lse_part, void *o_codes,
  * row block and key partition) refines the per-(head, batch) grid of the
  * commit log at e4ee9fdc for this hardware.
  *
- *   waves_per_group  4 or 8: wavefronts per workgroup; 8 when fewer than
- *                    two 16-row units per compute unit exist
+ *   waves_per_group  4 or 8: wavefronts per workgroup; 8 for few-unit
+ *                    grids (fewer than two 16-row units per compute unit),
+ *                    the one-pass / pass kernels and the hd-512 row kernel
  *   tiles_per_group  16-row tiles per workgroup (1 or 2; 4 or 8 row-parallel)
  *   one_slice        1 when every workgroup's key range fits one pass
  *   streaming        1 when no two workgroups read the same K/V rows
- *   row_parallel     1 when each wave owns whole rows and the waves share
- *                    K/V chunks staged in LDS (many rows per KV head)
+ *   row_parallel     1 when each wave owns whole rows (at hd 512 half of
+ *                    each row's head dim) and the waves share K/V chunks
+ *                    staged in LDS (many rows per KV head)
  *   workgroups       grid size
  *   threads_per_group  work-items per workgroup (64 * waves_per_group)
  *   kernel           NUL-terminated name of the kernel template instance the
- *                    call launches, e.g. "stream_kernel<128, true>"
+ *                    call launches, e.g. "stream_kernel<128, true, true, 4, 1>"
  * k_st / v_st matter through their head strides (both 0 = MQA) and their
- * token strides: the row-parallel kernel stages K/V by 1 KiB buffer loads
- * with 32-bit offsets from the load's first key row, so it is chosen only
- * when (1024 / (2 hd) - 1) * token stride * 2 + 2 hd < 2^31 bytes.
+ * token strides: the row-parallel kernel stages K/V by buffer loads with
+ * 32-bit offsets from a load's (hd 512: a 32-key chunk's) first key row, so
+ * it is chosen only when (1024 / (2 hd) - 1) * token stride * 2 + 2 hd
+ * (hd 512: 31 * token stride * 2 + 1024) < 2^31 bytes; the one-pass and
+ * pass kernels address a wave's rows (up to 64) the same way, and are chosen
+ * only when 63 * token stride * 2 + 256 < 2^31.
  * Errors: as fmha_forward for sizes and mask arguments (including
  * FMHA_ERR_UNSUPPORTED for a grid of 2^32 work-items or more);
  * FMHA_ERR_INVALID_ARG for a null plan or split_len < 0.

@@ -159,7 +159,8 @@ def test_merge_rejects(lib, kw, code):
 @pytest.mark.parametrize("args,kw,want", [
     # split-KV GQA decode, 64 partitions of 128 keys: one slice, streamed
     ((32, 64, 8, 1, 8192, 128), dict(split_len=128), (4, 1, 1, 1, 16384)),
-    # MQA decode (128 heads on one KV head), 512 keys: few units, eight waves
+    # MQA decode (128 heads on one KV head), 512 keys: few units, the pass
+    # kernel's eight waves over four 128-key passes
     ((8, 128, 1, 1, 512, 512), {}, (8, 1, 0, 0, 64)),
     # the same through a head stride of 0 with n_kv_h = n_h: planned as MQA
     ((8, 128, 128, 1, 512, 512), dict(mqa_stride0=True), (8, 1, 0, 0, 64)),
@@ -189,7 +190,10 @@ def test_plan_of_each_workload(lib, args, kw, want):
 
 @pytest.mark.parametrize("args,kw,kernel", [
     ((32, 64, 8, 1, 8192, 128), dict(split_len=128), "stream_kernel<128, true, true, 4, 1>"),
-    ((8, 128, 1, 1, 512, 512), {}, "attn_kernel<512, 8, 2, 4, 1, false, false, false>"),
+    ((8, 128, 1, 1, 512, 512), {}, "pass_loop_kernel<512, false>"),
+    # more 16-row units than compute units (but fewer than two per unit): the
+    # per-wave kernel with eight waves
+    ((40, 128, 1, 1, 512, 512), {}, "attn_kernel<512, 8, 2, 4, 1, false, false, false>"),
     ((8, 128, 1, 1, 512, 512), dict(split_len=128), "pass_kernel<512, true>"),
     ((2, 16, 1, 128, 4096, 512), dict(causal=True, window=128), "pass_kernel<512, false>"),
     ((4, 32, 32, 128, 512, 512), dict(causal=True), "rows_split_kernel<512, false>"),
