@@ -1,5 +1,6 @@
 // rows_kernel.hpp -- row-parallel attention for prefill-shaped work (many
-// query rows per KV head) on gfx950.
+// query rows per KV head) on gfx950, hd 64 to 256 (hd 512:
+// rows_split_kernel.hpp).
 //
 // One workgroup (4 waves) serves 64*RT consecutive stacked rows of one
 // (batch, KV head, partition): wave w owns 16-row tiles w*RT .. w*RT + RT - 1
@@ -14,12 +15,10 @@
 //     compiler's waits for LDS reads exact) into one of two K and two V
 //     slots; K runs one chunk ahead of V, so the QK product of chunk n+1 is
 //     issued together with the softmax of chunk n (independent MFMA and
-//     vector work in one basic block, which the hardware overlaps), then
+//     vector work in one basic block, which the hardware overlaps) and
 //     chunk n's PV product;
 //   * LDS key row r holds its 16-byte column chunk c at slot
-//     (c + 2*(r mod 8)) mod CHUNKS, for both K and V (at hd 512 the row is
-//     padded and shifted by 2*(r mod 8) chunks instead: the same banks, and
-//     every read address is a base plus a constant);
+//     (c + 2*(r mod 8)) mod CHUNKS, for both K and V;
 //   * S^T = K . Q^T with the K A-operand read from LDS (16 bytes per lane),
 //     O^T += V^T . P^T with V^T from the transposing LDS read
 //     ds_read_b64_tr_b16, P^T straight from the QK result registers -- the
@@ -46,28 +45,18 @@ struct RowsShape {
     static constexpr int PART_BYTES = KC * ROW_BYTES;  // K (or V) bytes of one chunk
     static constexpr int LOADS = PART_BYTES / (256 * 16);  // 16-byte loads per lane per slot
     static constexpr int ROWS = 64 * RT;           // rows per workgroup
-    // LDS key rows: up to hd 256 a row is stored in ROW_BYTES with its chunks
-    // rotated in place; at hd 512 (one 1 KiB row per wave-wide load) rows are
-    // padded to PITCH and shifted whole, which keeps the bank spread of the
-    // rotation while every LDS read of a slot is one per-lane base plus a
-    // compile-time offset (no per-step address registers)
-    static constexpr bool SHIFTED = HD >= 512;
-    static constexpr int PITCH = SHIFTED ? ROW_BYTES + 256 : ROW_BYTES;
-    static constexpr int SLOT_BYTES = KC * PITCH;
+    static constexpr int SLOT_BYTES = PART_BYTES;  // one K or V chunk in LDS
     static_assert(KC % 32 == 0 && PART_BYTES % (256 * 16) == 0, "whole wave-wide loads");
-    static_assert(!SHIFTED || ROW_BYTES == 1024, "a shifted row is one wave-wide load");
-    // four slots: 32 or 64 KiB up to hd 256 (two workgroups per CU), 160 KiB
-    // at hd 512 (one; its full-width Q and O tiles fill a SIMD's registers)
-    static_assert(4 * SLOT_BYTES <= 160 * 1024, "four slots fit the LDS");
+    // four slots: 32 or 64 KiB (two workgroups per CU)
+    static_assert(4 * SLOT_BYTES <= 80 * 1024, "four slots leave room for two workgroups per CU");
 };
 
 template <int HD, int RT, int KC, bool SPLIT>
-__global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdParams p) {
+__global__ __launch_bounds__(256, 2) void rows_kernel(const FwdParams p) {
     using S = RowsShape<HD, RT, KC>;
     constexpr int KSTEPS = S::KSTEPS, NB = S::NB, CHUNKS = S::CHUNKS, ROW_BYTES = S::ROW_BYTES;
     constexpr int KB = S::KB, KS = S::KS, SLOT_BYTES = S::SLOT_BYTES;
-    constexpr int LOADS = S::LOADS, PITCH = S::PITCH;
-    constexpr bool SHIFTED = S::SHIFTED;
+    constexpr int LOADS = S::LOADS;
     // two K and two V slots as four LDS objects, used in turn by a loop
     // unrolled by two: the compiler can then tell each prefetch from the
     // reads of the other slot and need not wait for the prefetch before them
@@ -204,22 +193,16 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
     for (int it = 0; it < LOADS; ++it) {
         const int i = wave * LOADS + it;  // wave-uniform
         ld_r0[it] = i * 1024 / ROW_BYTES;
-        if constexpr (SHIFTED) {
-            ld_row[it] = i;
-            ld_col[it] = lane;
-            ld_dst[it] = i * PITCH + rot_of(i) * 16;
-        } else {
-            const int x = (i * 64 + lane) * 16;  // LDS byte of this lane
-            ld_row[it] = x / ROW_BYTES;
-            ld_col[it] = ((x % ROW_BYTES) / 16 - rot_of(ld_row[it]) + CHUNKS) % CHUNKS;
-            ld_dst[it] = i * 1024;
-        }
+        const int x = (i * 64 + lane) * 16;  // LDS byte of this lane
+        ld_row[it] = x / ROW_BYTES;
+        ld_col[it] = ((x % ROW_BYTES) / 16 - rot_of(ld_row[it]) + CHUNKS) % CHUNKS;
+        ld_dst[it] = i * 1024;
         ld_koff[it] = (unsigned)(((int64_t)(ld_row[it] - ld_r0[it]) * p.k_st + ld_col[it] * 8) * 2);
         ld_voff[it] = (unsigned)(((int64_t)(ld_row[it] - ld_r0[it]) * p.v_st + ld_col[it] * 8) * 2);
     }
     auto issue = [&](const uint16_t *base, int64_t st, const unsigned (&off)[LOADS], int k0, unsigned char *slot)
                      __attribute__((always_inline)) {
-        if (SHIFTED || k0 + KC <= khi) {  // wave-uniform
+        if (k0 + KC <= khi) {  // wave-uniform
 #pragma unroll
             for (int it = 0; it < LOADS; ++it)
                 load_lds_buf(base + key_offset(min(k0 + ld_r0[it], khi - 1), st), off[it], slot + ld_dst[it]);
@@ -238,19 +221,13 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
     // lg addresses key 4*lg + s/4 (+16) of a 32-key slice, columns 4*(s%4)..+3
     const int tr_row0 = 4 * lg + (lr >> 2);
     const int tr_col = 4 * (lr & 3);
-    // shifted rows: this lane's LDS byte for K chunk 4s + lg of key row
-    // 16 kb + lr is k_lane + 16 kb PITCH + 64 s, for V^T columns 16 nb + tr_col
-    // of key row 32 ks + 16 half + tr_row0 it is v_lane + (32 ks + 16 half)
-    // PITCH + 32 nb (the rotation of a row depends on its index mod 8 only)
-    const int k_lane = lr * PITCH + (lg + rot_of(lr)) * 16;
-    const int v_lane = tr_row0 * PITCH + ((tr_col >> 3) + rot_of(tr_row0)) * 16 + (tr_col & 7) * 2;
     // one 32-key PV slice per chunk and at least four head-dim steps: the
     // step runs in the explicit order below (operands read ahead of their
     // MFMAs); rotated rows then need one address per head-dim step (K) and
     // per column block (V^T) -- a row's rotation depends on its index mod 8,
     // which 16-key block offsets keep
-    constexpr bool ORDERED = SHIFTED || (KS == 1 && KSTEPS >= 4 && NB >= 4);
-    constexpr int NKA = (ORDERED && !SHIFTED) ? KSTEPS : 1, NVA = (ORDERED && !SHIFTED) ? NB : 1;
+    constexpr bool ORDERED = KS == 1 && KSTEPS >= 4 && NB >= 4;
+    constexpr int NKA = ORDERED ? KSTEPS : 1, NVA = ORDERED ? NB : 1;
     int k_at[NKA], v_at[NVA];
 #pragma unroll
     for (int st = 0; st < NKA; ++st) k_at[st] = lr * ROW_BYTES + ((4 * st + lg + rot_of(lr)) % CHUNKS) * 16;
@@ -264,9 +241,8 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
     // keys; each K operand read from LDS feeds the MFMAs of all the tiles.
     // With fewer than four (tile, key-block) accumulators (one tile per wave
     // at 32-key chunks, hd 256), each is split into NP partial sums over
-    // alternate head-dim steps, added at the end in a fixed order (at hd 512
-    // the extra accumulators would not fit the registers).
-    constexpr int NP = (RT * KB >= 4 || HD >= 512) ? 1 : 4 / (RT * KB);
+    // alternate head-dim steps, added at the end in a fixed order.
+    constexpr int NP = RT * KB >= 4 ? 1 : 4 / (RT * KB);
     auto qk = [&](const unsigned char *sK, f32x4 (&sc)[RT][KB]) __attribute__((always_inline)) {
         f32x4 part[NP][RT][KB];
 #pragma unroll
@@ -283,13 +259,9 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
             bf16x8 kf[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                if constexpr (SHIFTED) {
-                    kf[kb] = *reinterpret_cast<const bf16x8 *>(sK + k_lane + 16 * kb * PITCH + 64 * s);
-                } else {
-                    const int r = 16 * kb + lr;
-                    const int slot = (4 * s + lg + rot_of(r)) % CHUNKS;
-                    kf[kb] = *reinterpret_cast<const bf16x8 *>(sK + r * ROW_BYTES + slot * 16);
-                }
+                const int r = 16 * kb + lr;
+                const int slot = (4 * s + lg + rot_of(r)) % CHUNKS;
+                kf[kb] = *reinterpret_cast<const bf16x8 *>(sK + r * ROW_BYTES + slot * 16);
             }
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -384,8 +356,7 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
                 for (int half = 0; half < 2; ++half) {
                     const int r = 32 * ks + 16 * half + tr_row0;
                     const int c = 16 * nb + tr_col;
-                    const int off = SHIFTED ? v_lane + (32 * ks + 16 * half) * PITCH + 32 * nb
-                                            : r * ROW_BYTES + (((c >> 3) + rot_of(r)) % CHUNKS) * 16 + (c & 7) * 2;
+                    const int off = r * ROW_BYTES + (((c >> 3) + rot_of(r)) % CHUNKS) * 16 + (c & 7) * 2;
                     q2[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                         (__attribute__((address_space(3))) bf16x4 *)(sV + off));
                 }
@@ -417,16 +388,14 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
         auto read_k = [&](int st, bf16x8 (&kf)[KB]) __attribute__((always_inline)) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-                kf[kb] = SHIFTED ? *reinterpret_cast<const bf16x8 *>(sK + k_lane + 16 * kb * PITCH + 64 * st)
-                                 : *reinterpret_cast<const bf16x8 *>(sK + k_at[st] + 16 * kb * ROW_BYTES);
+                kf[kb] = *reinterpret_cast<const bf16x8 *>(sK + k_at[st] + 16 * kb * ROW_BYTES);
         };
         auto read_v = [&](int nb) __attribute__((always_inline)) {
             bf16x4 q2[2];
 #pragma unroll
             for (int half = 0; half < 2; ++half)
                 q2[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (__attribute__((address_space(3))) bf16x4 *)(sV + (SHIFTED ? v_lane + 16 * half * PITCH + 32 * nb
-                                                                                : v_at[nb] + 16 * half * ROW_BYTES)));
+                    (__attribute__((address_space(3))) bf16x4 *)(sV + v_at[nb] + 16 * half * ROW_BYTES));
             return __builtin_shufflevector(q2[0], q2[1], 0, 1, 2, 3, 4, 5, 6, 7);
         };
         bf16x8 kf[R][KB];
@@ -481,75 +450,6 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // ---- hd 512 (shifted rows, one wave per SIMD): the same step with the
-    // PV product after the QK product and the weights' vector work spread
-    // over the QK steps, one element per step (interleaving the two products
-    // as above measured 1.3% slower here: the single wave's weights then sit
-    // between the reads and the first MFMAs)
-    auto fused_shifted = [&](const unsigned char *sK, f32x4 (&sn)[RT][KB], const f32x4 (&sc)[RT][KB],
-                     const unsigned char *sV) __attribute__((always_inline)) {
-        static_assert(!SHIFTED || (KS == 1 && KSTEPS >= RT * KB * 4 && KSTEPS >= 4 && NB >= 4), "one PV slice per chunk");
-        constexpr int D = 4, R = D + 1;  // read-ahead distance, ring size
-        auto read_k = [&](int st, bf16x8 (&kf)[KB]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                kf[kb] = *reinterpret_cast<const bf16x8 *>(sK + k_lane + 16 * kb * PITCH + 64 * st);
-        };
-        auto read_v = [&](int nb) __attribute__((always_inline)) {
-            bf16x4 q2[2];
-#pragma unroll
-            for (int half = 0; half < 2; ++half)
-                q2[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (__attribute__((address_space(3))) bf16x4 *)(sV + v_lane + 16 * half * PITCH + 32 * nb));
-            return __builtin_shufflevector(q2[0], q2[1], 0, 1, 2, 3, 4, 5, 6, 7);
-        };
-        bf16x8 kf[R][KB];
-        bf16x8 vt[R];
-#pragma unroll
-        for (int st = 0; st < D; ++st) read_k(st, kf[st]);
-#pragma unroll
-        for (int mt = 0; mt < RT; ++mt)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) sn[mt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        bf16x8 pt[RT];
-        float psum[RT];
-#pragma unroll
-        for (int mt = 0; mt < RT; ++mt) psum[mt] = 0.f;
-#pragma unroll
-        for (int st = 0; st < KSTEPS; ++st) {
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int mt = 0; mt < RT; ++mt) sn[mt][kb] = mfma_16x16x32(kf[st % R][kb], qf[mt][st], sn[mt][kb]);
-            if (st + D < KSTEPS)
-                read_k(st + D, kf[(st + D) % R]);
-            else
-                vt[(st + D - KSTEPS) % R] = read_v(st + D - KSTEPS);
-            // weights, one element per step: e = (mt, kb, j)
-            if (st < RT * KB * 4) {
-                const int mt = st / (KB * 4), kb = (st / 4) % KB, j = st % 4;
-                const float pj = fast_exp2(fmaf(sc[mt][kb][j], c_scale, neg_m[mt]));
-                pt[mt][kb * 4 + j] = to_bf16(pj);
-                psum[mt] += pj;
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int mt = 0; mt < RT; ++mt) {
-            l[mt] += psum[mt];
-            accq[mt] = mfma_16x16x32(ones, pt[mt], accq[mt]);
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int mt = 0; mt < RT; ++mt) acc[mt][nb] = mfma_16x16x32(vt[nb % R], pt[mt], acc[mt][nb]);
-            if (nb + D < NB) vt[(nb + D) % R] = read_v(nb + D);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
     // ---- the pipeline.  Step n starts with chunk n+1's K and chunk n's V on
     // chip and chunk n's scores in registers; it requests chunk n+2's K and
     // chunk n+1's V into the slots step n-1 finished with, then computes
@@ -586,9 +486,7 @@ __global__ __launch_bounds__(256, HD >= 512 ? 1 : 2) void rows_kernel(const FwdP
         if (n + 1 < nchunks) issue(vbase, p.v_st, ld_voff, k0 + KC, sVfill);
         prep(k0, sc);
         f32x4 sn[RT][KB];
-        if constexpr (SHIFTED) {
-            fused_shifted(sKnext, sn, sc, sVcur);
-        } else if constexpr (ORDERED) {
+        if constexpr (ORDERED) {
             fused(sKnext, sn, sc, sVcur);
         } else {
             qk(sKnext, sn);
