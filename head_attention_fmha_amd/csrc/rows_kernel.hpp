@@ -368,17 +368,25 @@ __global__ __launch_bounds__(256, 2) void rows_kernel(const FwdParams p) {
     };
 
     // ---- one 32-key PV slice per chunk (hd 128 and 256 at 32-key chunks):
-    // the straight-line part of a step -- chunk n's weights, then
-    // chunk n+1's QK product interleaved with chunk n's PV product -- in an
-    // explicit order.  The QK product has only RT KB accumulators (2 or 4),
-    // each a chain over the head-dim steps, and a 16x16x32 MFMA that depends
-    // on the one just issued waits for it: each QK step is therefore followed
-    // by the PV MFMAs of NB / KSTEPS column blocks (RT NB independent
-    // accumulators), so the MFMA pipe always has independent work.  One or
-    // two waves per SIMD leave little to cover LDS latency, so each K operand
-    // is read D head-dim steps and each V^T operand DV steps before its
-    // MFMAs; the scheduling barriers keep the compiler from regrouping (it
-    // would issue every read just before its use and wait for it there).
+    // the straight-line part of a step in an explicit order; the scheduling
+    // barriers keep the compiler from regrouping (it would issue every LDS
+    // read just before its use and wait for it there, and put every
+    // exponential ahead of the first MFMA).
+    //  * hd 128 (four head-dim steps, two tiles per wave on the long
+    //    prefill): every K operand of chunk n+1 is read up front; chunk n's
+    //    weights are computed one (or a few) per QK MFMA of chunk n+1, so
+    //    the quarter-rate exponentials issue beside the MFMA pipe instead of
+    //    ahead of it; chunk n's V^T operands are read during the QK product
+    //    and its PV product follows (measured: long causal GQA prefill
+    //    1.5-2% faster than weights-then-MFMAs).
+    //  * hd 256: chunk n's weights, then chunk n+1's QK product interleaved
+    //    with chunk n's PV product.  The QK product has only RT KB
+    //    accumulators (2), each a chain over the head-dim steps, and a
+    //    16x16x32 MFMA that depends on the one just issued waits for it: each
+    //    QK step is therefore followed by the PV MFMAs of NB / KSTEPS column
+    //    blocks, so the MFMA pipe always has independent work.  Each K
+    //    operand is read D head-dim steps and each V^T operand DV steps
+    //    before its MFMAs (all of them up front would not fit the registers).
     auto fused = [&](const unsigned char *sK, f32x4 (&sn)[RT][KB], const f32x4 (&sc)[RT][KB],
                      const unsigned char *sV) __attribute__((always_inline)) {
         static_assert(!ORDERED || (KS == 1 && KSTEPS >= 4 && NB % KSTEPS == 0), "one PV slice per chunk");
@@ -398,56 +406,118 @@ __global__ __launch_bounds__(256, 2) void rows_kernel(const FwdParams p) {
                     (__attribute__((address_space(3))) bf16x4 *)(sV + v_at[nb] + 16 * half * ROW_BYTES));
             return __builtin_shufflevector(q2[0], q2[1], 0, 1, 2, 3, 4, 5, 6, 7);
         };
-        bf16x8 kf[R][KB];
-        bf16x8 vt[RV][BPS];
+        if constexpr (KSTEPS == 4) {
+            constexpr int NQ = KSTEPS * KB * RT;  // QK MFMAs of the step
+            constexpr int NE = RT * KB * 4;       // weights of the step, per lane
+            static_assert(NE % KSTEPS == 0, "weight sums spread evenly over the PV groups");
+            bf16x8 kf[KSTEPS][KB];
+            bf16x8 vt[NB];
 #pragma unroll
-        for (int st = 0; st < D; ++st) read_k(st, kf[st]);
+            for (int st = 0; st < KSTEPS; ++st) read_k(st, kf[st]);
+            float pf[RT][KB * 4];  // chunk n's weights (fp32)
+            bf16x8 pt[RT];         // and their bf16 forms, the PV B operand
+            float psum[RT];
 #pragma unroll
-        for (int sv = 0; sv < DV; ++sv)
+            for (int mt = 0; mt < RT; ++mt) {
+                psum[mt] = 0.f;
 #pragma unroll
-            for (int u = 0; u < BPS; ++u) vt[sv][u] = read_v(sv * BPS + u);
-        // chunk n's weights 2^(s c - m), their bf16 forms and sums
-        bf16x8 pt[RT];
+                for (int kb = 0; kb < KB; ++kb) sn[mt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            // QK MFMA qi of chunk n+1, then weights qi NE/NQ .. (qi+1) NE/NQ - 1
+            // of chunk n (weight e: tile e / 4KB, block (e / 4) % KB, element e % 4)
 #pragma unroll
-        for (int mt = 0; mt < RT; ++mt) {
-            float psum = 0.f;
+            for (int st = 0; st < KSTEPS; ++st) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float pj = fast_exp2(fmaf(sc[mt][kb][j], c_scale, neg_m[mt]));
-                    pt[mt][kb * 4 + j] = to_bf16(pj);
-                    psum += pj;
+                    for (int mt = 0; mt < RT; ++mt) {
+                        const int qi = (st * KB + kb) * RT + mt;
+                        __builtin_amdgcn_sched_barrier(0);
+                        sn[mt][kb] = mfma_16x16x32(kf[st][kb], qf[mt][st], sn[mt][kb]);
+#pragma unroll
+                        for (int e = qi * NE / NQ; e < (qi + 1) * NE / NQ; ++e) {
+                            const int et = e / (KB * 4), ek = (e / 4) % KB, ej = e % 4;
+                            pf[et][ek * 4 + ej] = fast_exp2(fmaf(sc[et][ek][ej], c_scale, neg_m[et]));
+                            pt[et][ek * 4 + ej] = to_bf16(pf[et][ek * 4 + ej]);
+                        }
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < BPS; ++u) vt[st * BPS + u] = read_v(st * BPS + u);
+            }
+            // chunk n's PV product (and the bf16 weight sum), the fp32 weight
+            // sums in between, in the same order as a plain loop over e
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < BPS; ++u)
+#pragma unroll
+                    for (int mt = 0; mt < RT; ++mt)
+                        acc[mt][st * BPS + u] = mfma_16x16x32(vt[st * BPS + u], pt[mt], acc[mt][st * BPS + u]);
+                if (st == 0) {
+#pragma unroll
+                    for (int mt = 0; mt < RT; ++mt) accq[mt] = mfma_16x16x32(ones, pt[mt], accq[mt]);
                 }
-            l[mt] += psum;
-        }
 #pragma unroll
-        for (int mt = 0; mt < RT; ++mt)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) sn[mt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < KSTEPS; ++st) {
+                for (int e = st * NE / KSTEPS; e < (st + 1) * NE / KSTEPS; ++e)
+                    psum[e / (KB * 4)] += pf[e / (KB * 4)][e % (KB * 4)];
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+            for (int mt = 0; mt < RT; ++mt) l[mt] += psum[mt];
+        } else {
+            bf16x8 kf[R][KB];
+            bf16x8 vt[RV][BPS];
 #pragma unroll
-                for (int mt = 0; mt < RT; ++mt) sn[mt][kb] = mfma_16x16x32(kf[st % R][kb], qf[mt][st], sn[mt][kb]);
+            for (int st = 0; st < D; ++st) read_k(st, kf[st]);
 #pragma unroll
-            for (int u = 0; u < BPS; ++u)
+            for (int sv = 0; sv < DV; ++sv)
 #pragma unroll
-                for (int mt = 0; mt < RT; ++mt)
-                    acc[mt][st * BPS + u] = mfma_16x16x32(vt[st % RV][u], pt[mt], acc[mt][st * BPS + u]);
-            if (st == 0) {
+                for (int u = 0; u < BPS; ++u) vt[sv][u] = read_v(sv * BPS + u);
+            // chunk n's weights 2^(s c - m), their bf16 forms and sums
+            bf16x8 pt[RT];
 #pragma unroll
-                for (int mt = 0; mt < RT; ++mt) accq[mt] = mfma_16x16x32(ones, pt[mt], accq[mt]);
+            for (int mt = 0; mt < RT; ++mt) {
+                float psum = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float pj = fast_exp2(fmaf(sc[mt][kb][j], c_scale, neg_m[mt]));
+                        pt[mt][kb * 4 + j] = to_bf16(pj);
+                        psum += pj;
+                    }
+                l[mt] += psum;
             }
-            if (st + D < KSTEPS) read_k(st + D, kf[(st + D) % R]);
-            if (st + DV < KSTEPS) {
 #pragma unroll
-                for (int u = 0; u < BPS; ++u) vt[(st + DV) % RV][u] = read_v((st + DV) * BPS + u);
+            for (int mt = 0; mt < RT; ++mt)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) sn[mt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int mt = 0; mt < RT; ++mt) sn[mt][kb] = mfma_16x16x32(kf[st % R][kb], qf[mt][st], sn[mt][kb]);
+#pragma unroll
+                for (int u = 0; u < BPS; ++u)
+#pragma unroll
+                    for (int mt = 0; mt < RT; ++mt)
+                        acc[mt][st * BPS + u] = mfma_16x16x32(vt[st % RV][u], pt[mt], acc[mt][st * BPS + u]);
+                if (st == 0) {
+#pragma unroll
+                    for (int mt = 0; mt < RT; ++mt) accq[mt] = mfma_16x16x32(ones, pt[mt], accq[mt]);
+                }
+                if (st + D < KSTEPS) read_k(st + D, kf[(st + D) % R]);
+                if (st + DV < KSTEPS) {
+#pragma unroll
+                    for (int u = 0; u < BPS; ++u) vt[(st + DV) % RV][u] = read_v((st + DV) * BPS + u);
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
     };
 
     // ---- the pipeline.  Step n starts with chunk n+1's K and chunk n's V on
