@@ -414,6 +414,10 @@ __global__ __launch_bounds__(256, 2) void rows_kernel(const FwdParams p) {
             bf16x8 vt[NB];
 #pragma unroll
             for (int st = 0; st < KSTEPS; ++st) read_k(st, kf[st]);
+            // raised wave priority over the step's MFMA work: of the two waves
+            // on a SIMD (two workgroups per CU), the one with MFMAs to issue
+            // is picked first (long causal GQA prefill 2-3% faster)
+            __builtin_amdgcn_s_setprio(1);
             float pf[RT][KB * 4];  // chunk n's weights (fp32)
             bf16x8 pt[RT];         // and their bf16 forms, the PV B operand
             float psum[RT];
@@ -466,6 +470,7 @@ __global__ __launch_bounds__(256, 2) void rows_kernel(const FwdParams p) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int mt = 0; mt < RT; ++mt) l[mt] += psum[mt];
+            __builtin_amdgcn_s_setprio(0);
         } else {
             bf16x8 kf[R][KB];
             bf16x8 vt[RV][BPS];
@@ -475,6 +480,7 @@ __global__ __launch_bounds__(256, 2) void rows_kernel(const FwdParams p) {
             for (int sv = 0; sv < DV; ++sv)
 #pragma unroll
                 for (int u = 0; u < BPS; ++u) vt[sv][u] = read_v(sv * BPS + u);
+            __builtin_amdgcn_s_setprio(1);  // as above
             // chunk n's weights 2^(s c - m), their bf16 forms and sums
             bf16x8 pt[RT];
 #pragma unroll
@@ -517,6 +523,7 @@ __global__ __launch_bounds__(256, 2) void rows_kernel(const FwdParams p) {
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
         }
     };
 

@@ -255,6 +255,8 @@ __global__ __launch_bounds__(512, 2) void rows_split_kernel(const FwdParams p) {
         for (int sv = 0; sv < DV; ++sv)
 #pragma unroll
             for (int u = 0; u < BPS; ++u) vt[sv][u] = read_v(sV, sv * BPS + u);
+        // raised wave priority over the step's MFMA work (as rows_kernel.hpp)
+        __builtin_amdgcn_s_setprio(1);
         bf16x8 pt;
         float psum = 0.f;
 #pragma unroll
@@ -283,6 +285,7 @@ __global__ __launch_bounds__(512, 2) void rows_split_kernel(const FwdParams p) {
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // ---- the pipeline (rows_kernel.hpp): step n starts with chunk n+1's K
