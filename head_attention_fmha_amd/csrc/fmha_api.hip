@@ -212,8 +212,16 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
     // tile per wave while that is needed to give every compute unit a
     // workgroup (short prefill); two -- every K operand read from LDS then
     // feeds two MFMAs -- once the grid has two workgroups per compute unit
-    // even so (long prefill)
-    if (!pl.one_slice && p.rows >= 64 && rows_loads_fit(p, hd)) {
+    // even so (long prefill).  At hd <= 128 also when one slice covers every
+    // tile's keys: a 64-row workgroup then reads each K/V byte once where four
+    // one-slice workgroups each read it (causal MHA prefill T 128 over 128
+    // keys: hd 64 8.2 -> 6.5 us, hd 128 11.1 -> 9.4 us; over 64 keys, no
+    // mask, hd 64: 6.2 -> 5.6 us) -- but not under a window, where the 64
+    // rows of a workgroup see many more keys than the 16 of a tile (window 32
+    // over 512 keys: 8.3 -> 9.8 us), nor over 32 keys or fewer, half a chunk
+    // (hd 128: 7.1 -> 7.6 us)
+    const bool rows_one_slice = hd <= 128 && p.window == 0 && span > 32;
+    if ((!pl.one_slice || rows_one_slice) && p.rows >= 64 && rows_loads_fit(p, hd)) {
         const int64_t per_kv = (int64_t)p.n_split * p.n_kv_h * p.batch;
         const int64_t groups1 = (int64_t)((p.rows + 63) / 64) * per_kv;
         const int64_t groups2 = (int64_t)((p.rows + 127) / 128) * per_kv;
