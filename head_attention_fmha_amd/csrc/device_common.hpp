@@ -20,6 +20,7 @@ namespace fmha {
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef unsigned u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned))));
+typedef unsigned u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned))));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -129,6 +130,14 @@ __device__ __forceinline__ u32x4 load16_buf(const void *base, unsigned voffset) 
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, -1, 0x00020000);
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, 0, NT ? 2 : 0));
+}
+
+// 8 bytes per lane into registers by a buffer load, as load16_buf.
+template <bool NT = false>
+__device__ __forceinline__ u32x2 load8_buf(const void *base, unsigned voffset) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, -1, 0x00020000);
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsrc, voffset, 0, NT ? 2 : 0));
 }
 
 // 16 bytes per lane stored by a buffer store with the device-scope cache

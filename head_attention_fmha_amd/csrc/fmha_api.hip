@@ -165,9 +165,9 @@ enum Variant : int {
     kAttnEight,     // attn_kernel, eight waves, several slices (hd >= 256)
     kStream,        // stream_kernel<128, STREAM = true, 4, 1>: one pass, non-temporal whole-line K/V loads
     kStreamShared,  // stream_kernel<128, STREAM = false, 4, 1>: one pass, row blocks sharing K/V through L2
-    kStreamWide,    // stream_kernel<128, true, 8, 1>: one pass of up to 256 keys, eight waves
+    kStreamWide,    // stream_kernel<HD <= 128, true, 8, 1>: one pass of up to 256 keys, eight waves
     kStreamWideShared,
-    kStreamWide2,   // stream_kernel<128, true, 8, 2>: one pass of up to 512 keys, eight waves
+    kStreamWide2,   // stream_kernel<HD <= 128, true, 8, 2>: one pass of up to 512 keys, eight waves
     kStreamWide2Shared,
     kPass,          // pass_kernel<HD>: one pass over <= 128 keys, every load up front (hd >= 256)
     kPassLoop,      // pass_loop_kernel<HD>: 128-key passes, few-unit grids (hd >= 256)
@@ -241,11 +241,14 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
     // behind the other's math)
     const bool pass = !pl.row_parallel && hd >= 256 && (span <= 128 || units1 <= kComputeUnits) &&
                       stream_loads_fit(p);
-    // hd 128, up to 512 keys per tile and at most one tile per compute unit:
+    // hd 64 / 128, up to 512 keys per tile and at most one tile per compute unit:
     // each workgroup must take in its whole key range, and whole-row loads
     // (the stream kernel, eight waves of 32 or 64 keys) reach it at about
-    // three times the rate of loads in the MFMA operand shape
-    const bool wide = !pl.row_parallel && hd == 128 && !pl.one_slice && span <= 512 && units1 <= kComputeUnits &&
+    // three times the rate of loads in the MFMA operand shape (MQA decode hd
+    // 64 over 512 keys: 6.4 -> 5.7 us against the per-wave kernel; one-slice
+    // work at hd 64 measured the same on either and stays on the per-wave
+    // kernel)
+    const bool wide = !pl.row_parallel && hd <= 128 && !pl.one_slice && span <= 512 && units1 <= kComputeUnits &&
                       stream_loads_fit(p) && (!split || stream_offsets_fit(p, hd));
     if (pass || wide) {
         pl.waves_per_group = 8;
@@ -334,19 +337,19 @@ void launch_hd(const FwdParams &p, int var, hipStream_t s) {
                 hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, false, 4, 1>), dim3(p.n_units), dim3(256), 0, s, p);
             break;
         case kStreamWide:
-            if constexpr (HD == 128)
+            if constexpr (HD <= 128)
                 hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, true, 8, 1>), dim3(p.n_units), dim3(512), 0, s, p);
             break;
         case kStreamWideShared:
-            if constexpr (HD == 128)
+            if constexpr (HD <= 128)
                 hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, false, 8, 1>), dim3(p.n_units), dim3(512), 0, s, p);
             break;
         case kStreamWide2:
-            if constexpr (HD == 128)
+            if constexpr (HD <= 128)
                 hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, true, 8, 2>), dim3(p.n_units), dim3(512), 0, s, p);
             break;
         case kStreamWide2Shared:
-            if constexpr (HD == 128)
+            if constexpr (HD <= 128)
                 hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, false, 8, 2>), dim3(p.n_units), dim3(512), 0, s, p);
             break;
         case kPass:

@@ -1,9 +1,10 @@
-// stream_kernel.hpp -- one-pass attention at hd 128 on gfx950: every
-// workgroup's keys fit one pass of NW waves x 32 KS keys (four waves x 32:
-// the split-KV decode with 128-key partitions, caches of at most 128 keys;
-// eight waves x 32 or 64: ranges of up to 256 or 512 keys on grids of at
-// most one workgroup per compute unit, such as the MQA decode of 128 query
-// heads over one KV head, where a workgroup must take in its whole range).
+// stream_kernel.hpp -- one-pass attention at hd 128 (and 64) on gfx950:
+// every workgroup's keys fit one pass of NW waves x 32 KS keys (four waves x
+// 32: the split-KV decode with 128-key partitions, caches of at most 128
+// keys; eight waves x 32 or 64: ranges of up to 256 or 512 keys on grids of
+// at most one workgroup per compute unit, such as the MQA decode of 128 query
+// heads over one KV head, where a workgroup must take in its whole range --
+// the only use at hd 64).
 //
 // Such work is bound by HBM bandwidth alone, and this GPU streams reads at
 // its best only with the non-temporal hint on loads that fetch whole cache
@@ -19,23 +20,27 @@
 //     operands of eight MFMAs, MFMA j covering head-dim columns 8m + j
 //     (m = 0..15).  Each output column is still one contiguous dot product
 //     over the keys, just on a different MFMA row than in attn_kernel.
+//     At hd 64 a lane loads 8 bytes (columns 4m .. 4m+3, still sixteen lanes
+//     to a row) and four MFMAs cover columns 4m + j; K rows are 128 bytes,
+//     eight to a load.
 //
 // Products as in attn_kernel.hpp (v_mfma_f32_16x16x32_bf16, keys in the M
 // dimension, lane l = lr + 16*lg):
 //   S^T (keys x rows) = K . Q^T   QK block b, M row lr <-> key 8(lr/4) + 4b + lr%4
-//   O^T (hd x rows)  += V^T . P^T  MFMA j, M row m <-> column 8m + j
+//   O^T (hd x rows)  += V^T . P^T  MFMA j, M row m <-> column (hd/16) m + j
 // The key order of the QK blocks puts keys 8lg .. 8lg+7 (in order) in the
 // result registers of lane (lr, lg) -- the PV B operand for row lr as it
 // stands, and the key order of the V registers.  The PV result leaves lane
-// (lr, lg) holding row lr's columns 32lg .. 32lg+31.
+// (lr, lg) holding row lr's columns (hd/4) lg .. (hd/4) lg + hd/4 - 1.
 //
 // Softmax: each wave takes 32 KS consecutive keys of the pass and computes
 // its own (max, sum, output) in one step -- the multi-tile kernel's running
 // max / running sum of the e4ee9fdc commit log of the pages with one slice
 // per wave -- and the NW waves are combined once, in a fixed order, through
 // LDS, each wave combining and storing one quarter of the columns of eight
-// or sixteen rows (whole 128-byte lines of fp32 partials per store
-// instruction, with the device-scope cache policy).  Scores are base 2 (x = q.k * scale * log2 e); O is
+// or sixteen rows at hd 128, four whole rows at hd 64 (whole 128-byte lines
+// of fp32 partials per store instruction, with the device-scope cache
+// policy).  Scores are base 2 (x = q.k * scale * log2 e); O is
 // normalised by the sum of the bf16-rounded weights the PV product consumes
 // and lse uses the fp32 sum, as in attn_kernel.hpp.
 #pragma once
@@ -54,14 +59,17 @@ namespace fmha {
 // wave (V takes 32 registers), two for 64.
 template <int HD, bool SPLIT, bool STREAM, int NW, int KS>
 __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const FwdParams p) {
-    static_assert(HD == 128, "the stream kernel serves hd 128: one 16-lane run covers a key row");
+    static_assert(HD == 64 || HD == 128, "the stream kernel serves hd 64 and 128: one 16-lane run covers a key row");
     static_assert((NW == 4 && KS == 1) || (NW == 8 && (KS == 1 || KS == 2)), "4 x 32, 8 x 32 or 8 x 64 keys");
+    constexpr bool H64 = HD == 64;
     constexpr int KSTEPS = HD / 32;     // QK MFMA steps over the head dim
     constexpr int CHUNKS = HD / 8;      // 16-byte chunks per key row
     constexpr int ROW_BYTES = HD * 2;
+    constexpr int RPL = 1024 / ROW_BYTES;                // key rows per wave-wide K load
+    constexpr int NB = HD / 16;                          // PV MFMAs per 32 keys (16 output columns each)
     constexpr int WAVE_KEYS = 32 * KS;
-    constexpr int K_BYTES = NW * WAVE_KEYS * ROW_BYTES;  // every wave's K slice (32, 64 or 128 KiB)
-    constexpr int REC = 36;                              // merge record per lane: 32 outputs, m, l, lq, pad
+    constexpr int K_BYTES = NW * WAVE_KEYS * ROW_BYTES;  // every wave's K slice (16 to 128 KiB)
+    constexpr int REC = HD / 4 + 4;                      // merge record per lane: HD/4 outputs, m, l, lq, pad
     constexpr int M_BYTES = NW * 64 * REC * 4;           // every wave's records (36 or 72 KiB)
     // the K slices, then (after every wave's QK) the merge records
     __shared__ __attribute__((aligned(16))) unsigned char smem[M_BYTES > K_BYTES ? M_BYTES : K_BYTES];
@@ -113,14 +121,20 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
     const int k0 = klo + WAVE_KEYS * wave;  // this wave's first key
     const bool active = k0 < khi;            // wave-uniform
 
-    // rotation of LDS key row r: chunk c lives in slot (c + rot(r)) % 16, so
-    // the 16 rows one QK read touches (keys 32ks + 8(i/4) + 4b + i%4) use 16
-    // different slots -- all the banks
-    auto rot_of = [](int r) __attribute__((always_inline)) { return (r + 4 * (r >> 4)) & (CHUNKS - 1); };
+    // rotation of LDS key row r: chunk c lives in slot (c + rot(r)) % CHUNKS,
+    // so the 16 rows one QK read touches (keys 32ks + 8(i/4) + 4b + i%4) use
+    // 16 different 16-byte bank groups -- all the banks (hd 64: two 128-byte
+    // rows per group of banks, the rotation found by exhaustive search)
+    auto rot_of = [](int r) __attribute__((always_inline)) {
+        return H64 ? ((r >> 1) ^ (r >> 3)) & (CHUNKS - 1) : (r + 4 * (r >> 4)) & (CHUNKS - 1);
+    };
     unsigned char *sKw = smem + wave * WAVE_KEYS * ROW_BYTES;
 
     u32x4 qraw[KSTEPS];  // Q^T B operand: Q[row lr][32s + 8lg .. +7]
-    u32x4 vr[KS][8];    // V[key k0 + 32ks + 8lg + i][8lr .. 8lr + 7]
+    // V[key k0 + 32ks + 8lg + i][NB lr .. NB lr + NB - 1]: 16 bytes per lane
+    // at hd 128, 8 at hd 64 -- sixteen lanes cover a key row either way
+    using VRow = typename std::conditional<H64, u32x2, u32x4>::type;
+    VRow vr[KS][8];
     if (active) {
         const uint16_t *qp = p.q + (int64_t)b * p.q_sb + (int64_t)t_row * p.q_st + (int64_t)h_row * p.q_sh + 8 * lg;
         // rows past the end read row 0 of the group (valid memory); they are
@@ -137,12 +151,13 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
         const uint16_t *kw = p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh + key_offset(k0, p.k_st);
         const uint16_t *vw = p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh + key_offset(k0, p.v_st);
         const unsigned kstride = (unsigned)p.k_st * 2u, vstride = (unsigned)p.v_st * 2u;
-        // K: 8 KS wave-wide loads of four whole key rows each, into the
-        // wave's LDS slice (lane L lands at byte 16 L of the load's 1 KiB)
+        // K: wave-wide loads of RPL whole key rows each (4 at hd 128, 8 at
+        // hd 64), into the wave's LDS slice (lane L lands at byte 16 L of the
+        // load's 1 KiB)
 #pragma unroll
-        for (int it = 0; it < WAVE_KEYS / 4; ++it) {
-            const int r = 4 * it + (lane >> 4);
-            const int chunk = (lr - rot_of(r)) & (CHUNKS - 1);
+        for (int it = 0; it < WAVE_KEYS / RPL; ++it) {
+            const int r = RPL * it + lane / CHUNKS;
+            const int chunk = (lane % CHUNKS - rot_of(r)) & (CHUNKS - 1);
             load_lds_buf<STREAM>(kw, (unsigned)min(r, last) * kstride + 16u * chunk, sKw + it * 1024);
         }
         __builtin_amdgcn_sched_barrier(0);  // Q, then K, then V: the waits below count on that order
@@ -150,15 +165,18 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                vr[ks][i] = load16_buf<STREAM>(vw, (unsigned)min(32 * ks + 8 * lg + i, last) * vstride + 16u * lr);
+            for (int i = 0; i < 8; ++i) {
+                const unsigned off = (unsigned)min(32 * ks + 8 * lg + i, last) * vstride + 2u * NB * lr;
+                if constexpr (H64) vr[ks][i] = load8_buf<STREAM>(vw, off);
+                else vr[ks][i] = load16_buf<STREAM>(vw, off);
+            }
         __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
     }
 
     float m = -INFINITY, l = 0.f, lq = 0.f;
-    f32x4 acc[8];
+    f32x4 acc[NB];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (active) {
         // Q and K have landed (V's 8 KS loads, issued last, may still fly)
@@ -221,13 +239,13 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
             }
         l = psum;
         lq = qsum;
-        // V^T operands: element i of MFMA j's operand is V[key 32ks + 8lg + i][8lr + j];
+        // V^T operands: element i of MFMA j's operand is V[key 32ks + 8lg + i][NB lr + j];
         // dword u pairs keys 2u, 2u+1 -- the low (j even) or high (j odd)
         // halves of dword j/2 of registers 2u and 2u+1 (v_perm_b32)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < NB; ++j) {
                 const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
                 u32x4 a;
 #pragma unroll
@@ -254,17 +272,22 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
     // read of four columns or of (m, l, lq) is one 16-byte read, and the 8
     // lanes of a row read 128 contiguous bytes (a slot-major layout put all
     // of a record in one bank: 8-way conflicts)
-    const int q = lane & 7;
-    const int cb = wave & 3;             // column quarter
-    const int c = 32 * cb + 4 * q;       // this lane's first column
-    constexpr int HALVES = NW == 4 ? 2 : 1;
+    // At hd 64 a row's 64 columns are 256 bytes of fp32 partials: wave w < 4
+    // merges rows 4w .. 4w + 3, all columns, lane (rr, q) = (lane / 16, lane %
+    // 16) taking columns 4q .. 4q + 3 of row 4w + rr (the other four waves of
+    // an eight-wave workgroup have no part in it).
+    const int q = H64 ? lane & 15 : lane & 7;
+    const int cb = wave & 3;                      // column quarter (hd 128)
+    const int c = H64 ? 4 * q : 32 * cb + 4 * q;  // this lane's first column
+    constexpr int HALVES = (NW == 4 && !H64) ? 2 : 1;
+    const bool merges = !H64 || wave < 4;         // wave-uniform
     // output addressing of this lane's rows, fixed before the barriers
     int rows_rr[HALVES];
     int64_t o_off[HALVES], l_off[HALVES];
 #pragma unroll
     for (int hh = 0; hh < HALVES; ++hh) {
         const int half = NW == 4 ? hh : (wave >> 2);
-        const int rr = (lane >> 3) + 8 * half;
+        const int rr = H64 ? 4 * cb + (lane >> 4) : (lane >> 3) + 8 * half;
         rows_rr[hh] = rr;
         const int rw = row0 + rr;
         const int rwc = rw < p.rows ? rw : row0;
@@ -283,24 +306,29 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
     float *red = reinterpret_cast<float *>(smem);
     {
         float *mine = red + (wave * 64 + lane) * REC;
+        // lane (lr, lg) holds columns NB (4 lg + t) + j of row lr (MFMA j,
+        // element t): HD/4 consecutive columns, stored in order
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                *reinterpret_cast<f32x4 *>(mine + 8 * t + 4 * h) =
+            for (int h = 0; h < NB / 4; ++h)
+                *reinterpret_cast<f32x4 *>(mine + NB * t + 4 * h) =
                     f32x4{acc[4 * h][t], acc[4 * h + 1][t], acc[4 * h + 2][t], acc[4 * h + 3][t]};
-        *reinterpret_cast<f32x4 *>(mine + 32) = f32x4{m, l, lq, 0.f};
+        *reinterpret_cast<f32x4 *>(mine + HD / 4) = f32x4{m, l, lq, 0.f};
     }
     __syncthreads();
+    if (!merges) return;
 #pragma unroll
     for (int hh = 0; hh < HALVES; ++hh) {
         const int rr = rows_rr[hh];
-        const float *src = red + (rr + 16 * cb) * REC;  // lane (rr, cb) of wave g: + g * 64 * REC
+        // the record of lane (rr, column group) of wave g: + g * 64 * REC
+        const float *src = red + (rr + 16 * (H64 ? q >> 2 : cb)) * REC;
+        const int val_off = H64 ? 4 * (q & 3) : 4 * q;
         f32x4 rec[NW], val[NW];
 #pragma unroll
         for (int g = 0; g < NW; ++g) {
-            rec[g] = *reinterpret_cast<const f32x4 *>(src + g * 64 * REC + 32);
-            val[g] = *reinterpret_cast<const f32x4 *>(src + g * 64 * REC + 4 * q);
+            rec[g] = *reinterpret_cast<const f32x4 *>(src + g * 64 * REC + HD / 4);
+            val[g] = *reinterpret_cast<const f32x4 *>(src + g * 64 * REC + val_off);
         }
         float M = -INFINITY;
 #pragma unroll
@@ -319,26 +347,28 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
         const float inv = LQ > 0.f ? 1.f / LQ : 0.f;
         const float lse_val = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
         o = o * inv;
+        const bool lse_lane = q == 0 && (H64 || cb == 0);
         if constexpr (SPLIT) {
             // byte offsets from the KV head's first partial row fit 32 bits
             // (the host checks it)
             const int64_t r0 = ((int64_t)b * p.n_h + kvh * p.group) * p.T * p.n_split_total + p.part_offset + part;
             store16_device_scope(p.o_part + r0 * HD, (unsigned)((o_off[hh] * HD + c) * 4), o);
-            if (cb == 0 && q == 0) p.lse_part[r0 + l_off[hh]] = lse_val;
+            if (lse_lane) p.lse_part[r0 + l_off[hh]] = lse_val;
         } else {
             if (p.out_format != kOutBf16) {
-                // the wave's 32 columns are one MX block, over the 8 lanes of the row
+                // 32-column MX blocks over 8 adjacent lanes of the row (hd
+                // 128: the wave's 32 columns; hd 64: two blocks per row)
                 const int64_t orow = o_off[hh];
                 const float v4[4] = {o[0], o[1], o[2], o[3]};
                 mx_store_block_8lanes(v4, p.out_format, p.o_codes + orow * (p.out_format == kOutMxFp8E4M3 ? HD : HD / 2),
-                                      p.o_scales + orow * (HD / 32), 32 * cb, q);
+                                      p.o_scales + orow * (HD / 32), H64 ? 32 * (q >> 3) : 32 * cb, q & 7);
             } else {
                 uint2 packed;
                 packed.x = (uint32_t)bf16_bits(o[0]) | ((uint32_t)bf16_bits(o[1]) << 16);
                 packed.y = (uint32_t)bf16_bits(o[2]) | ((uint32_t)bf16_bits(o[3]) << 16);
                 *reinterpret_cast<uint2 *>(p.o + o_off[hh] + c) = packed;
             }
-            if (cb == 0 && q == 0 && p.lse != nullptr) p.lse[l_off[hh]] = lse_val;
+            if (lse_lane && p.lse != nullptr) p.lse[l_off[hh]] = lse_val;
         }
     }
 }

@@ -202,6 +202,10 @@ def test_plan_of_each_workload(lib, args, kw, want):
     # MQA decode at hd 128 over 256 / 512 keys (64 tiles): one pass of eight waves
     ((8, 128, 1, 1, 256, 128), {}, "stream_kernel<128, false, false, 8, 1>"),
     ((8, 128, 1, 1, 512, 128), {}, "stream_kernel<128, false, false, 8, 2>"),
+    # ... and at hd 64 (one-slice work at hd 64 stays on the per-wave kernel)
+    ((8, 128, 1, 1, 256, 64), {}, "stream_kernel<64, false, false, 8, 1>"),
+    ((8, 128, 1, 1, 512, 64), {}, "stream_kernel<64, false, false, 8, 2>"),
+    ((8, 128, 1, 1, 128, 64), {}, "attn_kernel<64, 4, 4, 1, 1, false, true, false>"),
     # causal MHA prefill T 1, hd 128, 512 keys (128 one-row tiles, nothing shared)
     ((4, 32, 32, 1, 512, 128), dict(causal=True), "stream_kernel<128, false, true, 8, 2>"),
     # more tiles than compute units: the per-wave kernel

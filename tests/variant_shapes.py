@@ -44,6 +44,8 @@ def branch(plan: dict) -> str:
 EXPECTED = {
     64: {"attn_kernel<64, 4, 4, 1, 1, false, false>", "attn_kernel<64, 4, 4, 1, 2, false, false>",
          "attn_kernel<64, 4, 4, 1, 1, true, false>", "attn_kernel<64, 4, 4, 1, 1, true, true>",
+         "stream_kernel<64, true, 8, 1>", "stream_kernel<64, false, 8, 1>",
+         "stream_kernel<64, true, 8, 2>", "stream_kernel<64, false, 8, 2>",
          "rows_kernel<64, 1, 64>", "rows_kernel<64, 2, 32>"},
     128: {"attn_kernel<128, 4, 4, 1, 1, false, false>", "attn_kernel<128, 4, 4, 1, 2, false, false>",
           "stream_kernel<128, true, 4, 1>", "stream_kernel<128, false, 4, 1>",
