@@ -76,7 +76,10 @@ struct PassShape {
 // The NK key groups of a pass or pass-loop workgroup combined and stored.
 // Each wave parks its 16 x 128 fp32 tile in LDS (16-byte chunk c of row r at
 // chunk c ^ r: one wave-wide write or read then touches every bank once)
-// with its rows' (m, l, lq); then wave (kg, hp) combines the groups' tiles, in
+// with its rows' (m, l, lq) -- at hd 512 in its own K slice (16 KiB, read by
+// no other wave, so no barrier is needed before the writes), at hd 256 (8 KiB
+// slices) from the start of LDS once every wave is done with the K slices
+// and the scores; then wave (kg, hp) combines the groups' tiles, in
 // a fixed order, over columns 128 hp + CPW kg .. + CPW -- a store instruction
 // writes RPI rows x 4 CPW contiguous bytes.  out_row / lse_idx: the output
 // rows of this lane (lane / LPR + RPI ps), computed by the caller.
@@ -92,11 +95,16 @@ __device__ __forceinline__ void pass_combine_store(const FwdParams &p, unsigned 
     const int kg = wave / NH, hp = wave % NH;
     const int lr = lane & 15, lg = lane >> 4;
     const int col0 = 128 * hp;
-    float *rbuf = reinterpret_cast<float *>(smem + S::SMALL_OFF);  // [NW][16][4]: m, l, lq
-    auto tile = [&](int w) __attribute__((always_inline)) { return smem + w * 16 * 512; };
+    constexpr bool OWN = KPW * 256 >= 16 * 512 + 16 * 16;  // tile and records fit the wave's K slice
+    auto tile = [&](int w) __attribute__((always_inline)) { return smem + w * (OWN ? KPW * 256 : 16 * 512); };
+    // per wave and row: m, l, lq
+    auto rec_of = [&](int w) __attribute__((always_inline)) {
+        return OWN ? reinterpret_cast<float *>(smem + w * KPW * 256 + 16 * 512)
+                   : reinterpret_cast<float *>(smem + S::SMALL_OFF) + w * 16 * 4;
+    };
     // key group g holds keys [klo + KPW g, ...): it has data iff that is below khi
     const int n_groups = min(NK, (khi - klo + KPW - 1) / KPW);  // wave-uniform
-    lds_barrier();  // every wave is done with the K slices and the scores
+    if constexpr (!OWN) lds_barrier();  // every wave is done with the K slices and the scores
     if (kg < n_groups) {
         unsigned char *mine = tile(wave);
 #pragma unroll
@@ -107,7 +115,7 @@ __device__ __forceinline__ void pass_combine_store(const FwdParams &p, unsigned 
                 *reinterpret_cast<f32x4 *>(mine + lr * 512 + chunk * 16) =
                     f32x4{acc[4 * h][t], acc[4 * h + 1][t], acc[4 * h + 2][t], acc[4 * h + 3][t]};
             }
-        if (lg == 0) *reinterpret_cast<f32x4 *>(rbuf + (wave * 16 + lr) * 4) = f32x4{m, l, lq, 0.f};
+        if (lg == 0) *reinterpret_cast<f32x4 *>(rec_of(wave) + lr * 4) = f32x4{m, l, lq, 0.f};
     }
     lds_barrier();
     const int q = lane % LPR;
@@ -122,7 +130,7 @@ __device__ __forceinline__ void pass_combine_store(const FwdParams &p, unsigned 
             if (g < n_groups) {
                 const int w = g * NH + hp;
                 part_o[g] = *reinterpret_cast<const f32x4 *>(tile(w) + rr * 512 + (((cw >> 2) ^ rr) * 16));
-                rec[g] = *reinterpret_cast<const f32x4 *>(rbuf + (w * 16 + rr) * 4);
+                rec[g] = *reinterpret_cast<const f32x4 *>(rec_of(w) + rr * 4);
             } else {
                 part_o[g] = f32x4{0.f, 0.f, 0.f, 0.f};
                 rec[g] = f32x4{-INFINITY, 0.f, 0.f, 0.f};
