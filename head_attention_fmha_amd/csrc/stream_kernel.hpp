@@ -135,6 +135,29 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
     // at hd 128, 8 at hd 64 -- sixteen lanes cover a key row either way
     using VRow = typename std::conditional<H64, u32x2, u32x4>::type;
     VRow vr[KS][8];
+    // Eight-wave workgroups (one per compute unit: few-unit grids, where a
+    // CU's ingest bounds the pass) request V step by step: Q and K first,
+    // each 32-key step's QK product as soon as its K has landed, that step's
+    // V after it -- the last step's after the softmax -- so the QK and the
+    // softmax overlap the V ingest (a wave issues in order, and load issue
+    // runs at the CU's ingest rate: with every load ahead of them they waited
+    // for the whole pass).  MQA decode hd 128 over 256 / 384 / 512 keys 5.98 /
+    // 6.72 / 7.13 -> 5.75 / 6.46 / 6.97 us; hd 64 over 512 keys 5.62 -> 5.54
+    // us.  Four-wave workgroups (the split decode, several per CU, bound by
+    // HBM) keep every load in flight at once.
+    constexpr bool LATE = NW == 8;
+    constexpr int KL = 32 / RPL;    // K loads per 32-key step
+    auto issue_v = [&](int ks) __attribute__((always_inline)) {
+        const int last = khi - 1 - k0;
+        const uint16_t *vw = p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh + key_offset(k0, p.v_st);
+        const unsigned vstride = (unsigned)p.v_st * 2u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const unsigned off = (unsigned)min(32 * ks + 8 * lg + i, last) * vstride + 2u * NB * lr;
+            if constexpr (H64) vr[ks][i] = load8_buf<STREAM>(vw, off);
+            else vr[ks][i] = load16_buf<STREAM>(vw, off);
+        }
+    };
     if (active) {
         const uint16_t *qp = p.q + (int64_t)b * p.q_sb + (int64_t)t_row * p.q_st + (int64_t)h_row * p.q_sh + 8 * lg;
         // rows past the end read row 0 of the group (valid memory); they are
@@ -161,16 +184,18 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
             load_lds_buf<STREAM>(kw, (unsigned)min(r, last) * kstride + 16u * chunk, sKw + it * 1024);
         }
         __builtin_amdgcn_sched_barrier(0);  // Q, then K, then V: the waits below count on that order
-        // V: 8 KS wave-wide register loads of four whole key rows each
+        if constexpr (!LATE) {
+            // V: 8 KS wave-wide register loads of four whole key rows each
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const unsigned off = (unsigned)min(32 * ks + 8 * lg + i, last) * vstride + 2u * NB * lr;
-                if constexpr (H64) vr[ks][i] = load8_buf<STREAM>(vw, off);
-                else vr[ks][i] = load16_buf<STREAM>(vw, off);
-            }
-        __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
+                for (int i = 0; i < 8; ++i) {
+                    const unsigned off = (unsigned)min(32 * ks + 8 * lg + i, last) * vstride + 2u * NB * lr;
+                    if constexpr (H64) vr[ks][i] = load8_buf<STREAM>(vw, off);
+                    else vr[ks][i] = load16_buf<STREAM>(vw, off);
+                }
+            __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
+        }
     }
 
     float m = -INFINITY, l = 0.f, lq = 0.f;
@@ -179,11 +204,46 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
     for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (active) {
+      const unsigned qmask = row_ok ? 0xffffffffu : 0u;
+      bf16x8 qf[KSTEPS];
+      f32x4 sc[KS][2];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sc[ks][0] = sc[ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (LATE) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            // Q and this step's K have landed (the next step's K, or this
+            // wave's first V loads, may still fly)
+            if (ks == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm((KS - 1) * KL));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks == 0) {
+#pragma unroll
+                for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, qraw[s] & qmask);
+            }
+            bf16x8 kf[KSTEPS][2];
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk) {
+                    const int r = 32 * ks + 8 * (lr >> 2) + 4 * blk + (lr & 3);
+                    const int slot = (4 * s + lg + rot_of(r)) & (CHUNKS - 1);
+                    kf[s][blk] = *reinterpret_cast<const bf16x8 *>(sKw + r * ROW_BYTES + 16 * slot);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk) sc[ks][blk] = mfma_16x16x32(kf[s][blk], qf[s], sc[ks][blk]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (KS == 1 || ks + 1 < KS) issue_v(ks);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
         // Q and K have landed (V's 8 KS loads, issued last, may still fly)
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * KS));
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const unsigned qmask = row_ok ? 0xffffffffu : 0u;
-        bf16x8 qf[KSTEPS];
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, qraw[s] & qmask);
         // every K operand read is issued before the first MFMA (a read waited
@@ -201,15 +261,13 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
                     kf[s][ks][blk] = *reinterpret_cast<const bf16x8 *>(sKw + r * ROW_BYTES + 16 * slot);
                 }
         __builtin_amdgcn_sched_barrier(0);
-        f32x4 sc[KS][2];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sc[ks][0] = sc[ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk) sc[ks][blk] = mfma_16x16x32(kf[s][ks][blk], qf[s], sc[ks][blk]);
+      }
         // scores of keys k0 + 32ks + 8lg + j, j = 0..7: block 0 holds j < 4,
         // block 1 the rest
         float x[KS][8];
@@ -239,11 +297,19 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
             }
         l = psum;
         lq = qsum;
+        if constexpr (LATE) {
+            if (KS > 1) issue_v(KS - 1);
+        }
         // V^T operands: element i of MFMA j's operand is V[key 32ks + 8lg + i][NB lr + j];
         // dword u pairs keys 2u, 2u+1 -- the low (j even) or high (j odd)
         // halves of dword j/2 of registers 2u and 2u+1 (v_perm_b32)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks) {
+            if (LATE && KS > 1) {  // step 0's V ahead of the last step's, issued last
+                if (ks == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
@@ -254,6 +320,8 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
                 acc[j] = mfma_16x16x32(__builtin_bit_cast(bf16x8, a), pt[ks],
                                        ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[j]);
             }
+            if (LATE && KS > 1) __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     l = row4_sum(l);
