@@ -631,15 +631,29 @@ __global__ __launch_bounds__(512, 2) void pass_loop_kernel(const FwdParams p) {
         // ---- online softmax of the key group and O^T += V^T . P^T
         float x[KS][8];
         float mx = -INFINITY;
+        // keys visible to every row of the tile (the first row's upper
+        // bound, the last row's lower one): the wave's keys need no mask
+        const int full_hi = p.causal ? min(khi, pos_lo + 1) : khi;
+        const int full_lo = p.window > 0 ? max(klo, pos_hi - p.window + 1) : klo;
+        if (k0 >= full_lo && k0 + 32 * KS <= full_hi) {  // wave-uniform
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int key = k0 + 32 * ks + 8 * lg + j;
-                const float s = j < 4 ? sc[ks][0][j] : sc[ks][1][j - 4];
-                x[ks][j] = (key >= r_lo && key < r_hi) ? s * p.scale_log2 : -INFINITY;
-                mx = fmaxf(mx, x[ks][j]);
-            }
+                for (int j = 0; j < 8; ++j) {
+                    x[ks][j] = (j < 4 ? sc[ks][0][j] : sc[ks][1][j - 4]) * p.scale_log2;
+                    mx = fmaxf(mx, x[ks][j]);
+                }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int key = k0 + 32 * ks + 8 * lg + j;
+                    const float s = j < 4 ? sc[ks][0][j] : sc[ks][1][j - 4];
+                    x[ks][j] = (key >= r_lo && key < r_hi) ? s * p.scale_log2 : -INFINITY;
+                    mx = fmaxf(mx, x[ks][j]);
+                }
+        }
         const float m_new = fmaxf(m, row4_max(mx));
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         if (P > 0) {  // (exp2(-inf) = 0 for a group with no visible key so far)
