@@ -70,7 +70,7 @@ __global__ __launch_bounds__(64 * NW, KS == 1 ? 4 : 2) void stream_kernel(const 
     constexpr int WAVE_KEYS = 32 * KS;
     constexpr int K_BYTES = NW * WAVE_KEYS * ROW_BYTES;  // every wave's K slice (16 to 128 KiB)
     constexpr int REC = HD / 4 + 4;                      // merge record per lane: HD/4 outputs, m, l, lq, pad
-    constexpr int M_BYTES = NW * 64 * REC * 4;           // every wave's records (36 or 72 KiB)
+    constexpr int M_BYTES = NW * 64 * REC * 4;           // every wave's records (20 to 72 KiB)
     // the K slices, then (after every wave's QK) the merge records
     __shared__ __attribute__((aligned(16))) unsigned char smem[M_BYTES > K_BYTES ? M_BYTES : K_BYTES];
 
