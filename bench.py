@@ -559,9 +559,9 @@ def run_cpu_baseline(I, torch, budget_s):
     GQA split-KV decode workload (split + merge, the bench step) and the
     single-head decode, the largest MQA decode point, the largest causal MHA
     prefill point and the sliding-window prefill (one fused call each), each
-    with one thread and with the machine's CPU share.  Runs are repeated up to
-    three times within the budget; the median is reported, excluding input
-    generation.  The headline `value` is the decode step with all threads."""
+    with one thread and with the host's CPU share (at most 16 threads).  Runs
+    are repeated up to three times within the budget; the median is reported,
+    excluding input generation.  The headline `value` is the decode step with all threads."""
     import oracle
     threads_all = oracle.default_threads()
     decode = I.GQA_SPLITKV_DECODE
