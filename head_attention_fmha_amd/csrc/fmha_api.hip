@@ -17,6 +17,7 @@
 #include "stream_kernel.hpp"
 #include "rows_split_kernel.hpp"
 #include "pass_kernel.hpp"
+#include "cols_kernel.hpp"
 #include "merge_kernel.hpp"
 
 namespace {
@@ -171,6 +172,7 @@ enum Variant : int {
     kStreamWide2Shared,
     kPass,          // pass_kernel<HD>: one pass over <= 128 keys, every load up front (hd >= 256)
     kPassLoop,      // pass_loop_kernel<HD>: 128-key passes, few-unit grids (hd >= 256)
+    kCols,          // cols_kernel<512>: one pass over <= 128 keys, keys split by wave for the scores, columns for PV
     kAttnOneStream, // attn_kernel, one slice, streamed
     kAttnOne,       // attn_kernel, one slice, K/V shared with other row blocks
     kAttnTwoTiles,  // attn_kernel, several slices, two tiles per workgroup
@@ -274,8 +276,10 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
         snprintf(pl.kernel, sizeof pl.kernel, "rows_kernel<%d, %d, %d, %s>", hd, var == kRowsTwoTiles ? 2 : 1,
                  var == kRowsTwoTiles ? 32 : rows_chunk_keys(hd), sp);
     } else if (pass) {
-        var = span <= 128 ? kPass : kPassLoop;
-        snprintf(pl.kernel, sizeof pl.kernel, "%s<%d, %s>", var == kPass ? "pass_kernel" : "pass_loop_kernel", hd, sp);
+        // hd 512 over one pass: the column-split kernel
+        var = span > 128 ? kPassLoop : hd == 512 ? kCols : kPass;
+        snprintf(pl.kernel, sizeof pl.kernel, "%s<%d, %s>",
+                 var == kPass ? "pass_kernel" : var == kCols ? "cols_kernel" : "pass_loop_kernel", hd, sp);
     } else if (wide) {
         const int ks = span <= 256 ? 1 : 2;
         var = ks == 1 ? (pl.streaming ? kStreamWide : kStreamWideShared)
@@ -353,8 +357,13 @@ void launch_hd(const FwdParams &p, int var, hipStream_t s) {
                 hipLaunchKernelGGL((fmha::stream_kernel<HD, SPLIT, false, 8, 2>), dim3(p.n_units), dim3(512), 0, s, p);
             break;
         case kPass:
-            if constexpr (HD >= 256)
+            if constexpr (HD == 256)
                 hipLaunchKernelGGL((fmha::pass_kernel<HD, SPLIT>), dim3(p.n_units), dim3(64 * fmha::PassShape<HD>::NW),
+                                   0, s, p);
+            break;
+        case kCols:
+            if constexpr (HD == 512)
+                hipLaunchKernelGGL((fmha::cols_kernel<HD, SPLIT>), dim3(p.n_units), dim3(64 * fmha::ColsShape<HD>::NW),
                                    0, s, p);
             break;
         case kPassLoop:

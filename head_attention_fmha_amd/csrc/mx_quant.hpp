@@ -132,4 +132,19 @@ __device__ __forceinline__ void mx_store_block_8lanes(const float (&v)[4], int f
     if (q == 0) scales_row[col / 32] = (uint8_t)(x + 127);
 }
 
+// One 32-column block over 2 lanes (lane and lane ^ 16, half = 0 / 1 holding
+// columns 0..15 / 16..31 of the block, v[4t + j] = column 4t + j of its half),
+// as the column-split kernel holds it.
+__device__ __forceinline__ void mx_store_block_2lanes(const float (&v)[16], int fmt, uint8_t *codes_row,
+                                                      uint8_t *scales_row, int col, int half) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = fmaxf(amax, xor_shuffle(amax, 16));
+    const int x = mx_block_exp(amax, mx_emax(fmt));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) mx_store4(v + 4 * t, x, fmt, codes_row, col + 16 * half + 4 * t);
+    if (half == 0) scales_row[col / 32] = (uint8_t)(x + 127);
+}
+
 }  // namespace fmha

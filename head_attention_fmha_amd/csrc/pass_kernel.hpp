@@ -1,8 +1,9 @@
 // pass_kernel.hpp -- attention at hd 256 and 512 on gfx950 for few-unit
 // grids: a workgroup computes one 16-row tile (one KV head, one key range)
 // in one pass over at most 128 keys with every load it needs in flight
-// together (pass_kernel), or in several such passes (pass_loop_kernel,
-// below).
+// together (pass_kernel, launched at hd 256; one pass at hd 512 runs the
+// column-split kernel of cols_kernel.hpp), or in several such passes
+// (pass_loop_kernel, below, hd 256 and 512).
 //
 // Grids of this kind are few-unit and latency-bound: the MQA decode of 128
 // query heads over one KV head (64 tiles; as split-KV, 128-key partitions),

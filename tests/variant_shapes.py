@@ -56,14 +56,14 @@ EXPECTED = {
           "attn_kernel<256, 8, 4, 2, 1, false, false>", "pass_kernel<256>", "pass_loop_kernel<256>",
           "rows_kernel<256, 1, 32>"},
     512: {"attn_kernel<512, 4, 1, 4, 1, false, false>", "attn_kernel<512, 4, 1, 4, 2, false, false>",
-          "attn_kernel<512, 8, 2, 4, 1, false, false>", "pass_kernel<512>", "pass_loop_kernel<512>",
+          "attn_kernel<512, 8, 2, 4, 1, false, false>", "cols_kernel<512>", "pass_loop_kernel<512>",
           "rows_split_kernel<512>"},
 }
 
 
 # position of the SPLIT template argument in each kernel family's name
 _SPLIT_ARG = {"attn_kernel": 5, "rows_kernel": 3, "rows_split_kernel": 1, "stream_kernel": 1, "pass_kernel": 1,
-              "pass_loop_kernel": 1}
+              "pass_loop_kernel": 1, "cols_kernel": 1}
 
 
 def split_twin(kernel: str) -> str:
