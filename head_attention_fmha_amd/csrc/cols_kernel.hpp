@@ -84,7 +84,7 @@ __device__ __forceinline__ void mx_store_fused(const FwdParams &p, int b, int t,
                           p.o_scales + orow * (HD / 32), col0 + 32 * (lg >> 1), lg & 1);
 }
 
-template <int HD, bool SPLIT>
+template <int HD, bool SPLIT, bool LOOP>
 __global__ __launch_bounds__(512, 2) void cols_kernel(const FwdParams p) {
     using S = ColsShape<HD>;
     constexpr int ROW = S::ROW, CH = S::CH, HS = S::HS, KPW = S::KPW, P_STRIDE = S::P_STRIDE;
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(512, 2) void cols_kernel(const FwdParams p) {
     int khi = min(klo + p.split_len, s_k);
     if (p.causal) khi = min(khi, pos_hi + 1);
     if (p.window > 0) klo = max(klo, pos_lo - p.window + 1);
-    const bool any = khi > klo;  // workgroup-uniform; at most 128 keys (host plan)
+    const bool any = khi > klo;  // workgroup-uniform; at most 128 keys without LOOP (host plan)
 
     // this lane's row (N column of both products) and its visible keys
     const int row = row0 + lr;
@@ -194,20 +194,23 @@ __global__ __launch_bounds__(512, 2) void cols_kernel(const FwdParams p) {
         load_lds_buf(qrow, 16u * (unsigned)((lane - rr) & (CH - 1)), sQ + rr * ROW);
     }
     const unsigned kstride = (unsigned)p.k_st * 2u, vstride = (unsigned)p.v_st * 2u;
-    if (active) {
-        const uint16_t *kw = p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh + key_offset(k0, p.k_st);
-        const int last = khi - 1 - k0;
+    const uint16_t *khead = p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
+    // the wave's 16 K rows from key k (keys past the range read key khi - 1)
+    auto issue_k = [&](int k) __attribute__((always_inline)) {
+        const uint16_t *kw = khead + key_offset(k, p.k_st);
+        const int last = khi - 1 - k;
 #pragma unroll
         for (int r = 0; r < KPW; ++r)
             load_lds_buf(kw, (unsigned)min(r, last) * kstride + 16u * (unsigned)((lane - r) & (CH - 1)),
                          sK + r * ROW);
-    }
-    u32x2 vr[4][8];  // V[key klo + 32ks + 8lg + i][col0 + 4lr .. +3]
+    };
+    if (active) issue_k(k0);
+    u32x2 vr[4][8];  // V[key kp + 32ks + 8lg + i][col0 + 4lr .. +3] of the pass from key kp
     const uint16_t *vhead = p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh + col0;
-    auto issue_v = [&](int ks) __attribute__((always_inline)) {
+    auto issue_v = [&](int kp, int ks) __attribute__((always_inline)) {
         // the step's first key row (key khi - 1 for a step past the range),
         // wave-uniform: the buffer base
-        const int first = min(klo + 32 * ks, khi - 1);
+        const int first = min(kp + 32 * ks, khi - 1);
         const uint16_t *vw = vhead + key_offset(first, p.v_st);
         const int last = khi - 1 - first;  // >= 0
 #pragma unroll
@@ -215,109 +218,148 @@ __global__ __launch_bounds__(512, 2) void cols_kernel(const FwdParams p) {
             vr[ks][i] = load8_buf<false>(vw, (unsigned)min(8 * lg + i, last) * vstride + 8u * (unsigned)lr);
     };
     __builtin_amdgcn_sched_barrier(0);
-    issue_v(0);
-    issue_v(1);
+    issue_v(klo, 0);
+    issue_v(klo, 1);
     __builtin_amdgcn_sched_barrier(0);
     // Q and K have landed (V steps 0 and 1 may still fly), then every wave's
     // Q rows are in LDS
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
     lds_barrier();
 
-    // ---- S^T = K . Q^T over the whole head dimension -----------------------
-    float x[4];
-    float mx = -INFINITY;
-    if (active) {
-        f32x4 sacc[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s4 = 0; s4 < HS; s4 += 4) {
-            bf16x8 kf[4], qf[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int slot = (4 * (s4 + u) + lg + lr) & (CH - 1);
-                kf[u] = *reinterpret_cast<const bf16x8 *>(sK + lr * ROW + 16 * slot);
-                qf[u] = *reinterpret_cast<const bf16x8 *>(sQ + lr * ROW + 16 * slot);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) sacc[u] = mfma_16x16x32(kf[u], qf[u], sacc[u]);
-        }
-        const f32x4 sc = ((sacc[0] + sacc[1]) + sacc[2]) + sacc[3];
-        // keys visible to every row of the tile (the first row's upper bound,
-        // the last row's lower one): the wave's keys need no mask
-        const int pos_f = s_k - p.T + row0 / p.group;
-        const int full_hi = p.causal ? min(khi, pos_f + 1) : khi;
-        const int full_lo = p.window > 0 ? max(klo, pos_hi - p.window + 1) : klo;
-        if (k0 >= full_lo && k0 + KPW <= full_hi) {  // wave-uniform
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                x[t] = sc[t] * p.scale_log2;
-                mx = fmaxf(mx, x[t]);
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int key = k0 + 4 * lg + t;
-                x[t] = (key >= r_lo && key < r_hi) ? sc[t] * p.scale_log2 : -INFINITY;
-                mx = fmaxf(mx, x[t]);
-            }
-        }
-        mx = row4_max(mx);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    issue_v(2);
-    issue_v(3);
-    __builtin_amdgcn_sched_barrier(0);
+    // keys visible to every row of the tile (the first row's upper bound, the
+    // last row's lower one): a wave whose keys lie inside needs no mask
+    const int pos_f = s_k - p.T + row0 / p.group;
+    const int full_hi = p.causal ? min(khi, pos_f + 1) : khi;
+    const int full_lo = p.window > 0 ? max(klo, pos_hi - p.window + 1) : klo;
 
-    // ---- the tile-wide row maximum, the weights and their sums -------------
-    if (lg == 0) sMx[wave * 16 + lr] = mx;
-    lds_barrier();
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < S::NW; ++w) M = fmaxf(M, sMx[w * 16 + lr]);
-    const float m_use = (M == -INFINITY) ? 0.f : M;
-    {
-        float l = 0.f, lq = 0.f;
-        unsigned pw[2] = {0u, 0u};
-        if (active) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float pj = fast_exp2(x[t] - m_use);
-                const uint16_t pb = bf16_bits(pj);
-                l += pj;
-                lq += __uint_as_float((unsigned)pb << 16);
-                pw[t >> 1] |= (unsigned)pb << (16 * (t & 1));
-            }
-            l = row4_sum(l);
-            lq = row4_sum(lq);
-        }
-        *reinterpret_cast<uint2 *>(sP + lr * P_STRIDE + 2 * (KPW * wave + 4 * lg)) = uint2{pw[0], pw[1]};
-        if (lg == 0) *reinterpret_cast<float2 *>(sSum + 2 * (wave * 16 + lr)) = float2{l, lq};
-    }
-
-    lds_barrier();
-
-    float L = 0.f, LQ = 0.f;
-#pragma unroll
-    for (int w = 0; w < S::NW; ++w) {
-        const float2 s2 = *reinterpret_cast<const float2 *>(sSum + 2 * (w * 16 + lr));
-        L += s2.x;
-        LQ += s2.y;
-    }
-
-    // ---- O^T += V^T . P^T over the tile's keys, this wave's 64 columns ------
+    // ---- passes of 128 keys (one without LOOP).  Pass P from key kp: the
+    // scores of wave w's keys kp + 16w .. +15, the tile-wide row maximum
+    // (running over the passes: the accumulators and sums are rescaled when
+    // it grows -- the multi-tile online softmax of the e4ee9fdc commit log
+    // of the pages), the weights, and O += P V over the pass's keys.  The
+    // next pass's K is requested into the wave's own slice once its QK
+    // product has read it, the next pass's V registers once its PV product
+    // has consumed them.
+    const int npass = LOOP ? (khi - klo + 127) / 128 : 1;  // workgroup-uniform, >= 1
+    float M = -INFINITY, L = 0.f, LQ = 0.f;
     f32x4 acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-        const int nks = (khi - klo + 31) / 32;  // 32-key steps holding keys (uniform)
+    for (int P = 0; P < npass; ++P) {
+        const int kp = klo + 128 * P;
+        const int kw0 = kp + KPW * wave;  // this wave's first key of the pass
+        const bool act = kw0 < khi;       // wave-uniform
+        // ---- S^T = K . Q^T over the whole head dimension
+        float x[4];
+        float mx = -INFINITY;
+        if (act) {
+            f32x4 sacc[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s4 = 0; s4 < HS; s4 += 4) {
+                bf16x8 kf[4], qf[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int slot = (4 * (s4 + u) + lg + lr) & (CH - 1);
+                    kf[u] = *reinterpret_cast<const bf16x8 *>(sK + lr * ROW + 16 * slot);
+                    qf[u] = *reinterpret_cast<const bf16x8 *>(sQ + lr * ROW + 16 * slot);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sacc[u] = mfma_16x16x32(kf[u], qf[u], sacc[u]);
+            }
+            const f32x4 sc = ((sacc[0] + sacc[1]) + sacc[2]) + sacc[3];
+            if (kw0 >= full_lo && kw0 + KPW <= full_hi) {  // wave-uniform
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    x[t] = sc[t] * p.scale_log2;
+                    mx = fmaxf(mx, x[t]);
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int key = kw0 + 4 * lg + t;
+                    x[t] = (key >= r_lo && key < r_hi) ? sc[t] * p.scale_log2 : -INFINITY;
+                    mx = fmaxf(mx, x[t]);
+                }
+            }
+            mx = row4_max(mx);
+        }
+        // the next pass's K into the wave's slice, once the QK reads are done
+        bool next_k = false;
+        if constexpr (LOOP) {
+            next_k = P + 1 < npass && kw0 + 128 < khi;  // wave-uniform
+            if (next_k) {
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                __builtin_amdgcn_sched_barrier(0);
+                issue_k(kw0 + 128);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue_v(kp, 2);
+        issue_v(kp, 3);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- the tile-wide row maximum, the weights and their sums
+        if (lg == 0) sMx[wave * 16 + lr] = mx;
+        lds_barrier();
+        float m_new = M;
+#pragma unroll
+        for (int w = 0; w < S::NW; ++w) m_new = fmaxf(m_new, sMx[w * 16 + lr]);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        if constexpr (LOOP) {
+            if (P > 0) {  // (exp2(-inf) = 0 while no key was visible)
+                const float alpha = fast_exp2(M - m_use);
+                L *= alpha;
+                LQ *= alpha;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] = acc[j] * alpha;
+            }
+        }
+        M = m_new;
+        {
+            float l = 0.f, lq = 0.f;
+            unsigned pw[2] = {0u, 0u};
+            if (act) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float pj = fast_exp2(x[t] - m_use);
+                    const uint16_t pb = bf16_bits(pj);
+                    l += pj;
+                    lq += __uint_as_float((unsigned)pb << 16);
+                    pw[t >> 1] |= (unsigned)pb << (16 * (t & 1));
+                }
+                l = row4_sum(l);
+                lq = row4_sum(lq);
+            }
+            *reinterpret_cast<uint2 *>(sP + lr * P_STRIDE + 2 * (KPW * wave + 4 * lg)) = uint2{pw[0], pw[1]};
+            if (lg == 0) *reinterpret_cast<float2 *>(sSum + 2 * (wave * 16 + lr)) = float2{l, lq};
+        }
+        lds_barrier();
+#pragma unroll
+        for (int w = 0; w < S::NW; ++w) {
+            const float2 s2 = *reinterpret_cast<const float2 *>(sSum + 2 * (w * 16 + lr));
+            L += s2.x;
+            LQ += s2.y;
+        }
+
+        // ---- O^T += V^T . P^T over the pass's keys, this wave's 64 columns
+        const int nks = min(4, (khi - kp + 31) / 32);  // 32-key steps holding keys (uniform)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            // step ks's V has landed (the later steps', 8 loads each, may fly)
-            if (ks == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(24));
-            else if (ks == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
-            else if (ks == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
-            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            // step ks's V has landed (the later steps', 8 loads each, and the
+            // next pass's K, 16, requested between steps 1 and 2, may fly)
+            if (ks == 0) {
+                if (next_k) __builtin_amdgcn_s_waitcnt(waitcnt_vm(40));
+                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(24));
+            } else if (ks == 1) {
+                if (next_k) __builtin_amdgcn_s_waitcnt(waitcnt_vm(32));
+                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
+            } else if (ks == 2) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+            } else {
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            }
             __builtin_amdgcn_sched_barrier(0);
             if (ks < nks) {
                 const bf16x8 pt = *reinterpret_cast<const bf16x8 *>(sP + lr * P_STRIDE + 64 * ks + 16 * lg);
@@ -330,6 +372,16 @@ __global__ __launch_bounds__(512, 2) void cols_kernel(const FwdParams p) {
                         a[u] = __builtin_amdgcn_perm(vr[ks][2 * u + 1][j >> 1], vr[ks][2 * u][j >> 1], sel);
                     acc[j] = mfma_16x16x32(__builtin_bit_cast(bf16x8, a), pt, acc[j]);
                 }
+            }
+        }
+        // the V registers are free: the next pass's steps 0 and 1 (its K has
+        // landed: the wait before step 3 covered it)
+        if constexpr (LOOP) {
+            if (P + 1 < npass) {
+                __builtin_amdgcn_sched_barrier(0);
+                issue_v(kp + 128, 0);
+                issue_v(kp + 128, 1);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }

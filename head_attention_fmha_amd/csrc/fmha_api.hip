@@ -172,7 +172,8 @@ enum Variant : int {
     kStreamWide2Shared,
     kPass,          // pass_kernel<HD>: one pass over <= 128 keys, every load up front (hd >= 256)
     kPassLoop,      // pass_loop_kernel<HD>: 128-key passes, few-unit grids (hd >= 256)
-    kCols,          // cols_kernel<512>: one pass over <= 128 keys, keys split by wave for the scores, columns for PV
+    kCols,          // cols_kernel<512, LOOP = false>: one pass over <= 128 keys, keys by wave for the scores, columns for PV
+    kColsLoop,      // cols_kernel<512, LOOP = true>: 128-key passes, few-unit grids
     kAttnOneStream, // attn_kernel, one slice, streamed
     kAttnOne,       // attn_kernel, one slice, K/V shared with other row blocks
     kAttnTwoTiles,  // attn_kernel, several slices, two tiles per workgroup
@@ -276,10 +277,21 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
         snprintf(pl.kernel, sizeof pl.kernel, "rows_kernel<%d, %d, %d, %s>", hd, var == kRowsTwoTiles ? 2 : 1,
                  var == kRowsTwoTiles ? 32 : rows_chunk_keys(hd), sp);
     } else if (pass) {
-        // hd 512 over one pass: the column-split kernel
-        var = span > 128 ? kPassLoop : hd == 512 ? kCols : kPass;
-        snprintf(pl.kernel, sizeof pl.kernel, "%s<%d, %s>",
-                 var == kPass ? "pass_kernel" : var == kCols ? "cols_kernel" : "pass_loop_kernel", hd, sp);
+        // hd 512: the column-split kernel over one pass, and over several when
+        // row blocks share each KV head's K/V through L2 (MQA decode hd 512
+        // over 256 / 384 / 512 keys: 16.0 / 20.6 / 25.1 -> 14.6 / 19.3 / 24.2
+        // us); a lone row block per KV head streams K/V that no other
+        // workgroup reads, where the pass loop's 256-byte row parts went
+        // faster (causal MHA prefill T 1 / T 4 over 512 keys: 30.2 / 30.3
+        // against 31.1 / 31.4 us)
+        const bool shared_kv = (p.rows + 15) / 16 > 1;
+        if (hd == 512 && (span <= 128 || shared_kv)) {
+            var = span > 128 ? kColsLoop : kCols;
+            snprintf(pl.kernel, sizeof pl.kernel, "cols_kernel<%d, %s, %s>", hd, sp, var == kColsLoop ? "true" : "false");
+        } else {
+            var = span > 128 ? kPassLoop : kPass;
+            snprintf(pl.kernel, sizeof pl.kernel, "%s<%d, %s>", var == kPass ? "pass_kernel" : "pass_loop_kernel", hd, sp);
+        }
     } else if (wide) {
         const int ks = span <= 256 ? 1 : 2;
         var = ks == 1 ? (pl.streaming ? kStreamWide : kStreamWideShared)
@@ -363,8 +375,13 @@ void launch_hd(const FwdParams &p, int var, hipStream_t s) {
             break;
         case kCols:
             if constexpr (HD == 512)
-                hipLaunchKernelGGL((fmha::cols_kernel<HD, SPLIT>), dim3(p.n_units), dim3(64 * fmha::ColsShape<HD>::NW),
-                                   0, s, p);
+                hipLaunchKernelGGL((fmha::cols_kernel<HD, SPLIT, false>), dim3(p.n_units),
+                                   dim3(64 * fmha::ColsShape<HD>::NW), 0, s, p);
+            break;
+        case kColsLoop:
+            if constexpr (HD == 512)
+                hipLaunchKernelGGL((fmha::cols_kernel<HD, SPLIT, true>), dim3(p.n_units),
+                                   dim3(64 * fmha::ColsShape<HD>::NW), 0, s, p);
             break;
         case kPassLoop:
             if constexpr (HD >= 256)

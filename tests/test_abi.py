@@ -190,12 +190,14 @@ def test_plan_of_each_workload(lib, args, kw, want):
 
 @pytest.mark.parametrize("args,kw,kernel", [
     ((32, 64, 8, 1, 8192, 128), dict(split_len=128), "stream_kernel<128, true, true, 4, 1>"),
-    ((8, 128, 1, 1, 512, 512), {}, "pass_loop_kernel<512, false>"),
+    ((8, 128, 1, 1, 512, 512), {}, "cols_kernel<512, false, true>"),
+    # one 16-row block per KV head over several passes: the pass loop
+    ((4, 32, 32, 1, 512, 512), dict(causal=True), "pass_loop_kernel<512, false>"),
     # more 16-row units than compute units (but fewer than two per unit): the
     # per-wave kernel with eight waves
     ((40, 128, 1, 1, 512, 512), {}, "attn_kernel<512, 8, 2, 4, 1, false, false, false>"),
-    ((8, 128, 1, 1, 512, 512), dict(split_len=128), "cols_kernel<512, true>"),
-    ((2, 16, 1, 128, 4096, 512), dict(causal=True, window=128), "cols_kernel<512, false>"),
+    ((8, 128, 1, 1, 512, 512), dict(split_len=128), "cols_kernel<512, true, false>"),
+    ((2, 16, 1, 128, 4096, 512), dict(causal=True, window=128), "cols_kernel<512, false, false>"),
     ((4, 32, 32, 128, 512, 512), dict(causal=True), "rows_split_kernel<512, false>"),
     ((2, 32, 8, 4096, 4096, 128), dict(causal=True), "rows_kernel<128, 2, 32, false>"),
     ((1, 1, 1, 1, 128, 64), {}, "attn_kernel<64, 4, 4, 1, 1, false, true, true>"),

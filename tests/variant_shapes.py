@@ -56,7 +56,7 @@ EXPECTED = {
           "attn_kernel<256, 8, 4, 2, 1, false, false>", "pass_kernel<256>", "pass_loop_kernel<256>",
           "rows_kernel<256, 1, 32>"},
     512: {"attn_kernel<512, 4, 1, 4, 1, false, false>", "attn_kernel<512, 4, 1, 4, 2, false, false>",
-          "attn_kernel<512, 8, 2, 4, 1, false, false>", "cols_kernel<512>", "pass_loop_kernel<512>",
+          "attn_kernel<512, 8, 2, 4, 1, false, false>", "cols_kernel<512, false>", "cols_kernel<512, true>", "pass_loop_kernel<512>",
           "rows_split_kernel<512>"},
 }
 
