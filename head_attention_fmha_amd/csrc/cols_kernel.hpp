@@ -1,9 +1,10 @@
-// cols_kernel.hpp -- one 16-row tile over at most 128 keys at hd 512, for
-// few-unit grids (the sliding-window MQA prefill, the MQA decode over 128
-// keys, the 128-key partitions of a split call), with the work divided
-// between the eight waves by keys for the scores and by output columns for
-// the product with V, so that no wave's partial result has to be summed
-// with another's:
+// cols_kernel.hpp -- one 16-row tile at hd 512 for few-unit grids, over at
+// most 128 keys in one pass (the sliding-window MQA prefill, the MQA decode
+// over 128 keys, the 128-key partitions of a split call) or, with LOOP, over
+// several 128-key passes (the MQA decode over longer caches), with the work
+// of a pass divided between the eight waves by keys for the scores and by
+// output columns for the product with V, so that no wave's partial result
+// has to be summed with another's:
 //
 //   * scores: wave w takes keys klo + 16w .. +15 over the whole head
 //     dimension (16 MFMA steps of 32 columns, four independent chains summed
