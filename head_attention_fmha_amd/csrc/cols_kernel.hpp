@@ -1,4 +1,4 @@
-// cols_kernel.hpp -- one 16-row tile at hd 512 for few-unit grids, over at
+// cols_kernel.hpp -- one 16-row tile at hd 512 (and 256) for few-unit grids, over at
 // most 128 keys in one pass (the sliding-window MQA prefill, the MQA decode
 // over 128 keys, the 128-key partitions of a split call) or, with LOOP, over
 // several 128-key passes (the MQA decode over longer caches), with the work
@@ -54,13 +54,17 @@ namespace fmha {
 
 template <int HD>
 struct ColsShape {
-    static_assert(HD == 512, "the column-split kernel serves hd 512");
+    static_assert(HD == 256 || HD == 512, "the column-split kernel serves hd 256 and 512");
     static constexpr int NW = 8;                  // waves
     static constexpr int KPW = 16;                // keys per wave (scores)
-    static constexpr int CPW = HD / NW;           // output columns per wave (64)
-    static constexpr int ROW = HD * 2;            // bytes per Q / K row (1 KiB)
-    static constexpr int CH = ROW / 16;           // 16-byte chunks per row (64)
-    static constexpr int HS = HD / 32;            // head-dim steps of the QK product (16)
+    static constexpr int CPW = 64;                // output columns per wave
+    static constexpr int NPV = HD / CPW;          // waves with output columns (8, or 4 at hd 256)
+    static constexpr int ROW = HD * 2;            // bytes per Q / K row (1 KiB at hd 512)
+    static constexpr int CH = ROW / 16;           // 16-byte chunks per row
+    static constexpr int RPI = 1024 / ROW;        // rows per wave-wide 16-byte load
+    static constexpr int LPR = 64 / RPI;          // lanes per row in such a load
+    static constexpr int KI = KPW / RPI;          // K load instructions per wave and pass
+    static constexpr int HS = HD / 32;            // head-dim steps of the QK product
     static constexpr int P_STRIDE = 128 * 2 + 16; // bytes per weight row (padded)
     static constexpr int Q_OFF = 0;
     static constexpr int K_OFF = Q_OFF + 16 * ROW;
@@ -89,6 +93,7 @@ template <int HD, bool SPLIT, bool LOOP>
 __global__ __launch_bounds__(512, 2) void cols_kernel(const FwdParams p) {
     using S = ColsShape<HD>;
     constexpr int ROW = S::ROW, CH = S::CH, HS = S::HS, KPW = S::KPW, P_STRIDE = S::P_STRIDE;
+    constexpr int RPI = S::RPI, LPR = S::LPR, KI = S::KI, NPV = S::NPV;
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::QK_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char xmem[S::X_BYTES];
 
@@ -138,6 +143,7 @@ __global__ __launch_bounds__(512, 2) void cols_kernel(const FwdParams p) {
     const int k0 = klo + KPW * wave;  // this wave's first key (scores)
     const bool active = k0 < khi;     // wave-uniform
     const int col0 = S::CPW * wave;   // this wave's first output column
+    const bool pv = NPV == S::NW || wave < NPV;  // the wave has output columns (wave-uniform)
 
     // output addresses of this lane's row
     const int64_t lse_idx = ((int64_t)b * p.n_h + h_row) * p.T + t_row;
@@ -155,7 +161,7 @@ __global__ __launch_bounds__(512, 2) void cols_kernel(const FwdParams p) {
     // unconditionally (K: by the waves that hold keys) and the waits count
     // them exactly
     if (!any) {
-        if (!row_ok) return;
+        if (!row_ok || !pv) return;
         const int c = col0 + 16 * lg;
         if constexpr (SPLIT) {
 #pragma unroll
@@ -192,7 +198,14 @@ __global__ __launch_bounds__(512, 2) void cols_kernel(const FwdParams p) {
         const int t = ok ? r / p.group : 0;
         const int h = kvh * p.group + (ok ? r % p.group : 0);
         const uint16_t *qrow = p.q + (int64_t)b * p.q_sb + (int64_t)t * p.q_st + (int64_t)h * p.q_sh;
-        load_lds_buf(qrow, 16u * (unsigned)((lane - rr) & (CH - 1)), sQ + rr * ROW);
+        if constexpr (RPI == 1) {
+            load_lds_buf(qrow, 16u * (unsigned)((lane - rr) & (CH - 1)), sQ + rr * ROW);
+        } else {
+            // two rows per load would need one base for both: one row per
+            // load, its half of the lanes (lane L lands at byte 16 L of rows
+            // 2w, 2w+1)
+            if ((lane >> 5) == i) load_lds_buf(qrow, 16u * (unsigned)((lane - rr) & (CH - 1)), sQ + 2 * wave * ROW);
+        }
     }
     const unsigned kstride = (unsigned)p.k_st * 2u, vstride = (unsigned)p.v_st * 2u;
     const uint16_t *khead = p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
@@ -201,9 +214,11 @@ __global__ __launch_bounds__(512, 2) void cols_kernel(const FwdParams p) {
         const uint16_t *kw = khead + key_offset(k, p.k_st);
         const int last = khi - 1 - k;
 #pragma unroll
-        for (int r = 0; r < KPW; ++r)
-            load_lds_buf(kw, (unsigned)min(r, last) * kstride + 16u * (unsigned)((lane - r) & (CH - 1)),
-                         sK + r * ROW);
+        for (int it = 0; it < KI; ++it) {
+            const int r = RPI * it + lane / LPR;
+            load_lds_buf(kw, (unsigned)min(r, last) * kstride + 16u * (unsigned)((lane % LPR - r) & (CH - 1)),
+                         sK + it * 1024);
+        }
     };
     if (active) issue_k(k0);
     u32x2 vr[4][8];  // V[key kp + 32ks + 8lg + i][col0 + 4lr .. +3] of the pass from key kp
@@ -218,13 +233,17 @@ __global__ __launch_bounds__(512, 2) void cols_kernel(const FwdParams p) {
         for (int i = 0; i < 8; ++i)
             vr[ks][i] = load8_buf<false>(vw, (unsigned)min(8 * lg + i, last) * vstride + 8u * (unsigned)lr);
     };
-    __builtin_amdgcn_sched_barrier(0);
-    issue_v(klo, 0);
-    issue_v(klo, 1);
-    __builtin_amdgcn_sched_barrier(0);
     // Q and K have landed (V steps 0 and 1 may still fly), then every wave's
     // Q rows are in LDS
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
+    if (pv) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_v(klo, 0);
+        issue_v(klo, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
+    } else {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
     lds_barrier();
 
     // keys visible to every row of the tile (the first row's upper bound, the
@@ -296,10 +315,12 @@ __global__ __launch_bounds__(512, 2) void cols_kernel(const FwdParams p) {
                 issue_k(kw0 + 128);
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        issue_v(kp, 2);
-        issue_v(kp, 3);
-        __builtin_amdgcn_sched_barrier(0);
+        if (pv) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_v(kp, 2);
+            issue_v(kp, 3);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 
         // ---- the tile-wide row maximum, the weights and their sums
         if (lg == 0) sMx[wave * 16 + lr] = mx;
@@ -345,16 +366,16 @@ __global__ __launch_bounds__(512, 2) void cols_kernel(const FwdParams p) {
         }
 
         // ---- O^T += V^T . P^T over the pass's keys, this wave's 64 columns
-        const int nks = min(4, (khi - kp + 31) / 32);  // 32-key steps holding keys (uniform)
+        const int nks = pv ? min(4, (khi - kp + 31) / 32) : 0;  // 32-key steps holding keys (uniform)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < 4 && pv; ++ks) {
             // step ks's V has landed (the later steps', 8 loads each, and the
-            // next pass's K, 16, requested between steps 1 and 2, may fly)
+            // next pass's K, KI, requested between steps 1 and 2, may fly)
             if (ks == 0) {
-                if (next_k) __builtin_amdgcn_s_waitcnt(waitcnt_vm(40));
+                if (next_k) __builtin_amdgcn_s_waitcnt(waitcnt_vm(24 + KI));
                 else __builtin_amdgcn_s_waitcnt(waitcnt_vm(24));
             } else if (ks == 1) {
-                if (next_k) __builtin_amdgcn_s_waitcnt(waitcnt_vm(32));
+                if (next_k) __builtin_amdgcn_s_waitcnt(waitcnt_vm(16 + KI));
                 else __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
             } else if (ks == 2) {
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
@@ -376,9 +397,11 @@ __global__ __launch_bounds__(512, 2) void cols_kernel(const FwdParams p) {
             }
         }
         // the V registers are free: the next pass's steps 0 and 1 (its K has
-        // landed: the wait before step 3 covered it)
+        // landed: the wait before step 3 covered it; a wave with no output
+        // columns waits for its K here)
         if constexpr (LOOP) {
-            if (P + 1 < npass) {
+            if (!pv) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            if (P + 1 < npass && pv) {
                 __builtin_amdgcn_sched_barrier(0);
                 issue_v(kp + 128, 0);
                 issue_v(kp + 128, 1);
@@ -395,6 +418,7 @@ __global__ __launch_bounds__(512, 2) void cols_kernel(const FwdParams p) {
     // non-temporally, then took 1.4x as long as the one-pass kernel's) -----
     const float inv = LQ > 0.f ? 1.f / LQ : 0.f;
     const float lse_val = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    if (!pv) return;
     const int n_ok = row_last - row0 + 1;  // rows of the tile that exist (workgroup-uniform)
     auto wave_sync = []() __attribute__((always_inline)) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -22,6 +22,7 @@ SHAPES = [
     ("wide-streamed-split-512", (2, 8, 2, 3, 1300), 480, True, 0),
     ("wide-shared-split-256", (1, 48, 2, 1, 700), 200, False, 0),
     ("multi-eight-waves", (40, 128, 1, 1, 300), 0, False, 0),
+    ("one-pass-shared-split", (2, 32, 1, 1, 256), 128, False, 0),
 ]
 
 HEAD_DIMS = (64, 128, 256, 512)
@@ -53,7 +54,8 @@ EXPECTED = {
           "stream_kernel<128, true, 8, 2>", "stream_kernel<128, false, 8, 2>",
           "rows_kernel<128, 1, 64>", "rows_kernel<128, 2, 32>"},
     256: {"attn_kernel<256, 4, 2, 2, 1, false, false>", "attn_kernel<256, 4, 2, 2, 2, false, false>",
-          "attn_kernel<256, 8, 4, 2, 1, false, false>", "pass_kernel<256>", "pass_loop_kernel<256>",
+          "attn_kernel<256, 8, 4, 2, 1, false, false>", "cols_kernel<256, false>", "pass_kernel<256>",
+          "pass_loop_kernel<256>",
           "rows_kernel<256, 1, 32>"},
     512: {"attn_kernel<512, 4, 1, 4, 1, false, false>", "attn_kernel<512, 4, 1, 4, 2, false, false>",
           "attn_kernel<512, 8, 2, 4, 1, false, false>", "cols_kernel<512, false>", "cols_kernel<512, true>", "pass_loop_kernel<512>",
