@@ -284,14 +284,14 @@ fmha_plan plan_attention(const FwdParams &p, int hd, bool split, int *variant_ou
         // workgroup reads, where the pass loop's 256-byte row parts went
         // faster (causal MHA prefill T 1 / T 4 over 512 keys: 30.2 / 30.3
         // against 31.1 / 31.4 us)
-        // At hd 256 only a fused one-pass call whose row blocks share K/V
-        // gained (MQA decode over 128 keys 6.64 -> 6.11 us); over several
-        // passes, split, or one row block per KV head the one-pass and
-        // pass-loop kernels stayed faster (MQA decode over 384 / 512 keys
-        // 11.3 / 14.5 against 12.1 / 16.5 us, causal MHA prefill T 1 over 128
-        // keys 7.9 against 8.3 us)
+        // At hd 256 only one-pass calls whose row blocks share K/V (MQA
+        // decode over 128 keys 6.64 -> 6.11 us); over several passes, or with
+        // one row block per KV head, the one-pass and pass-loop kernels
+        // stayed faster (MQA decode over 384 / 512 keys 11.3 / 14.5 against
+        // 12.1 / 16.5 us, causal MHA prefill T 1 over 128 keys 7.9 against
+        // 8.3 us).  A split call takes the same kernel as the fused one.
         const bool shared_kv = (p.rows + 15) / 16 > 1;
-        const bool cols = hd == 512 ? (span <= 128 || shared_kv) : (!split && span <= 128 && shared_kv);
+        const bool cols = hd == 512 ? (span <= 128 || shared_kv) : (span <= 128 && shared_kv);
         if (cols) {
             var = span > 128 ? kColsLoop : kCols;
             snprintf(pl.kernel, sizeof pl.kernel, "cols_kernel<%d, %s, %s>", hd, sp, var == kColsLoop ? "true" : "false");

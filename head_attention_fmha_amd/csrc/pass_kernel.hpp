@@ -2,8 +2,8 @@
 // grids: a workgroup computes one 16-row tile (one KV head, one key range)
 // in one pass over at most 128 keys with every load it needs in flight
 // together (pass_kernel, launched at hd 256; one pass at hd 512 runs the
-// column-split kernel of cols_kernel.hpp, as do fused one-pass calls at hd
-// 256 whose row blocks share K/V), or in several such passes
+// column-split kernel of cols_kernel.hpp, as do one-pass calls at hd 256
+// whose row blocks share K/V), or in several such passes
 // (pass_loop_kernel, below, where cols_kernel is not chosen).
 //
 // Grids of this kind are few-unit and latency-bound: the MQA decode of 128
